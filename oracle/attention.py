@@ -1,0 +1,228 @@
+"""Plain float64 CPU oracle for exact attention.  TEST INFRASTRUCTURE ONLY.
+
+Only the tests, the package's ``smoke()`` entry and the benchmark's CPU
+baseline leg may import this module.  It shares no code with the HIP path and
+imports nothing from it.
+
+Notation and sources (the pages are cited by title and section):
+
+* "flash-attention" encyclopedia page (tonho.wtf), section "o problema":
+  standard attention computes S = Q K^T, P = softmax(S), O = P V, with S and P
+  held in full.  The oracle does exactly that, in float64, per (batch, head).
+* same page, section "como funciona": the scores carry a scale tau
+  (S = tau * Q_i K_j^T), the softmax is decomposed with a running row maximum m
+  and a running row sum l, and the backward keeps only O and (m, l) and uses
+  D_i = P_i . dP_i = dO_i . O_i.
+* "Atenção eficiente — FlashAttention, sparse e híbrida" (josenaldo.com.br),
+  section "FlashAttention não acelera o decode": decode is one query row per
+  sequence against the whole KV cache.
+
+Readings where the pages are silent (each listed in the design notes):
+
+* causal mask: key j is visible to query i iff j <= i (diagonal included),
+  with as many queries as keys; decode sees every valid key of its sequence.
+* the saved statistic is LSE = m + ln(l), natural log, of the tau-scaled
+  scores; it replaces the pair (m, l).
+* the gradients are derived by hand from O = softmax(tau Q K^T) V:
+  dV = P^T dO, dP = dO V^T, D = rowsum(P o dP), dS = P o (dP - D),
+  dQ = tau dS K, dK = tau dS^T Q.
+
+Every function here is pinned by the tests in ``tests/test_oracle.py``
+against closed forms, invariants, a hand-worked example, a library softmax
+and central finite differences; none is "parity unpinned".
+"""
+from __future__ import annotations
+
+import numpy as np
+
+__all__ = [
+    "scores", "probs", "attention_fwd_head", "attention_fwd", "attention_bwd_head",
+    "attention_bwd", "decode_fwd", "tiled_fwd_literal", "split_kv_decode",
+]
+
+
+def scores(q_rows, k, tau, row_idx, causal):
+    """S[r, j] = tau * q_rows[r] . k[j], with -inf where key j > query row_idx[r]
+    under the causal mask ("o problema": S = Q K^T; "como funciona": the scale tau)."""
+    s = tau * (np.asarray(q_rows, dtype=np.float64) @ np.asarray(k, dtype=np.float64).T)
+    if causal:
+        key_idx = np.arange(k.shape[0])
+        s = np.where(key_idx[None, :] > np.asarray(row_idx)[:, None], -np.inf, s)
+    return s
+
+
+def probs(s):
+    """Row softmax of a full score block: P = exp(S - m) / l, m = rowmax, l = rowsum.
+
+    Returns (P, m, l)."""
+    m = s.max(axis=1)
+    e = np.exp(s - m[:, None])
+    l = e.sum(axis=1)
+    return e / l[:, None], m, l
+
+
+def attention_fwd_head(q, k, v, tau, causal, rows=None, chunk=1024):
+    """Standard attention for one (batch, head): O[r] and LSE[r] for the requested rows.
+
+    q: [Nq, d], k/v: [Nk, d].  The score rows are materialised whole, in chunks
+    of at most ``chunk`` rows; under the causal mask a chunk computes scores only
+    against keys up to its last query (the rest are masked, so exp gives 0).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    if causal and q.shape[0] != k.shape[0]:
+        raise ValueError("causal attention needs as many queries as keys")
+    rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
+    o = np.empty((len(rows), v.shape[1]))
+    lse = np.empty(len(rows))
+    for a in range(0, len(rows), chunk):
+        r = rows[a:a + chunk]
+        kmax = (int(r.max()) + 1) if causal else k.shape[0]
+        s = scores(q[r], k[:kmax], tau, r, causal)
+        p, m, l = probs(s)
+        o[a:a + len(r)] = p @ v[:kmax]
+        lse[a:a + len(r)] = m + np.log(l)
+    return o, lse
+
+
+def attention_fwd(q, k, v, tau, causal):
+    """Standard attention over [B, H, N, d] tensors: returns O [B,H,N,d], LSE [B,H,N]."""
+    B, H, N, d = q.shape
+    o = np.empty((B, H, N, v.shape[-1]))
+    lse = np.empty((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            o[b, h], lse[b, h] = attention_fwd_head(q[b, h], k[b, h], v[b, h], tau, causal)
+    return o, lse
+
+
+def attention_bwd_head(q, k, v, do, tau, causal):
+    """Hand-derived gradients of O = softmax(tau Q K^T [+mask]) V for one head.
+
+    With the loss's gradient dO:
+      dV = P^T dO;  dP = dO V^T;  D_i = sum_j P_ij dP_ij;
+      dS = P o (dP - D)  (zero on masked entries, where P = 0);
+      dQ = tau dS K;  dK = tau dS^T Q.
+    The identity D_i = dO_i . O_i ("como funciona", backward paragraph) is
+    returned as a second form of D for the tests to compare.
+    Returns dict(dq, dk, dv, o, lse, D, D_from_o).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    n = q.shape[0]
+    s = scores(q, k, tau, np.arange(n), causal)
+    p, m, l = probs(s)
+    o = p @ v
+    dv = p.T @ do
+    dp = do @ v.T
+    D = (p * dp).sum(axis=1)
+    ds = p * (dp - D[:, None])
+    dq = tau * (ds @ k)
+    dk = tau * (ds.T @ q)
+    return {"dq": dq, "dk": dk, "dv": dv, "o": o, "lse": m + np.log(l),
+            "D": D, "D_from_o": (do * o).sum(axis=1)}
+
+
+def attention_bwd(q, k, v, do, tau, causal):
+    """attention_bwd_head over [B, H, N, d]; returns dq, dk, dv, D as arrays."""
+    B, H, N, d = q.shape
+    out = {name: np.empty((B, H, N, d)) for name in ("dq", "dk", "dv")}
+    out["D"] = np.empty((B, H, N))
+    for b in range(B):
+        for h in range(H):
+            g = attention_bwd_head(q[b, h], k[b, h], v[b, h], do[b, h], tau, causal)
+            for name in ("dq", "dk", "dv", "D"):
+                out[name][b, h] = g[name]
+    return out
+
+
+def decode_fwd(q, k, v, seqlens, tau, heads=None, batches=None):
+    """One query per (b, h) against keys [0, L_b) of the cache; no mask inside.
+
+    q: [B,H,1,d]; k, v: [B,H,N_max,d] (rows at and beyond L_b are never read);
+    seqlens: [B].  Returns O [B,H,1,d] and LSE [B,H] (entries outside the
+    selected batches/heads are NaN).
+    """
+    B, H = q.shape[0], q.shape[1]
+    batches = range(B) if batches is None else batches
+    heads = range(H) if heads is None else heads
+    o = np.full((B, H, 1, v.shape[-1]), np.nan)
+    lse = np.full((B, H), np.nan)
+    for b in batches:
+        L = int(seqlens[b])
+        for h in heads:
+            oo, ll = attention_fwd_head(q[b, h], k[b, h, :L], v[b, h, :L], tau, False)
+            o[b, h] = oo
+            lse[b, h] = ll[0]
+    return o, lse
+
+
+def tiled_fwd_literal(q, k, v, tau, causal, Br, Bc):
+    """Self-check of the tiled recurrence, in the page's own loop order.
+
+    Follows "como funciona" of the "flash-attention" encyclopedia page: the outer
+    loop walks KV blocks of Bc rows, the inner loop walks Q blocks of Br rows;
+    O_i, l_i and m_i live in "HBM" arrays that are loaded and stored around each
+    block step; per block, m~ = rowmax(S_ij), P~ = exp(S_ij - m~),
+    m_new = max(m_i, m~), l_new = e^(m_i - m_new) l_i + e^(m~ - m_new) rowsum(P~),
+    and O_i = (l_i e^(m_i - m_new) O_i + e^(m~ - m_new) P~ V_j) / l_new.
+
+    Under the causal mask a block row can be fully masked (m~ = -inf); it then
+    contributes no term and that row's statistics are left as they were.
+    Returns O [N,d] and LSE = m + ln(l) [N] for one head.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    nq, nk = q.shape[0], k.shape[0]
+    O = np.zeros((nq, v.shape[1]))
+    l = np.zeros(nq)
+    m = np.full(nq, -np.inf)
+    for j0 in range(0, nk, Bc):
+        Kj, Vj = k[j0:j0 + Bc], v[j0:j0 + Bc]
+        for i0 in range(0, nq, Br):
+            rows = np.arange(i0, min(i0 + Br, nq))
+            Qi, Oi, li, mi = q[rows], O[rows].copy(), l[rows].copy(), m[rows].copy()
+            Sij = tau * (Qi @ Kj.T)
+            if causal:
+                keys = np.arange(j0, j0 + Kj.shape[0])
+                Sij = np.where(keys[None, :] > rows[:, None], -np.inf, Sij)
+            m_til = Sij.max(axis=1)
+            live = np.isfinite(m_til)
+            if not live.any():
+                continue
+            Sl, ml = Sij[live], m_til[live]
+            P_til = np.exp(Sl - ml[:, None])
+            m_new = np.maximum(mi[live], ml)
+            a_old = np.exp(mi[live] - m_new)
+            a_new = np.exp(ml - m_new)
+            l_new = a_old * li[live] + a_new * P_til.sum(axis=1)
+            Oi[live] = ((li[live] * a_old)[:, None] * Oi[live]
+                        + a_new[:, None] * (P_til @ Vj)) / l_new[:, None]
+            li[live], mi[live] = l_new, m_new
+            O[rows], l[rows], m[rows] = Oi, li, mi
+    return O, m + np.log(l)
+
+
+def split_kv_decode(q, k, v, tau, bounds):
+    """Self-check of the split-KV decode for one (b, h): q [1,d], k/v [L,d].
+
+    Each split s covers keys [bounds[s], bounds[s+1]) and yields its own
+    normalised output o_s and lse_s = m_s + ln l_s (standard attention on the
+    split).  The splits are merged with the same rule the tiled recurrence uses
+    to merge blocks ("como funciona"): LSE = ln sum_s exp(lse_s), taken after
+    subtracting max_s lse_s, and O = sum_s exp(lse_s - LSE) o_s.
+    Returns O [1,d], LSE scalar.
+    """
+    parts = []
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        if b > a:
+            parts.append(attention_fwd_head(q, k[a:b], v[a:b], tau, False))
+    lses = np.array([p[1][0] for p in parts])
+    mx = lses.max()
+    lse = mx + np.log(np.exp(lses - mx).sum())
+    o = sum(np.exp(ls - lse) * p[0] for ls, p in zip(lses, parts))
+    return o, lse

@@ -1,0 +1,320 @@
+"""Pins of the float64 oracle against facts fixed by the pages and by mathematics.
+
+Each test names what it pins.  None of them compares the oracle with itself:
+they use closed forms, invariants, a hand-worked example, an independent
+library softmax, the literal tiled recurrence and central finite differences.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+
+import fa_inputs
+from oracle import attention as orc
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_example.json")
+
+
+def _ev(expr):
+    return eval(expr, {"__builtins__": {}}, {"ln": math.log})  # fixture written by hand
+
+
+def _arr(x):
+    if isinstance(x, str):
+        return _ev(x)
+    return np.array([[_ev(e) for e in row] if isinstance(row, list) else _ev(row) for row in x],
+                    dtype=np.float64)
+
+
+def _rand(shape, seed):
+    return np.random.Generator(np.random.PCG64(seed)).standard_normal(shape)
+
+
+# --- hand-worked example --------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_hand_example_forward_and_backward(causal):
+    """Pins S = tau Q K^T (not K Q^T), the scale, the LSE base, the causal
+    diagonal and every gradient formula against values worked by hand."""
+    g = json.load(open(GOLDEN))
+    tau = _ev(g["tau"])
+    q, k, v, do = (_arr(g[n]) for n in ("q", "k", "v", "do"))
+    exp = g["causal" if causal else "noncausal"]
+    o, lse = orc.attention_fwd_head(q, k, v, tau, causal)
+    np.testing.assert_allclose(o, _arr(exp["o"]), rtol=0, atol=1e-14)
+    np.testing.assert_allclose(lse, np.array([_ev(e) for e in exp["lse"]]), rtol=0, atol=1e-14)
+    gr = orc.attention_bwd_head(q, k, v, do, tau, causal)
+    for name in ("dv", "dq", "dk"):
+        np.testing.assert_allclose(gr[name], _arr(exp[name]), rtol=0, atol=1e-14, err_msg=name)
+    np.testing.assert_allclose(gr["D"], [_ev(e) for e in exp["D"]], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(gr["D_from_o"], [_ev(e) for e in exp["D"]], rtol=0, atol=1e-14)
+
+
+def test_hand_example_decode():
+    g = json.load(open(GOLDEN))
+    tau = _ev(g["tau"])
+    q, k, v = (_arr(g[n]) for n in ("q", "k", "v"))
+    qd = q[1].reshape(1, 1, 1, 2)
+    kk = np.full((1, 1, 4, 2), np.nan)
+    vv = np.full((1, 1, 4, 2), np.nan)
+    kk[0, 0, :2], vv[0, 0, :2] = k, v
+    for L in (1, 2):
+        o, lse = orc.decode_fwd(qd, kk, vv, np.array([L]), tau)
+        e = g["decode"]["L%d" % L]
+        np.testing.assert_allclose(o[0, 0, 0], [_ev(x) for x in e["o"]], atol=1e-14)
+        assert abs(lse[0, 0] - _ev(e["lse"])) < 1e-14
+
+
+# --- softmax normalisation and closed forms -------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_probability_rows_sum_to_one(causal):
+    """Softmax weights of every query sum to 1 (attention-sinks section of the
+    "Atenção eficiente" page); so V = 1 gives O = 1."""
+    n, d = 37, 8
+    q, k = _rand((n, d), 1) * 3, _rand((n, d), 2) * 3
+    s = orc.scores(q, k, 0.7, np.arange(n), causal)
+    p, _, _ = orc.probs(s)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-12)
+    if causal:
+        assert np.all(p[np.triu_indices(n, 1)] == 0.0)
+    o, _ = orc.attention_fwd_head(q, k, np.ones((n, 5)), 0.7, causal)
+    np.testing.assert_allclose(o, 1.0, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_zero_query_is_uniform_average(causal):
+    """Q = 0: all visible scores are 0, so P is uniform: O_i = mean of visible V
+    and LSE_i = ln(#visible) (ln N, or ln(i+1) under the causal mask)."""
+    n, d = 50, 16
+    k, v = _rand((n, d), 3), _rand((n, d), 4)
+    o, lse = orc.attention_fwd_head(np.zeros((n, d)), k, v, 0.25, causal)
+    if causal:
+        cnt = np.arange(1, n + 1)
+        np.testing.assert_allclose(o, np.cumsum(v, axis=0) / cnt[:, None], atol=1e-13)
+        np.testing.assert_allclose(lse, np.log(cnt), atol=1e-13)
+    else:
+        np.testing.assert_allclose(o, np.broadcast_to(v.mean(axis=0), o.shape), atol=1e-13)
+        np.testing.assert_allclose(lse, np.log(n), atol=1e-13)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_identical_keys_average_values(causal):
+    """All keys equal: every visible score of a row is the same, O = mean of V,
+    and LSE_i = tau q_i.k + ln(#visible)."""
+    n, d, tau = 33, 8, 0.3
+    q, v = _rand((n, d), 5), _rand((n, d), 6)
+    kvec = _rand((d,), 7)
+    k = np.tile(kvec, (n, 1))
+    o, lse = orc.attention_fwd_head(q, k, v, tau, causal)
+    cnt = np.arange(1, n + 1) if causal else np.full(n, n)
+    mean = np.cumsum(v, axis=0) / cnt[:, None] if causal else np.broadcast_to(v.mean(0), v.shape)
+    np.testing.assert_allclose(o, mean, atol=1e-13)
+    np.testing.assert_allclose(lse, tau * q @ kvec + np.log(cnt), atol=1e-12)
+
+
+def test_dominant_score_selects_value_row():
+    """One score larger than the others by >= 40 picks its V row, and huge
+    scores (~1e4) neither overflow nor lose the row (max-shift stability)."""
+    n, d = 20, 8
+    rng = np.random.Generator(np.random.PCG64(8))
+    q = rng.standard_normal((n, d))
+    q /= np.linalg.norm(q, axis=1, keepdims=True)
+    k = rng.standard_normal((n, d)) * 0.1
+    v = rng.standard_normal((n, d))
+    star = rng.permutation(n)
+    for scale in (60.0, 1e4):
+        # query i gets one dominant key, star[i], aligned with q_i; the other
+        # keys are small, so the gap in scores is about `scale`.
+        out = []
+        for i in range(n):
+            k2 = k.copy()
+            k2[star[i]] = scale * q[i]
+            o, lse = orc.attention_fwd_head(q[i:i + 1], k2, v, 1.0, False)
+            out.append(o[0])
+            assert np.isfinite(lse[0])
+            assert abs(lse[0] - scale) < 1e-6 * scale
+        np.testing.assert_allclose(np.array(out), v[star], atol=1e-12)
+
+
+def test_softmax_matches_library_routine():
+    """Row softmax and LSE agree with scipy.special.softmax/logsumexp."""
+    n, d, tau = 40, 16, 0.2
+    q, k = _rand((n, d), 9) * 4, _rand((n, d), 10) * 4
+    s = orc.scores(q, k, tau, np.arange(n), False)
+    p, _, _ = orc.probs(s)
+    np.testing.assert_allclose(p, scipy.special.softmax(tau * q @ k.T, axis=1), atol=1e-14)
+    _, lse = orc.attention_fwd_head(q, k, _rand((n, 3), 11), tau, False)
+    np.testing.assert_allclose(lse, scipy.special.logsumexp(tau * q @ k.T, axis=1), atol=1e-12)
+
+
+def test_joint_key_value_permutation_invariance():
+    """Non-causal attention does not depend on the order of the (key, value) pairs."""
+    n, d = 29, 8
+    q, k, v = _rand((n, d), 12), _rand((n, d), 13), _rand((n, d), 14)
+    perm = np.random.Generator(np.random.PCG64(15)).permutation(n)
+    o1, l1 = orc.attention_fwd_head(q, k, v, 0.4, False)
+    o2, l2 = orc.attention_fwd_head(q, k[perm], v[perm], 0.4, False)
+    np.testing.assert_allclose(o1, o2, atol=1e-13)
+    np.testing.assert_allclose(l1, l2, atol=1e-13)
+
+
+def test_row_subset_and_chunking_agree_with_full():
+    n, d = 300, 8
+    q, k, v = _rand((n, d), 16), _rand((n, d), 17), _rand((n, d), 18)
+    for causal in (False, True):
+        o, lse = orc.attention_fwd_head(q, k, v, 0.3, causal)
+        rows = np.array([0, 1, 63, 64, 150, 299])
+        o2, l2 = orc.attention_fwd_head(q, k, v, 0.3, causal, rows=rows, chunk=4)
+        np.testing.assert_allclose(o2, o[rows], atol=1e-13)
+        np.testing.assert_allclose(l2, lse[rows], atol=1e-13)
+
+
+# --- the tiled recurrence and the split-KV merge --------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("br,bc", [(16, 16), (7, 13), (13, 7), (1, 64), (64, 5), (100, 100)])
+def test_tiled_recurrence_equals_standard(causal, br, bc):
+    """The block recurrence with running (m, l) ("como funciona") gives exactly
+    standard attention; its result is identical, not approximate."""
+    n, d = 61, 8
+    q, k, v = _rand((n, d), 19) * 2, _rand((n, d), 20) * 2, _rand((n, d), 21)
+    o, lse = orc.attention_fwd_head(q, k, v, 0.5, causal)
+    ot, lt = orc.tiled_fwd_literal(q, k, v, 0.5, causal, br, bc)
+    np.testing.assert_allclose(ot, o, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lt, lse, rtol=0, atol=1e-12)
+
+
+def test_tiled_recurrence_catches_a_dropped_rescale():
+    """The tiled check is sensitive: leaving out the e^(m_i - m_new) rescale of
+    the running output (a plausible kernel bug) moves the result far."""
+    n, d = 40, 8
+    q, k, v = _rand((n, d), 22) * 3, _rand((n, d), 23) * 3, _rand((n, d), 24)
+    o, _ = orc.attention_fwd_head(q, k, v, 0.5, False)
+    O = np.zeros((n, d)); l = np.zeros(n); m = np.full(n, -np.inf)
+    for j0 in range(0, n, 8):
+        s = 0.5 * q @ k[j0:j0 + 8].T
+        mt = s.max(1); p = np.exp(s - mt[:, None])
+        mn = np.maximum(m, mt)
+        ln_ = np.exp(m - mn) * l + np.exp(mt - mn) * p.sum(1)
+        O = (l[:, None] * O + np.exp(mt - mn)[:, None] * (p @ v[j0:j0 + 8])) / ln_[:, None]
+        l, m = ln_, mn
+    assert np.abs(O - o).max() > 1e-3
+
+
+def test_split_kv_merge_equals_unsplit():
+    """Merging split-KV partials by their LSE reproduces single-pass decode."""
+    d, L = 16, 517
+    q = _rand((1, d), 25)
+    k, v = _rand((L, d), 26) * 2, _rand((L, d), 27)
+    o, lse = orc.attention_fwd_head(q, k, v, 0.25, False)
+    for bounds in ([0, L], [0, 100, L], [0, 1, 2, 300, 301, L], list(range(0, L, 64)) + [L]):
+        o2, l2 = orc.split_kv_decode(q, k, v, 0.25, bounds)
+        np.testing.assert_allclose(o2, o, rtol=0, atol=1e-12)
+        assert abs(l2 - lse[0]) < 1e-12
+
+
+def test_decode_is_last_row_of_causal_attention():
+    """A decode step is the newest query of causal attention: it sees every key."""
+    n, d = 45, 8
+    q, k, v = _rand((n, d), 28), _rand((n, d), 29), _rand((n, d), 30)
+    o, lse = orc.attention_fwd_head(q, k, v, 0.35, True)
+    kk = np.full((1, 1, 64, d), np.nan); vv = np.full((1, 1, 64, d), np.nan)
+    kk[0, 0, :n], vv[0, 0, :n] = k, v
+    od, ld = orc.decode_fwd(q[-1].reshape(1, 1, 1, d), kk, vv, np.array([n]), 0.35)
+    np.testing.assert_allclose(od[0, 0, 0], o[-1], atol=1e-13)
+    assert abs(ld[0, 0] - lse[-1]) < 1e-13
+
+
+# --- backward --------------------------------------------------------------
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_D_identity(causal):
+    """D_i = P_i . dP_i equals dO_i . O_i ("como funciona", backward)."""
+    n, d = 40, 8
+    q, k, v, do = (_rand((n, d), s) for s in (31, 32, 33, 34))
+    g = orc.attention_bwd_head(q, k, v, do, 0.5, causal)
+    np.testing.assert_allclose(g["D"], g["D_from_o"], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_backward_column_sum_invariants(causal):
+    """Rows of P sum to 1, so sum_j dS_ij = 0: sum_j dK_j = 0 and sum_j dV_j = sum_i dO_i."""
+    n, d = 48, 8
+    q, k, v, do = (_rand((n, d), s) for s in (35, 36, 37, 38))
+    g = orc.attention_bwd_head(q, k, v, do, 0.4, causal)
+    np.testing.assert_allclose(g["dk"].sum(axis=0), 0.0, atol=1e-12)
+    np.testing.assert_allclose(g["dv"].sum(axis=0), do.sum(axis=0), atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n,d", [(5, 3), (9, 4), (16, 8)])
+def test_backward_matches_finite_differences(causal, n, d):
+    """Central differences of L = sum(O o dO) match dQ, dK and dV (rel <= 1e-6)."""
+    tau, h = 0.6, 1e-6
+    rng = np.random.Generator(np.random.PCG64(100 + n))
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    g = orc.attention_bwd_head(q, k, v, do, tau, causal)
+
+    def loss(qq, kk, vv):
+        o, _ = orc.attention_fwd_head(qq, kk, vv, tau, causal)
+        return float((o * do).sum())
+
+    for name, idx in (("dq", 0), ("dk", 1), ("dv", 2)):
+        base = [q, k, v]
+        num = np.empty((n, d))
+        for i in range(n):
+            for j in range(d):
+                plus = [x.copy() for x in base]
+                minus = [x.copy() for x in base]
+                plus[idx][i, j] += h
+                minus[idx][i, j] -= h
+                num[i, j] = (loss(*plus) - loss(*minus)) / (2 * h)
+        err = np.abs(num - g[name]).max() / max(np.abs(num).max(), 1e-30)
+        assert err <= 1e-6, (name, err)
+
+
+def test_batched_wrappers_match_per_head():
+    B, H, n, d = 2, 3, 17, 4
+    rng = np.random.Generator(np.random.PCG64(40))
+    q, k, v, do = (rng.standard_normal((B, H, n, d)) for _ in range(4))
+    o, lse = orc.attention_fwd(q, k, v, 0.5, True)
+    g = orc.attention_bwd(q, k, v, do, 0.5, True)
+    for b in range(B):
+        for hh in range(H):
+            o1, l1 = orc.attention_fwd_head(q[b, hh], k[b, hh], v[b, hh], 0.5, True)
+            g1 = orc.attention_bwd_head(q[b, hh], k[b, hh], v[b, hh], do[b, hh], 0.5, True)
+            np.testing.assert_allclose(o[b, hh], o1, atol=0)
+            np.testing.assert_allclose(lse[b, hh], l1, atol=0)
+            for name in ("dq", "dk", "dv"):
+                np.testing.assert_allclose(g[name][b, hh], g1[name], atol=0)
+
+
+# --- the shared input generator --------------------------------------------
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.0 + 2**-8, 1.0 + 3 * 2**-8, 1.0 + 2**-9, -2.5, 3.0e38, 1e-40, np.nan],
+                 dtype=np.float32)
+    bits = fa_inputs.bf16_bits(x)
+    back = fa_inputs.bf16_bits_to_f64(bits)
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: even mantissa (1.0) wins;
+    # 1 + 3*2^-8 ties between 1+2^-7 and 1+2^-6: 1 + 2^-6 has the even mantissa.
+    assert back[0] == 1.0 and back[1] == 1.0 and back[2] == 1.0 + 2**-6
+    assert back[3] == 1.0 and back[4] == -2.5
+    assert np.isfinite(back[5]) and abs(back[5] - 3.0e38) / 3.0e38 < 2**-8
+    assert np.isnan(back[7])
+    r = fa_inputs.normal_f32((1000,), 1)
+    rb = fa_inputs.bf16_bits_to_f64(fa_inputs.bf16_bits(r))
+    assert np.all(np.abs(rb - r) <= np.abs(r) * 2**-8 + 1e-45)
+
+
+def test_decode_inputs_poison_padding():
+    d = fa_inputs.decode_inputs(3, 2, 40, 8, "bf16", 5, seqlens=[1, 39, 40])
+    kf = d["k"].f64()
+    assert np.all(np.isnan(kf[0, :, 1:])) and np.all(np.isfinite(kf[0, :, :1]))
+    assert np.all(np.isnan(kf[1, :, 39:])) and np.all(np.isfinite(kf[2]))
+    s = fa_inputs.decode_seqlens(64, 1024, 8192, 1404)
+    assert s.min() >= 1024 and s.max() <= 8192
