@@ -1,0 +1,343 @@
+"""Throughput of the exact-attention path on one MI355X.
+
+One step = one pass of the whole path over the GPT-2-medium-shaped batch
+(B=8, H=16, N=1024, d=64, bf16, tau=1/8):
+    fa_fwd non-causal, fa_fwd causal, fa_bwd causal (its three kernels enqueued
+    one by one through fa_bwd_stage), and fa_decode with one query per sequence
+    against the same K/V as the cache (L_b = N for every b).
+value = algorithmic TFLOP/s of the step (forward 4*B*H*N^2*d, halved when
+causal; backward 10*B*H*N^2*d halved when causal; decode 4*B*H*N*d), from the
+wall clock around exactly --steps steps bracketed by device synchronisation.
+
+The line also carries, measured in the same run:
+  * "kernels": every call of the step timed with HIP events on the stream the
+    library launches on, with TFLOP/s and GB/s of algorithmic work;
+  * "roofline": the kernel with the largest share of the step against its
+    peak (MFMA bf16 2.5 PFLOP/s; HBM 8 TB/s), with the HBM traffic read from
+    the committed rocprofv3 counter summary when it matches the sources;
+  * "also_measured": the long causal prefill (1x32x16384x128), the split-KV
+    decode (64x32, L_b ~ U[1024, 8192], d=128) and the causal backward
+    (4x16x4096x64) at full size, each against its roofline (skip: --no-extra);
+  * "cpu_baseline": the float64 oracle on the host over a bounded sample of
+    the same step (whole heads, about 10 s of CPU work).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_MFMA_BF16 = 2.5e15     # dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12           # HBM3E, B/s
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def src_digest():
+    h = hashlib.sha256()
+    d = os.path.join(ROOT, "io_aware_tiled_03_amd", "csrc")
+    for name in sorted(os.listdir(d)):
+        with open(os.path.join(d, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+class Timer:
+    """HIP events recorded on the given stream around every call of one kind."""
+
+    def __init__(self, stream):
+        self.stream = stream
+        self.pairs = {}
+
+    def run(self, name, fn):
+        import torch
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(self.stream)
+        fn()
+        b.record(self.stream)
+        self.pairs.setdefault(name, []).append((a, b))
+
+    def mean_ms(self, name):
+        p = self.pairs[name]
+        return sum(a.elapsed_time(b) for a, b in p) / len(p)
+
+
+def fwd_flops(B, H, N, d, causal):
+    f = 4.0 * B * H * N * N * d
+    return f / 2 if causal else f
+
+
+def make_step(fa, x, B, H, N, d, tau, timer=None):
+    """Returns a closure running one step; tensors are preallocated (no allocation inside)."""
+    import torch
+    q, k, v, do = x["q"], x["k"], x["v"], x["do"]
+    o_nc, lse_nc = torch.empty_like(q), torch.empty(B, H, N, device=q.device)
+    o_c, lse_c = torch.empty_like(q), torch.empty(B, H, N, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.bwd_workspace_bytes(B, H, N) // 4, device=q.device)
+    qd = q[:, :, -1:, :].contiguous()
+    od, lsed = torch.empty_like(qd), torch.empty(B, H, device=q.device)
+    seq = torch.full((B,), N, dtype=torch.int32, device=q.device)
+    wsd = torch.empty(fa.decode_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+
+    calls = [
+        ("fwd_noncausal", lambda: fa.fwd(q, k, v, tau, False, o_nc, lse_nc)),
+        ("fwd_causal", lambda: fa.fwd(q, k, v, tau, True, o_c, lse_c)),
+        ("bwd_pre", lambda: fa.bwd(q, k, v, o_c, lse_c, do, tau, True, dq, dk, dv, ws, stage=0)),
+        ("bwd_dkdv", lambda: fa.bwd(q, k, v, o_c, lse_c, do, tau, True, dq, dk, dv, ws, stage=1)),
+        ("bwd_dq", lambda: fa.bwd(q, k, v, o_c, lse_c, do, tau, True, dq, dk, dv, ws, stage=2)),
+        ("decode", lambda: fa.decode(qd, k, v, seq, tau, 0, od, lsed, wsd)),
+    ]
+
+    def step():
+        for name, fn in calls:
+            if timer is None:
+                fn()
+            else:
+                timer.run(name, fn)
+    return step
+
+
+def step_work(B, H, N, d):
+    """Algorithmic FLOPs and HBM bytes per call of the step (bf16 = 2 bytes)."""
+    e = 2
+    t = B * H * N * d * e          # one [B,H,N,d] bf16 tensor
+    lse = B * H * N * 4
+    n2 = B * H * N * N * d
+    return {
+        "fwd_noncausal": (4.0 * n2, 3 * t + t + lse),
+        "fwd_causal": (2.0 * n2, 3 * t + t + lse),
+        "bwd_pre": (2.0 * B * H * N * d, 2 * t + lse),
+        # dK/dV kernel: S, dP, dV, dK products (4 of the 5 backward GEMMs), causal half
+        "bwd_dkdv": (4.0 * n2, 4 * t + 2 * lse + 2 * t),
+        # dQ kernel: the dQ product (1 of 5) plus its own S and dP recompute
+        "bwd_dq": (1.0 * n2, 4 * t + 2 * lse + t),
+        "decode": (4.0 * B * H * N * d, 2 * t + 2 * B * H * d * e + B * H * 4),
+    }
+
+
+def algorithmic_step_flops(B, H, N, d):
+    """fwd nc 4BHN^2d + fwd causal 2BHN^2d + bwd causal 5BHN^2d + decode 4BHNd."""
+    n2 = B * H * N * N * d
+    return 4.0 * n2 + 2.0 * n2 + 5.0 * n2 + 4.0 * B * H * N * d
+
+
+def load_traffic(kernel):
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get("kernels", {}).get(kernel)
+    if not e or t.get("src_digest") != src_digest():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_baseline(xh, B, H, N, d, tau, budget_s=10.0):
+    """The float64 oracle over whole heads of the same step until ~budget_s seconds."""
+    import numpy as np
+    from oracle import attention as orc
+    threads = None
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        threads = max((i.get("num_threads") or 0) for i in info) if info else None
+    except Exception:
+        pass
+    qf, kf, vf, dof = (xh[n].f64() for n in ("q", "k", "v", "do"))
+    heads, flops = 0, 0.0
+    t0 = time.perf_counter()
+    per_head = algorithmic_step_flops(1, 1, N, d)
+    for idx in range(B * H):
+        b, h = divmod(idx, H)
+        orc.attention_fwd_head(qf[b, h], kf[b, h], vf[b, h], tau, False)
+        orc.attention_fwd_head(qf[b, h], kf[b, h], vf[b, h], tau, True)
+        orc.attention_bwd_head(qf[b, h], kf[b, h], vf[b, h], dof[b, h], tau, True)
+        orc.decode_fwd(qf[b:b + 1, h:h + 1, -1:], kf[b:b + 1, h:h + 1], vf[b:b + 1, h:h + 1],
+                       np.array([N]), tau)
+        heads += 1
+        flops += per_head
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": threads or os.cpu_count(), "kind": "oracle",
+            "sample": "%d of %d (b,h) heads of the step (fwd non-causal, fwd causal, bwd causal, "
+                      "decode), float64 NumPy, %.1f s" % (heads, B * H, dt)}
+
+
+def bench_extra(fa, reps=20):
+    """Full-size long-prefill, decode and backward workloads, each vs its roofline."""
+    import torch
+    out = {}
+    dev = "cuda"
+    g = torch.Generator(device=dev)
+    stream = torch.cuda.current_stream()
+
+    def time_it(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            a.record(stream)
+            fn()
+            b.record(stream)
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in ev)
+        return ts[len(ts) // 2]
+
+    # long causal prefill: 1 x 32 x 16384 x 128, bf16
+    B, H, N, d = 1, 32, 16384, 128
+    g.manual_seed(1003)
+    q, k, v = (torch.randn(B, H, N, d, device=dev, generator=g).to(torch.bfloat16) for _ in range(3))
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, N, device=dev)
+    tau = 1 / math.sqrt(d)
+    ms = time_it(lambda: fa.fwd(q, k, v, tau, True, o, lse), reps)
+    fl = fwd_flops(B, H, N, d, True)
+    out["long_causal_prefill"] = {"shape": [B, H, N, d], "causal": True, "ms": round(ms, 4),
+                                  "TFLOP/s": round(fl / ms / 1e9, 2),
+                                  "frac_mfma_bf16": round(fl / ms / 1e-3 / PEAK_MFMA_BF16, 4)}
+    del q, k, v, o, lse
+
+    # decode: 64 x 32 x 8192 x 128, L_b ~ U[1024, 8192]
+    B, H, N, d = 64, 32, 8192, 128
+    import fa_inputs
+    seqlens = fa_inputs.decode_seqlens(B, 1024, 8192, 1004 + 400)
+    g.manual_seed(1004)
+    q = torch.randn(B, H, 1, d, device=dev, generator=g).to(torch.bfloat16)
+    k = torch.randn(B, H, N, d, device=dev, generator=g).to(torch.bfloat16)
+    v = torch.randn(B, H, N, d, device=dev, generator=g).to(torch.bfloat16)
+    sl = torch.from_numpy(seqlens).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, device=dev)
+    ws = torch.empty(fa.decode_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+    ms = time_it(lambda: fa.decode(q, k, v, sl, 1 / math.sqrt(d), 0, o, lse, ws), reps * 2)
+    nbytes = float(seqlens.astype("int64").sum()) * H * d * 2 * 2 + 2 * B * H * d * 2 + B * H * 4
+    out["decode_splitkv"] = {"shape": [B, H, N, d], "seqlens_sum": int(seqlens.sum()),
+                             "num_splits": fa.decode_num_splits(B, H, N, d),
+                             "ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1),
+                             "frac_hbm": round(nbytes / ms / 1e-3 / PEAK_HBM, 4)}
+    del q, k, v, o, lse, ws
+
+    # backward: 4 x 16 x 4096 x 64, causal
+    B, H, N, d = 4, 16, 4096, 64
+    g.manual_seed(1005)
+    q, k, v, do = (torch.randn(B, H, N, d, device=dev, generator=g).to(torch.bfloat16)
+                   for _ in range(4))
+    tau = 1 / math.sqrt(d)
+    o, lse = fa.fwd(q, k, v, tau, True)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(B * H * N, device=dev)
+    ms = time_it(lambda: fa.bwd(q, k, v, o, lse, do, tau, True, dq, dk, dv, ws), reps)
+    fl = 10.0 * B * H * N * N * d / 2
+    out["bwd_recompute"] = {"shape": [B, H, N, d], "causal": True, "ms": round(ms, 4),
+                            "TFLOP/s": round(fl / ms / 1e9, 2),
+                            "frac_mfma_bf16": round(fl / ms / 1e-3 / PEAK_MFMA_BF16, 4)}
+    return out
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    args = ap.parse_args(argv)
+    if args.gpus != 1:
+        print("bench.py: this attention path runs on one GPU; --gpus %d is not supported "
+              "(sharding over (batch, head) is described in the design notes, not built)"
+              % args.gpus, file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import fa_inputs
+    import io_aware_tiled_03_amd as fa
+    fa.lib()   # fails loudly if the library is not built
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 2
+    torch.cuda.set_device(0)
+
+    w = fa_inputs.WORKLOADS[2]
+    B, H, N, d, tau = w.B, w.H, w.N, w.d, w.tau
+    xh = fa_inputs.dense_inputs(B, H, N, d, "bf16", w.seed, with_do=True)
+    x = {n: torch.from_numpy(np.ascontiguousarray(xh[n].raw).view(np.int16)).view(
+        torch.bfloat16).cuda() for n in ("q", "k", "v", "do")}
+
+    plain = make_step(fa, x, B, H, N, d, tau)
+    for _ in range(args.warmup):
+        plain()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        plain()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall / args.steps * 1e3
+    step_flops = algorithmic_step_flops(B, H, N, d)
+    value = step_flops / (wall / args.steps) / 1e12
+
+    # per-call HIP events over a second timed pass of the same steps
+    stream = torch.cuda.current_stream()
+    timer = Timer(stream)
+    timed = make_step(fa, x, B, H, N, d, tau, timer)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        timed()
+    torch.cuda.synchronize()
+    work = step_work(B, H, N, d)
+    kernels = {}
+    for name in work:
+        ms = timer.mean_ms(name)
+        fl, by = work[name]
+        kernels[name] = {"ms": round(ms, 5), "TFLOP/s": round(fl / ms / 1e9, 2),
+                         "GB/s": round(by / ms / 1e6, 1)}
+    dom = max(kernels, key=lambda n: kernels[n]["ms"])
+    fl, by = work[dom]
+    dms = timer.mean_ms(dom)
+    if fl / by > 300:
+        roof = {"bound": "mfma", "achieved": round(fl / dms / 1e9, 2), "peak": PEAK_MFMA_BF16 / 1e12,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": round(by / dms / 1e6, 1), "peak": PEAK_HBM / 1e9,
+                "unit": "GB/s"}
+    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
+    roof["kernel"] = dom
+    roof["traffic"] = load_traffic(dom)
+
+    line = {
+        "metric": "attention fwd/bwd TFLOP/s and % MFMA peak (bf16, d=64/128); decode HBM GB/s",
+        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "gpt2-medium-shaped attention step: fwd non-causal + fwd causal "
+                               "+ bwd causal + decode (L_b=N)", "B": B, "H": H, "N": N, "d": d,
+                   "tau": tau, "parallelism": "single GPU"},
+        "frac_of_mfma_peak": round(value * 1e12 / PEAK_MFMA_BF16, 4),
+        "kernels": kernels,
+        "roofline": roof,
+    }
+    if not args.no_extra:
+        line["also_measured"] = bench_extra(fa)
+    if not args.no_cpu:
+        line["cpu_baseline"] = cpu_baseline(xh, B, H, N, d, tau)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

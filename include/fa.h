@@ -1,0 +1,171 @@
+/*
+ * fa.h - C ABI of the MI355X (gfx950) exact-attention library, libfa.so.
+ *
+ * The library computes exact attention O = softmax(tau * Q K^T [+ causal mask]) V
+ * without ever writing the N x N score matrix to HBM: Q is tiled, K/V tiles are
+ * staged on chip, and the softmax is carried through the key blocks with a
+ * running row maximum m and row sum l that rescale the partial output whenever
+ * a block is merged ("flash-attention" encyclopedia page, sections "a ideia"
+ * and "como funciona").  The forward saves only O and the per-row
+ * log-sum-exp, and the backward recomputes S and P from them (same page,
+ * backward paragraph of "como funciona").
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * Tensors   : device pointers to contiguous row-major [B, H, N, d] arrays, d
+ *             fastest, 16-byte aligned.  The caller owns every buffer; the
+ *             library allocates nothing and keeps no global state.
+ * dtype     : FA_BF16 (bfloat16) or FA_F32 (IEEE float).  O, dQ, dK and dV
+ *             take the input dtype; LSE and D are always float.
+ * Arithmetic: products are accumulated in fp32 (bf16 MFMA with fp32
+ *             accumulation for FA_BF16; fp32 throughout for FA_F32).  The
+ *             probabilities P are rounded to bf16 before the P V product on the
+ *             FA_BF16 path.
+ * tau       : the scale applied to Q K^T before the softmax (typically
+ *             1/sqrt(d)); must be finite and > 0.
+ * causal    : 0 or 1.  When 1, key j is visible to query i iff j <= i
+ *             (diagonal included; as many queries as keys).
+ * LSE       : natural-log log-sum-exp of each row of the tau-scaled scores,
+ *             LSE_i = m_i + ln(l_i), float [B, H, N].
+ * stream    : a hipStream_t (NULL = the default stream).  Every call only
+ *             validates on the host and enqueues kernels; it returns before
+ *             the work finishes.
+ * Errors    : every entry point returns an fa_status.  Arguments are checked
+ *             on the host before anything is launched; a failed check launches
+ *             nothing and writes nothing.  FA_ERR_HIP reports a launch error
+ *             (hipGetLastError after the launches).  Nothing is thrown across
+ *             the ABI.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FA_OK = 0,
+    FA_ERR_NULL = 1,         /* a required pointer is NULL                     */
+    FA_ERR_SHAPE = 2,        /* B, H, N, d or a length out of range            */
+    FA_ERR_UNSUPPORTED = 3,  /* dtype, head dim or flag value not supported    */
+    FA_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required        */
+    FA_ERR_HIP = 5,          /* the HIP runtime reported a launch error        */
+    FA_ERR_ALIGN = 6,        /* a pointer is not 16-byte aligned               */
+    FA_ERR_ARG = 7           /* tau not finite and positive, or bad split count */
+} fa_status;
+
+typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
+
+/* Supported head dimensions: 64 and 128.  Sizes: B, H, N >= 1 and
+ * B*H <= 2^31-1, N <= 2^20 (FA_ERR_SHAPE otherwise). */
+
+/*
+ * fa_fwd - fused exact-attention forward (prefill).
+ *
+ * Defined by the standard statement S = tau Q K^T, P = softmax(S), O = P V
+ * ("flash-attention" page, sections "o problema" and "como funciona"), computed
+ * tile by tile with the running (m, l) statistics so that S and P never leave
+ * the chip ("FlashAttention e o gargalo real de inferência", section
+ * "FlashAttention: eliminar a viagem").
+ *
+ * q, k, v : [B, H, N, d] inputs of dtype `dtype`.
+ * o       : [B, H, N, d] output, dtype `dtype`.
+ * lse     : [B, H, N] float output (the statistic the backward needs).
+ * Fully masked causal tiles are never visited.
+ */
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
+           int B, int H, int N, int d, float tau, int causal, int dtype, void* stream);
+
+/*
+ * fa_decode_workspace_bytes - workspace that fa_decode needs.
+ *
+ * num_splits = 0 asks for the size of the split count that fa_decode chooses
+ * by itself for these sizes; otherwise the size for that explicit count.
+ * Returns 0 for arguments fa_decode would reject.
+ */
+size_t fa_decode_workspace_bytes(int B, int H, int N_max, int d, int num_splits);
+
+/*
+ * fa_decode_num_splits - the split count fa_decode uses for these sizes
+ * (num_splits = 0 picks it from B*H and N_max; otherwise returns num_splits).
+ */
+int fa_decode_num_splits(int B, int H, int N_max, int d, int num_splits);
+
+/*
+ * fa_decode - one query per sequence against a KV cache, split over the keys.
+ *
+ * The decode step is a single query row reading the whole KV cache from HBM
+ * ("Atenção eficiente — FlashAttention, sparse e híbrida", section
+ * "FlashAttention não acelera o decode").  Each (b, h) key range [0, L_b) is cut
+ * into num_splits contiguous chunks of equal length (the last ones may be
+ * short or empty); each chunk yields its normalised partial output o_s and its
+ * lse_s in the workspace, and a merge kernel combines them with the block-merge
+ * rule of the running (m, l) statistics ("flash-attention" page, "como
+ * funciona"): LSE = ln sum_s exp(lse_s), O = sum_s exp(lse_s - LSE) o_s.
+ *
+ * q         : [B, H, 1, d] queries (the newest token of each sequence).
+ * k, v      : [B, H, N_max, d] caches; rows at and beyond L_b are never read.
+ * seqlens_k : device int32 [B], L_b.  Values are clamped to [0, N_max] on the
+ *             device; a sequence with L_b = 0 yields O = 0 and LSE = -inf.
+ * o         : [B, H, 1, d] output (dtype `dtype`); lse: [B, H] float output.
+ * num_splits: 0 = automatic, else 1..1024.
+ * workspace : device memory of at least fa_decode_workspace_bytes(...) bytes,
+ *             16-byte aligned; its contents on entry do not matter.
+ * No mask: all L_b keys are visible to the decode query.
+ */
+int fa_decode(const void* q, const void* k, const void* v, const int* seqlens_k,
+              int B, int H, int N_max, int d, float tau, void* o, float* lse,
+              int num_splits, void* workspace, size_t workspace_bytes,
+              int dtype, void* stream);
+
+/*
+ * fa_bwd_workspace_bytes - workspace of fa_bwd: D, B*H*N floats.
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N);
+
+/*
+ * fa_bwd - recomputing backward of fa_fwd.
+ *
+ * Uses only O and LSE saved by the forward ("flash-attention" page, "como
+ * funciona", backward paragraph): first D_i = dO_i . O_i (the page's identity
+ * D_i = P_i . dP_i = dO_i . O_i, an inner product of length d), then one kernel
+ * per key tile that recomputes S = tau Q K^T and P = exp(S - LSE) on chip and
+ * accumulates dV = P^T dO and dK = tau dS^T Q with dS = P o (dO V^T - D), and
+ * one kernel per query tile that accumulates dQ = tau dS K.  No atomics: the
+ * result is deterministic.
+ *
+ * q, k, v, o, dout : [B, H, N, d], dtype `dtype`; o is fa_fwd's output.
+ * lse              : [B, H, N] float, fa_fwd's output.
+ * dq, dk, dv       : [B, H, N, d] outputs, dtype `dtype`.
+ * workspace        : >= fa_bwd_workspace_bytes(B, H, N) bytes; on return it
+ *                    holds D as float [B, H, N].
+ */
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv,
+           int B, int H, int N, int d, float tau, int causal,
+           void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * fa_bwd_stage - enqueue one of fa_bwd's three kernels.
+ *
+ * stage 0 computes D into the workspace, stage 1 dK and dV, stage 2 dQ (stages
+ * 1 and 2 read D, so stage 0 must have run on the same inputs).  Enqueuing
+ * stages 0, 1, 2 in order on one stream is exactly fa_bwd.  Same arguments and
+ * checks as fa_bwd, plus FA_ERR_ARG for a stage outside 0..2.  Meant for
+ * per-kernel timing and for callers that only need D.
+ */
+int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                 int B, int H, int N, int d, float tau, int causal,
+                 void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/* fa_status_string - static, human-readable text of a status code. */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,164 @@
+"""Python binding of libfa.so, the gfx950 exact-attention library.
+
+Argument marshalling only: every call goes through the C ABI declared in
+``include/fa.h`` and every step of the computation runs in the library's HIP
+kernels.  PyTorch supplies device memory and the current stream.  If the
+library has not been built this module raises instead of computing anything
+elsewhere.
+
+    o, lse = fwd(q, k, v, tau=None, causal=False)
+    o, lse = decode(q, k, v, seqlens_k, tau=None, num_splits=0)
+    dq, dk, dv = bwd(q, k, v, o, lse, do, tau=None, causal=False)
+
+Tensors are contiguous [B, H, N, d] on the GPU, dtype bfloat16 or float32.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+FA_F32, FA_BF16 = 0, 1
+STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED",
+          4: "FA_ERR_WORKSPACE", 5: "FA_ERR_HIP", 6: "FA_ERR_ALIGN", 7: "FA_ERR_ARG"}
+
+# (name, restype, argtypes) of every symbol that fa.h declares.
+_P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+SIGNATURES = {
+    "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
+    "fa_decode_num_splits": (_I, [_I, _I, _I, _I, _I]),
+    "fa_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _I, _P, _Z, _I, _P]),
+    "fa_bwd_workspace_bytes": (_Z, [_I, _I, _I]),
+    "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _Z, _I, _P]),
+    "fa_bwd_stage": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _Z,
+                          _I, _P]),
+    "fa_status_string": (ctypes.c_char_p, [_I]),
+}
+
+_lib = None
+
+
+class FAError(RuntimeError):
+    def __init__(self, fn, status, text):
+        super().__init__("%s failed: %s (%s)" % (fn, STATUS.get(status, status), text))
+        self.status = status
+
+
+def lib():
+    """Load libfa.so (once) and declare its signatures; raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libfa.so is not built at %s; run "
+                               "`python -m io_aware_tiled_03_amd.build`" % LIB_PATH)
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(handle, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = handle
+    return _lib
+
+
+def check(fn, status):
+    if status != 0:
+        raise FAError(fn, status, lib().fa_status_string(status).decode())
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float32:
+        return FA_F32
+    raise TypeError("unsupported dtype %s" % t.dtype)
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _need(t, name):
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def fwd(q, k, v, tau=None, causal=False, o=None, lse=None):
+    """O = softmax(tau Q K^T [+causal mask]) V and LSE, via fa_fwd."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        _need(t, n)
+    B, H, N, d = q.shape
+    tau = 1.0 / math.sqrt(d) if tau is None else float(tau)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    st = lib().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+                      B, H, N, d, tau, int(bool(causal)), _dtype_code(q), _stream(q))
+    check("fa_fwd", st)
+    return o, lse
+
+
+def decode_workspace_bytes(B, H, N_max, d, num_splits=0):
+    return int(lib().fa_decode_workspace_bytes(B, H, N_max, d, num_splits))
+
+
+def decode_num_splits(B, H, N_max, d, num_splits=0):
+    return int(lib().fa_decode_num_splits(B, H, N_max, d, num_splits))
+
+
+def decode(q, k, v, seqlens_k, tau=None, num_splits=0, o=None, lse=None, workspace=None):
+    """One query per (b, h) against the KV cache rows [0, seqlens_k[b]), via fa_decode."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (seqlens_k, "seqlens_k")):
+        _need(t, n)
+    if seqlens_k.dtype != torch.int32:
+        raise TypeError("seqlens_k must be int32")
+    B, H, N_max, d = k.shape
+    tau = 1.0 / math.sqrt(d) if tau is None else float(tau)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    need = decode_workspace_bytes(B, H, N_max, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib().fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), seqlens_k.data_ptr(), B, H,
+                         N_max, d, tau, o.data_ptr(), lse.data_ptr(), int(num_splits),
+                         workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                         _dtype_code(q), _stream(q))
+    check("fa_decode", st)
+    return o, lse
+
+
+def bwd_workspace_bytes(B, H, N):
+    return int(lib().fa_bwd_workspace_bytes(B, H, N))
+
+
+def bwd(q, k, v, o, lse, do, tau=None, causal=False, dq=None, dk=None, dv=None, workspace=None,
+        stage=None):
+    """dQ, dK, dV of fa_fwd's output given dO, via fa_bwd (workspace holds D on return).
+
+    With stage in (0, 1, 2) only that kernel is enqueued, via fa_bwd_stage."""
+    import torch
+    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (do, "do")):
+        _need(t, n)
+    B, H, N, d = q.shape
+    tau = 1.0 / math.sqrt(d) if tau is None else float(tau)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    if workspace is None:
+        workspace = torch.empty(bwd_workspace_bytes(B, H, N) // 4, dtype=torch.float32,
+                                device=q.device)
+    args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
+            do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, tau,
+            int(bool(causal)), workspace.data_ptr(),
+            workspace.numel() * workspace.element_size(), _dtype_code(q), _stream(q))
+    if stage is None:
+        check("fa_bwd", lib().fa_bwd(*args))
+    else:
+        check("fa_bwd_stage", lib().fa_bwd_stage(int(stage), *args))
+    return dq, dk, dv

@@ -1,0 +1,152 @@
+// fa_api.cpp - the extern "C" entry points of libfa.so (declared in fa.h).
+// Validates every argument on the host, resolves the launch configuration and
+// enqueues the kernels on the caller's stream.  Nothing here allocates or
+// touches device memory.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+
+#include "fa.h"
+#include "fa_internal.h"
+
+namespace {
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool aligned4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
+
+int check_common(int B, int H, int N, int d, float tau, int dtype) {
+    if (B < 1 || H < 1 || N < 1 || N > (1 << 20)) return FA_ERR_SHAPE;
+    if ((long long)B * H > 0x7fffffffLL) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_F32 && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (!(tau > 0.f) || !isfinite(tau)) return FA_ERR_ARG;
+    return FA_OK;
+}
+
+// Workgroups of the largest grid a call launches must stay addressable.
+bool grid_ok(long long blocks, int threads) {
+    return blocks >= 1 && blocks * threads < (1LL << 32) && blocks < 0x7fffffffLL;
+}
+
+int after_launch() {
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
+           int d, float tau, int causal, int dtype, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    int st = check_common(B, H, N, d, tau, dtype);
+    if (st != FA_OK) return st;
+    if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
+        return FA_ERR_ALIGN;
+    const long long bh = (long long)B * H;
+    if (!grid_ok(bh * ((N + 63) / 64), 256)) return FA_ERR_SHAPE;
+    fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, tau, causal, dtype};
+    (void)hipGetLastError();
+    fa::launch_fwd(a, (hipStream_t)stream);
+    return after_launch();
+}
+
+int fa_decode_num_splits(int B, int H, int N_max, int d, int num_splits) {
+    if (B < 1 || H < 1 || N_max < 1 || N_max > (1 << 20) || (d != 64 && d != 128)) return 0;
+    if (num_splits < 0 || num_splits > 1024) return 0;
+    return fa::decode_splits(B, H, N_max, d, num_splits);
+}
+
+size_t fa_decode_workspace_bytes(int B, int H, int N_max, int d, int num_splits) {
+    const int s = fa_decode_num_splits(B, H, N_max, d, num_splits);
+    if (s == 0) return 0;
+    return fa::decode_ws_bytes(B, H, d, s);
+}
+
+int fa_decode(const void* q, const void* k, const void* v, const int* seqlens_k, int B, int H,
+              int N_max, int d, float tau, void* o, float* lse, int num_splits, void* workspace,
+              size_t workspace_bytes, int dtype, void* stream) {
+    if (!q || !k || !v || !seqlens_k || !o || !lse) return FA_ERR_NULL;
+    int st = check_common(B, H, N_max, d, tau, dtype);
+    if (st != FA_OK) return st;
+    if (num_splits < 0 || num_splits > 1024) return FA_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse) ||
+        !aligned4(seqlens_k))
+        return FA_ERR_ALIGN;
+    const int S = fa::decode_splits(B, H, N_max, d, num_splits);
+    const size_t need = fa::decode_ws_bytes(B, H, d, S);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+    if (B > 65535 || H > 65535 || !grid_ok((long long)S * B * H, 256)) return FA_ERR_SHAPE;
+    float* ws = (float*)workspace;
+    const size_t n_o = (size_t)S * B * H * d;
+    fa::DecodeArgs a{q, k, v, seqlens_k, B, H, N_max, d, tau, o, lse, S,
+                     fa::decode_chunk(N_max, S), ws, ws + n_o, dtype};
+    (void)hipGetLastError();
+    fa::launch_decode(a, (hipStream_t)stream);
+    return after_launch();
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N) {
+    if (B < 1 || H < 1 || N < 1) return 0;
+    return (size_t)B * H * N * sizeof(float);
+}
+
+namespace {
+
+int bwd_common(int stages, const void* q, const void* k, const void* v, const void* o,
+               const float* lse, const void* dout, void* dq, void* dk, void* dv, int B, int H,
+               int N, int d, float tau, int causal, void* workspace, size_t workspace_bytes,
+               int dtype, void* stream) {
+    if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
+    int st = check_common(B, H, N, d, tau, dtype);
+    if (st != FA_OK) return st;
+    if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
+        !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned4(lse))
+        return FA_ERR_ALIGN;
+    if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, H, N)) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+    if (!grid_ok((long long)B * H * ((N + 63) / 64), 256)) return FA_ERR_SHAPE;
+    fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, (float*)workspace, B, H, N, d, tau, causal,
+                  dtype};
+    (void)hipGetLastError();
+    fa::launch_bwd(a, stages, (hipStream_t)stream);
+    return after_launch();
+}
+
+}  // namespace
+
+int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
+           const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d, float tau,
+           int causal, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+    return bwd_common(7, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, tau, causal, workspace,
+                      workspace_bytes, dtype, stream);
+}
+
+int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, const void* dout, void* dq, void* dk, void* dv, int B, int H,
+                 int N, int d, float tau, int causal, void* workspace, size_t workspace_bytes,
+                 int dtype, void* stream) {
+    if (stage < 0 || stage > 2) return FA_ERR_ARG;
+    return bwd_common(1 << stage, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, tau, causal,
+                      workspace, workspace_bytes, dtype, stream);
+}
+
+const char* fa_status_string(int status) {
+    switch (status) {
+        case FA_OK: return "ok";
+        case FA_ERR_NULL: return "a required pointer is NULL";
+        case FA_ERR_SHAPE: return "a size is out of range";
+        case FA_ERR_UNSUPPORTED: return "unsupported dtype, head dimension or flag";
+        case FA_ERR_WORKSPACE: return "workspace missing or too small";
+        case FA_ERR_HIP: return "HIP launch error";
+        case FA_ERR_ALIGN: return "a pointer is not aligned (16 bytes for tensors)";
+        case FA_ERR_ARG: return "tau must be finite and positive; num_splits in 0..1024";
+        default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// fa_internal.h - argument bundles and launcher declarations shared by the
+// C-ABI layer (fa_api.cpp) and the kernel translation units.  Launchers assume
+// arguments were validated by the ABI layer.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+namespace fa {
+
+enum { kF32 = 0, kBF16 = 1 };
+
+struct FwdArgs {
+    const void *q, *k, *v;
+    void* o;
+    float* lse;
+    int B, H, N, d;
+    float tau;
+    int causal, dtype;
+};
+void launch_fwd(const FwdArgs& a, hipStream_t st);
+
+struct DecodeArgs {
+    const void *q, *k, *v;
+    const int* seqlens;
+    int B, H, N_max, d;
+    float tau;
+    void* o;
+    float* lse;
+    int num_splits;       // resolved (>= 1)
+    int chunk;            // keys per split: ceil(N_max / num_splits) rounded up to 64
+    float* ws_o;          // [num_splits, B, H, d] normalised partial outputs
+    float* ws_lse;        // [num_splits, B, H] partial LSE (-inf for empty splits)
+    int dtype;
+};
+void launch_decode(const DecodeArgs& a, hipStream_t st);
+int decode_splits(int B, int H, int N_max, int d, int requested);
+int decode_chunk(int N_max, int splits);
+size_t decode_ws_bytes(int B, int H, int d, int splits);
+
+struct BwdArgs {
+    const void *q, *k, *v, *o;
+    const float* lse;
+    const void* dout;
+    void *dq, *dk, *dv;
+    float* D;             // [B, H, N] workspace
+    int B, H, N, d;
+    float tau;
+    int causal, dtype;
+};
+// stages: bit 0 = D preprocess, bit 1 = dK/dV, bit 2 = dQ (launched in that order)
+void launch_bwd(const BwdArgs& a, int stages, hipStream_t st);
+
+}  // namespace fa

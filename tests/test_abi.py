@@ -1,0 +1,142 @@
+"""Host-side checks of libfa.so: it loads, exports every symbol fa.h declares, and
+rejects invalid arguments with the documented status before launching anything.
+None of these calls reaches a kernel, so they run without a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _lib():
+    import io_aware_tiled_03_amd as fa
+    if not os.path.exists(fa.LIB_PATH):
+        pytest.skip("libfa.so not built")
+    return fa, fa.lib()
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    import io_aware_tiled_03_amd as fa
+    assert _declared() == sorted(fa.SIGNATURES)
+
+
+def test_library_exports_every_declared_symbol():
+    fa, lib = _lib()
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    fa, lib = _lib()
+    for code in range(8):
+        assert lib.fa_status_string(code)
+    assert lib.fa_status_string(99) == b"unknown status"
+
+
+P = 4096  # a fake, 16-byte aligned non-null address: never dereferenced on failure paths
+
+
+def _fwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=16, d=64, tau=0.125, causal=0, dtype=1)
+    a.update(kw)
+    return lib.fa_fwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"], a["d"],
+                      a["tau"], a["causal"], a["dtype"], None)
+
+
+def test_fwd_rejects_bad_arguments():
+    fa, lib = _lib()
+    assert _fwd(lib, q=None) == 1
+    assert _fwd(lib, lse=None) == 1
+    assert _fwd(lib, N=0) == 2
+    assert _fwd(lib, B=-1) == 2
+    assert _fwd(lib, N=(1 << 20) + 1) == 2
+    assert _fwd(lib, d=96) == 3
+    assert _fwd(lib, dtype=7) == 3
+    assert _fwd(lib, causal=2) == 3
+    assert _fwd(lib, tau=0.0) == 7
+    assert _fwd(lib, tau=float("nan")) == 7
+    assert _fwd(lib, tau=float("inf")) == 7
+    assert _fwd(lib, q=P + 8) == 6
+    assert _fwd(lib, lse=P + 2) == 6
+
+
+def _dec(lib, **kw):
+    a = dict(q=P, k=P, v=P, sl=P, B=2, H=2, N=100, d=128, tau=0.1, o=P, lse=P, ns=0, ws=P,
+             wsb=1 << 30, dtype=1)
+    a.update(kw)
+    return lib.fa_decode(a["q"], a["k"], a["v"], a["sl"], a["B"], a["H"], a["N"], a["d"],
+                         a["tau"], a["o"], a["lse"], a["ns"], a["ws"], a["wsb"], a["dtype"], None)
+
+
+def test_decode_rejects_bad_arguments():
+    fa, lib = _lib()
+    assert _dec(lib, sl=None) == 1
+    assert _dec(lib, N=0) == 2
+    assert _dec(lib, d=32) == 3
+    assert _dec(lib, ns=-1) == 7
+    assert _dec(lib, ns=5000) == 7
+    assert _dec(lib, ws=None) == 4
+    need = lib.fa_decode_workspace_bytes(2, 2, 100, 128, 0)
+    assert need > 0
+    assert _dec(lib, wsb=need - 1) == 4
+    assert _dec(lib, ws=P + 4) == 6
+
+
+def test_decode_split_rule():
+    fa, lib = _lib()
+    # automatic splits: >= 256 keys per split unless that would exceed 16384 workgroups
+    assert lib.fa_decode_num_splits(1, 1, 8192, 128, 0) == 32
+    assert lib.fa_decode_num_splits(64, 32, 8192, 128, 0) == 8
+    assert lib.fa_decode_num_splits(1, 1, 100, 128, 0) == 1
+    # explicit counts use equal chunks rounded up to 64 keys
+    assert lib.fa_decode_num_splits(1, 1, 300, 64, 7) == 5
+    assert lib.fa_decode_num_splits(1, 1, 300, 64, 1) == 1
+    s = lib.fa_decode_num_splits(64, 32, 8192, 128, 0)
+    assert lib.fa_decode_workspace_bytes(64, 32, 8192, 128, 0) == s * 64 * 32 * 129 * 4
+    assert lib.fa_decode_workspace_bytes(1, 1, 100, 96, 0) == 0
+
+
+def _bwd(lib, **kw):
+    a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=2, N=64, d=64, tau=0.125,
+             causal=1, ws=P, wsb=1 << 20, dtype=1)
+    a.update(kw)
+    return lib.fa_bwd(a["q"], a["k"], a["v"], a["o"], a["lse"], a["do"], a["dq"], a["dk"],
+                      a["dv"], a["B"], a["H"], a["N"], a["d"], a["tau"], a["causal"], a["ws"],
+                      a["wsb"], a["dtype"], None)
+
+
+def test_bwd_rejects_bad_arguments():
+    fa, lib = _lib()
+    assert _bwd(lib, dv=None) == 1
+    assert _bwd(lib, N=0) == 2
+    assert _bwd(lib, d=80) == 3
+    assert _bwd(lib, dtype=0) == 3
+    assert _bwd(lib, ws=None) == 4
+    assert _bwd(lib, wsb=1 * 2 * 64 * 4 - 1) == 4
+    assert _bwd(lib, dq=P + 2) == 6
+    assert lib.fa_bwd_workspace_bytes(1, 2, 64) == 512
+
+
+def test_bwd_stage_rejects_bad_arguments():
+    fa, lib = _lib()
+    args = (P, P, P, P, P, P, P, P, P, 1, 2, 64, 64, 0.125, 1, P, 1 << 20, 1, None)
+    assert lib.fa_bwd_stage(3, *args) == 7
+    assert lib.fa_bwd_stage(-1, *args) == 7
+    bad = list(args); bad[10] = 0
+    assert lib.fa_bwd_stage(1, *bad) == 2
+
+
+def test_binding_refuses_cpu_tensors():
+    fa, lib = _lib()
+    import torch
+    x = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(ValueError):
+        fa.fwd(x, x, x)

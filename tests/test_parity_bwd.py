@@ -1,0 +1,74 @@
+"""GPU parity of fa_bwd (D preprocess, dK/dV, dQ) against the float64 oracle."""
+import numpy as np
+import pytest
+
+import fa_inputs
+from oracle import attention as orc
+from tests.util import assert_close, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(x, causal, tau):
+    import io_aware_tiled_03_amd as fa
+    import torch
+    q, k, v, do = (to_device(x[n]) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, tau=tau, causal=causal)
+    B, H, N, d = q.shape
+    ws = torch.empty(fa.bwd_workspace_bytes(B, H, N) // 4, dtype=torch.float32, device="cuda")
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, tau=tau, causal=causal, workspace=ws)
+    return {"dq": to_f64(dq), "dk": to_f64(dk), "dv": to_f64(dv), "D": to_f64(ws).reshape(B, H, N)}
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("N", [1, 7, 63, 130, 257, 600])
+def test_bwd_small(N, causal, d):
+    B, H = 2, 2
+    x = fa_inputs.dense_inputs(B, H, N, d, "bf16", 10000 + N, with_do=True)
+    tau = 1.0 / np.sqrt(d)
+    g = _run(x, causal, tau)
+    ref = orc.attention_bwd(*(x[n].f64() for n in ("q", "k", "v", "do")), tau, causal)
+    for name in ("dq", "dk", "dv"):
+        assert_close(g[name], ref[name], "bf16", name)
+    # D is computed from the forward's bf16 output O, so it inherits O's error:
+    # |D_gpu - D| <= sum_d |dO_d| * (|O_d - bf16(O_d)| + |err of O_d|), with the
+    # bf16 rounding of O bounded by 2^-8 |O_d| (one unit in the last place, so a
+    # rounding that lands on the other side is covered) and O's error by the
+    # mean tolerance 2e-3.
+    do64, o64 = x["do"].f64(), orc.attention_fwd(*(x[n].f64() for n in ("q", "k", "v")),
+                                                 tau, causal)[0]
+    bound = (np.abs(do64) * (2.0 ** -8 * np.abs(o64) + 2e-3)).sum(axis=-1)
+    assert np.all(np.abs(g["D"] - ref["D"]) <= bound), np.abs(g["D"] - ref["D"]).max()
+
+
+def test_bwd_workload_full():
+    """Workload 5 at full size (4x16x4096x64 bf16, causal): 3 sampled heads compared
+    element by element; the column-sum invariants checked over every head."""
+    w = fa_inputs.WORKLOADS[5]
+    x = fa_inputs.workload_inputs(w)
+    g = _run(x, True, w.tau)
+    qf, kf, vf, dof = (x[n].f64() for n in ("q", "k", "v", "do"))
+    for b, h in ((0, 0), (2, 7), (3, 15)):
+        ref = orc.attention_bwd_head(qf[b, h], kf[b, h], vf[b, h], dof[b, h], w.tau, True)
+        for name in ("dq", "dk", "dv"):
+            assert_close(g[name][b, h], ref[name], "bf16", "%s[%d,%d]" % (name, b, h))
+    # sum_j dV_j = sum_i dO_i and sum_j dK_j = 0 hold for every head (rows of P sum to 1)
+    sdv = g["dv"].sum(axis=2)
+    sdo = dof.sum(axis=2)
+    assert np.abs(sdv - sdo).max() <= 0.5, np.abs(sdv - sdo).max()
+    assert np.abs(g["dk"].sum(axis=2)).max() <= 0.5, np.abs(g["dk"].sum(axis=2)).max()
+    for name in ("dq", "dk", "dv"):
+        assert np.all(np.isfinite(g[name]))
+
+
+def test_bwd_deterministic():
+    import io_aware_tiled_03_amd as fa
+    import torch
+    x = fa_inputs.dense_inputs(2, 2, 700, 64, "bf16", 10500, with_do=True)
+    q, k, v, do = (to_device(x[n]) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, causal=True)
+    a = fa.bwd(q, k, v, o, lse, do, causal=True)
+    b = fa.bwd(q, k, v, o, lse, do, causal=True)
+    for t1, t2 in zip(a, b):
+        assert torch.equal(t1, t2)

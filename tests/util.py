@@ -1,0 +1,44 @@
+"""Helpers for the parity tests: upload seeded host tensors and compare to the oracle."""
+import numpy as np
+
+# Tolerances on |GPU - oracle| (absolute), per output and input dtype.
+TOL = {
+    "bf16": {"max": 2e-2, "mean": 2e-3, "lse": 1e-3},
+    "f32": {"max": 1e-5, "mean": 1e-5, "lse": 1e-5},
+}
+
+
+def to_device(ht, device="cuda"):
+    """HostTensor -> torch tensor on the GPU holding exactly the same bits."""
+    import torch
+    if ht.dtype == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(ht.raw).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(ht.raw))
+    return t.to(device)
+
+
+def to_f64(t):
+    """GPU tensor -> float64 numpy array (exact widening)."""
+    import torch
+    return t.detach().to("cpu", torch.float64).numpy()
+
+
+def err_stats(got, ref):
+    d = np.abs(np.asarray(got, dtype=np.float64) - np.asarray(ref, dtype=np.float64))
+    return float(d.max()) if d.size else 0.0, float(d.mean()) if d.size else 0.0
+
+
+def assert_close(got, ref, dtype, what, kind="out"):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), "%s: non-finite values" % what
+    mx, mean = err_stats(got, ref)
+    tol = TOL[dtype]
+    if kind == "lse":
+        assert mx <= tol["lse"], "%s: max |err| %.3g > %.3g" % (what, mx, tol["lse"])
+    else:
+        assert mx <= tol["max"], "%s: max |err| %.3g > %.3g (mean %.3g)" % (what, mx, tol["max"], mean)
+        assert mean <= tol["mean"], "%s: mean |err| %.3g > %.3g" % (what, mean, tol["mean"])
+    return mx, mean
