@@ -156,8 +156,8 @@ def cpu_baseline(xh, B, H, N, d, tau, budget_s=10.0):
     heads, flops = 0, 0.0
     t0 = time.perf_counter()
     per_head = algorithmic_step_flops(1, 1, N, d)
-    for idx in range(B * H):
-        b, h = divmod(idx, H)
+    for it in range(1 << 30):
+        b, h = divmod(it % (B * H), H)
         orc.attention_fwd_head(qf[b, h], kf[b, h], vf[b, h], tau, False)
         orc.attention_fwd_head(qf[b, h], kf[b, h], vf[b, h], tau, True)
         orc.attention_bwd_head(qf[b, h], kf[b, h], vf[b, h], dof[b, h], tau, True)
@@ -170,8 +170,9 @@ def cpu_baseline(xh, B, H, N, d, tau, budget_s=10.0):
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
             "cores": threads or os.cpu_count(), "kind": "oracle",
-            "sample": "%d of %d (b,h) heads of the step (fwd non-causal, fwd causal, bwd causal, "
-                      "decode), float64 NumPy, %.1f s" % (heads, B * H, dt)}
+            "sample": "%d (b,h) heads (cycling over the %d of the batch) of the step: fwd "
+                      "non-causal, fwd causal, bwd causal, decode; float64 NumPy, %.1f s"
+                      % (heads, B * H, dt)}
 
 
 def bench_extra(fa, reps=20):
@@ -254,6 +255,9 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB five times "
+                         "(scales the HBM byte counters of a profiler run) and exit")
     args = ap.parse_args(argv)
     if args.gpus != 1:
         print("bench.py: this attention path runs on one GPU; --gpus %d is not supported "
@@ -271,6 +275,15 @@ def main(argv=None):
         print("bench.py: no GPU visible", file=sys.stderr)
         return 2
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": n, "launches": 5}))
+        return 0
 
     w = fa_inputs.WORKLOADS[2]
     B, H, N, d, tau = w.B, w.H, w.N, w.d, w.tau
