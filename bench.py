@@ -217,13 +217,18 @@ def bench_extra(fa, reps=20):
     seqlens = fa_inputs.decode_seqlens(B, 1024, 8192, 1004 + 400)
     g.manual_seed(1004)
     q = torch.randn(B, H, 1, d, device=dev, generator=g).to(torch.bfloat16)
-    k = torch.randn(B, H, N, d, device=dev, generator=g).to(torch.bfloat16)
-    v = torch.randn(B, H, N, d, device=dev, generator=g).to(torch.bfloat16)
+    k = torch.empty(B, H, N, d, device=dev, dtype=torch.bfloat16)
+    v = torch.empty_like(k)
+    for b in range(B):   # one sequence at a time keeps each draw far below 2^31 elements
+        k[b] = torch.randn(H, N, d, device=dev, generator=g).to(torch.bfloat16)
+        v[b] = torch.randn(H, N, d, device=dev, generator=g).to(torch.bfloat16)
     sl = torch.from_numpy(seqlens).to(dev)
     o = torch.empty_like(q)
     lse = torch.empty(B, H, device=dev)
     ws = torch.empty(fa.decode_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
     ms = time_it(lambda: fa.decode(q, k, v, sl, 1 / math.sqrt(d), 0, o, lse, ws), reps * 2)
+    if not bool(torch.isfinite(o.float()).all()):
+        raise RuntimeError("decode produced non-finite output")
     nbytes = float(seqlens.astype("int64").sum()) * H * d * 2 * 2 + 2 * B * H * d * 2 + B * H * 4
     out["decode_splitkv"] = {"shape": [B, H, N, d], "seqlens_sum": int(seqlens.sum()),
                              "num_splits": fa.decode_num_splits(B, H, N, d),

@@ -18,7 +18,9 @@ import ctypes
 import math
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+# FA_LIB may name another build of the same library (for example a tuning build).
+LIB_PATH = os.environ.get("FA_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                    "libfa.so")
 
 FA_F32, FA_BF16 = 0, 1
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED",

@@ -14,6 +14,7 @@ from __future__ import annotations
 
 import argparse
 import concurrent.futures as cf
+import hashlib
 import os
 import subprocess
 import sys
@@ -47,30 +48,42 @@ def _run(cmd, verbose):
     return out
 
 
-def build(jobs: int = 4, verbose: bool = False) -> str:
-    """Compile every source and link libfa.so; returns the library path."""
-    os.makedirs(OUT_DIR, exist_ok=True)
+def build(jobs: int = 4, verbose: bool = False, defines=(), out: str = LIB) -> str:
+    """Compile every source and link the library (default libfa.so); returns its path.
+
+    `defines` are extra -D macros (tile and launch parameters) for tuning builds,
+    which should go to another `out` path."""
+    if out == LIB:
+        obj_dir = OUT_DIR
+    else:   # objects of a tuning build sit beside that library
+        obj_dir = os.path.join(os.path.dirname(out), "_build",
+                               hashlib.sha1(out.encode()).hexdigest()[:8])
+    os.makedirs(obj_dir, exist_ok=True)
+    dflags = ["-D" + d for d in defines]
     objs, cmds = [], []
     for src in SOURCES:
-        obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(obj_dir, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmds.append([HIPCC] + FLAGS + lang + ["-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC] + FLAGS + dflags + lang + ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:
             f.result()
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("-j", "--jobs", type=int, default=4)
     ap.add_argument("-v", "--verbose", action="store_true")
+    ap.add_argument("-D", dest="defines", action="append", default=[],
+                    help="extra preprocessor define for a tuning build")
+    ap.add_argument("-o", "--out", default=LIB, help="library path (default: in-tree libfa.so)")
     args = ap.parse_args(argv)
-    print(build(args.jobs, args.verbose))
+    print(build(args.jobs, args.verbose, args.defines, os.path.abspath(args.out)))
 
 
 if __name__ == "__main__":

@@ -78,7 +78,7 @@ int fa_decode(const void* q, const void* k, const void* v, const int* seqlens_k,
     const size_t need = fa::decode_ws_bytes(B, H, d, S);
     if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FA_ERR_ALIGN;
-    if (B > 65535 || H > 65535 || !grid_ok((long long)S * B * H, 256)) return FA_ERR_SHAPE;
+    if (!grid_ok((long long)S * B * H, 256)) return FA_ERR_SHAPE;
     float* ws = (float*)workspace;
     const size_t n_o = (size_t)S * B * H * d;
     fa::DecodeArgs a{q, k, v, seqlens_k, B, H, N_max, d, tau, o, lse, S,

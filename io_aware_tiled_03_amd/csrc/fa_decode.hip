@@ -41,22 +41,58 @@ template <> struct Elem<float> {      // fp32: 4 elements per 16-byte piece
     }
 };
 
+// Sum of a partial dot product over the CPR lanes that hold one key row.
+template <int CPR>
+__device__ __forceinline__ float row_sum(float x) {
+    if constexpr (CPR <= 16) {
+        return group_sum<CPR>(x);
+    } else {
+        x = group_sum<16>(x);
+        return x + __shfl_xor(x, 16, 64);
+    }
+}
+
+#ifndef FA_DECODE_U
+#define FA_DECODE_U 4
+#endif
+#ifndef FA_DECODE_ROTATE
+#define FA_DECODE_ROTATE 0
+#endif
+#ifndef FA_DECODE_NT
+#define FA_DECODE_NT 1
+#endif
+
+// Streaming 16-byte load of the KV cache (read once: optionally non-temporal).
+__device__ __forceinline__ u32x4 ld16_stream(const void* p) {
+#if FA_DECODE_NT
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+#else
+    return ld16(p);
+#endif
+}
+
 template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_split_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
-    const int* __restrict__ seqlens, int H, int N_max, int chunk, float scale_log2, float tau,
-    float* __restrict__ ws_o, float* __restrict__ ws_lse) {
+    const int* __restrict__ seqlens, int B, int H, int N_max, int chunk, float scale_log2,
+    float tau, float* __restrict__ ws_o, float* __restrict__ ws_lse) {
     constexpr int PER = Elem<T>::PER16;
     constexpr int CPR = D / PER;          // lanes per key row
     constexpr int KPL = 64 / CPR;         // keys per wave load instruction
-    constexpr int U = 8;                  // loads in flight per operand
-    constexpr int KPI = U * KPL;          // keys per wave iteration
-    const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-    const int S = gridDim.x, B = gridDim.z;
+    constexpr int U = FA_DECODE_U;        // loads per operand per pipeline stage
+    constexpr int KPI = U * KPL;          // keys per wave per stage
+    // Linear grid with (b, h) fastest: consecutive workgroups, which the
+    // dispatcher deals round-robin to the 8 XCDs, belong to different
+    // sequences, so every XCD gets a share of every split index (high splits
+    // are often empty); split 0, always full, is dispatched first.
+    const int BH = H * B;
+    const int s = (int)(blockIdx.x / (unsigned)BH);
+    const int bhi = (int)(blockIdx.x % (unsigned)BH);
+    const int b = bhi / H, h = bhi % H;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int c = lane % CPR, g = lane / CPR;
-    const size_t bh = (size_t)b * H + h;
-    const size_t wsi = ((size_t)s * B + b) * H + h;
+    const size_t bh = (size_t)bhi;
+    const size_t wsi = (size_t)s * BH + bhi;
 
     const int L = min(max(seqlens[b], 0), N_max);
     const int kb = s * chunk, ke = min(L, kb + chunk);
@@ -75,18 +111,17 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
 #pragma unroll
     for (int i = 0; i < PER; ++i) o[i] = 0.f;
 
-    for (int k0 = kb + wave * KPI; k0 < ke; k0 += 4 * KPI) {
-        u32x4 kr[U], vr[U];
+    // Keys past ke are clamped to row ke-1 (always a valid row, so finite) and
+    // their scores are masked to -inf: no branch around any load.
+    auto load = [&](u32x4* kr, u32x4* vr, int k0) {
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            const int key = k0 + u * KPL + g;
-            kr[u] = key < ke ? ld16(Kb + (size_t)key * D) : u32x4{0, 0, 0, 0};
+            const size_t row = (size_t)min(k0 + u * KPL + g, ke - 1) * D;
+            kr[u] = ld16_stream(Kb + row);
+            vr[u] = ld16_stream(Vb + row);
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int key = k0 + u * KPL + g;
-            vr[u] = key < ke ? ld16(Vb + (size_t)key * D) : u32x4{0, 0, 0, 0};
-        }
+    };
+    auto consume = [&](const u32x4* kr, const u32x4* vr, int k0) {
         float sc[U];
         float mx = neg_inf();
 #pragma unroll
@@ -96,8 +131,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
             float acc = 0.f;
 #pragma unroll
             for (int i = 0; i < PER; ++i) acc = __builtin_fmaf(qv[i], kv[i], acc);
-#pragma unroll
-            for (int off = 1; off < CPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
+            acc = row_sum<CPR>(acc);
             sc[u] = (k0 + u * KPL + g < ke) ? acc : neg_inf();
             mx = fmaxf(mx, sc[u]);
         }
@@ -119,6 +153,36 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
             for (int i = 0; i < PER; ++i) o[i] = __builtin_fmaf(p, vv[i], o[i]);
         }
         m = mnew;
+    };
+
+    // The chunk is walked in stages of KPI keys; wave w takes stages w, w+4, ...
+    // Each workgroup starts at a rotated stage so that concurrently running
+    // workgroups, whose chunks begin at large power-of-two offsets, do not all
+    // hit the same HBM channels in lock step (the softmax merge does not depend
+    // on the order of the keys).  Two register stages: the loads of the next
+    // keys are in flight while the current ones are consumed.
+    const int nst = (ke - kb + KPI - 1) / KPI;
+    const int rot = (int)(blockIdx.x % (unsigned)nst) * FA_DECODE_ROTATE;
+    auto stage_key = [&](int t) {
+        int p = t + rot;
+        p = p >= nst ? p - nst : p;
+        return kb + p * KPI;
+    };
+    int t = wave;
+    if (t < nst) {
+        u32x4 ka[U], va[U], kn[U], vn[U];
+        load(ka, va, stage_key(t));
+        while (true) {
+            const int t1 = t + 4;
+            if (t1 < nst) load(kn, vn, stage_key(t1));
+            consume(ka, va, stage_key(t));
+            if (t1 >= nst) break;
+            const int t2 = t1 + 4;
+            if (t2 < nst) load(ka, va, stage_key(t2));
+            consume(kn, vn, stage_key(t1));
+            if (t2 >= nst) break;
+            t = t2;
+        }
     }
     // combine the KPL key groups of the wave (lanes with equal c)
 #pragma unroll
@@ -197,8 +261,8 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
 
 template <typename T, int D>
 void launch(const DecodeArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(a.num_splits, a.H, a.B), dim3(256), 0, st,
-                       (const T*)a.q, (const T*)a.k, (const T*)a.v, a.seqlens, a.H, a.N_max,
+    hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(a.num_splits * a.B * a.H), dim3(256), 0, st,
+                       (const T*)a.q, (const T*)a.k, (const T*)a.v, a.seqlens, a.B, a.H, a.N_max,
                        a.chunk, a.tau * kLog2e, a.tau, a.ws_o, a.ws_lse);
     hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.B * a.H), dim3(64), 0, st, a.ws_o,
                        a.ws_lse, a.num_splits, a.B * a.H, (T*)a.o, a.lse);

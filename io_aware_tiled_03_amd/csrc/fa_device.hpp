@@ -55,8 +55,57 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
+// DPP lane moves inside a row of 16 lanes (no LDS round trip).
+enum : int {
+    kDppXor1 = 0xB1,        // quad_perm [1,0,3,2]
+    kDppXor2 = 0x4E,        // quad_perm [2,3,0,1]
+    kDppRowRor4 = 0x124,    // rotate the 16-lane row by 4
+    kDppRowRor8 = 0x128,    // rotate the 16-lane row by 8
+    kDppHalfMirror = 0x141  // reverse each group of 8 lanes
+};
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of G lanes (G = 8 or 16); every lane gets its group's sum.
+template <int G>
+__device__ __forceinline__ float group_sum(float x) {
+    static_assert(G == 8 || G == 16, "group of 8 or 16 lanes");
+    x += dpp_mov<kDppXor1>(x);
+    x += dpp_mov<kDppXor2>(x);
+    if constexpr (G == 8) {
+        x += dpp_mov<kDppHalfMirror>(x);
+    } else {
+        x += dpp_mov<kDppRowRor4>(x);
+        x += dpp_mov<kDppRowRor8>(x);
+    }
+    return x;
+}
+
 // Value held by lane (lane ^ 32): swaps the two halves of the wave.
 __device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32, 64); }
+
+// Transposing LDS read (ds_read_b64_tr_b16).  Within each group of 16 lanes,
+// lane i receives 16-bit element (i % 4) of the 8-byte pieces addressed by
+// lanes 4j + i/4 of its group, for j = 0..3.  So if lane s of a group
+// addresses row r0 + s/4, columns c0 + 4*(s%4) .. +3 of a row-major 16-bit
+// matrix, lane i receives rows r0..r0+3 of column c0 + i: a column-major piece
+// of a row-major tile, ready as MFMA operand slots.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* lds) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+    const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds));
+    return __builtin_bit_cast(u32x2, r);
+}
+
+// a.lo*b.lo + a.hi*b.hi + c for packed bf16 pairs, fp32 accumulation.
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
+                                           __builtin_bit_cast(bf16x2, b), c, false);
+}
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }

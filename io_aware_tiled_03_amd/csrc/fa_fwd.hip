@@ -13,14 +13,21 @@
 //    operand of S^T = K Q^T, so in the result every lane holds one query
 //    (column) and 16 keys per 32-key block (rows): the row max/sum of the
 //    softmax is a register loop plus one exchange between wave halves;
-//  * K rows are read from LDS in the order pi(m) (see kperm) chosen so that
-//    the registers of S^T already hold, per lane half, 8 consecutive keys:
-//    the bf16-rounded P^T feeds the P V product as the B operand directly;
-//  * V is staged transposed in LDS (V^T rows = head-dim index) so the A
-//    operand of O^T = V^T P^T is one 16-byte read per lane;
+//  * K rows are stored in LDS in the order pi^-1 (see kperm/kperm_inv) so that
+//    lane m reading physical row m gets key pi(m), chosen such that the
+//    registers of S^T already hold, per lane half, 8 consecutive keys: the
+//    bf16-rounded P^T feeds the P V product as the B operand directly;
+//  * V stays row-major in LDS; the A operand of O^T = V^T P^T comes from the
+//    transposing LDS read, four keys of one head-dim column per 8-byte read;
+//  * K and V tiles are double-buffered in LDS (one barrier per tile), the next
+//    tile's global loads are in flight during the current tile's math;
 //  * the loop runs over key tiles in order and, under the causal mask, stops
 //    at the diagonal tile; waves whose rows precede the whole tile skip it;
-//  * exp2 with tau*log2(e) folded into one FMA; O is normalised once at the end.
+//  * exp2 with tau*log2(e) folded into one FMA; the running reference max is
+//    only moved (and O rescaled) when a score exceeds it by more than 2^8, so
+//    most tiles skip the rescale; O is normalised once at the end.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
@@ -28,16 +35,42 @@ namespace fa {
 
 namespace {
 
-// Row of the K tile that lane-row m reads so that C-register r of lane half h
-// holds key 16*(r/8) + 8*h + r%8 of the 32-key block (see header comment).
+// Key (within a 32-key block) that lane-row m of the S^T MFMA must hold so
+// that C-register r of lane half h holds key 16*(r/8) + 8*h + r%8.
 __device__ __forceinline__ int kperm(int m) {
     const int j = 4 * (m >> 3) + (m & 3);
     return 16 * (j >> 3) + 8 * ((m >> 2) & 1) + (j & 7);
 }
+// Inverse of kperm: the LDS row that key r of a 32-key block is stored in.
+__device__ __forceinline__ int kperm_inv(int r) {
+    return 8 * (2 * (r >> 4) + ((r >> 2) & 1)) + 4 * ((r >> 3) & 1) + (r & 3);
+}
 
-// XOR swizzles of the 16-byte chunk index inside an LDS row.
-__device__ __forceinline__ int swz_k(int row) { return (row & 3) | ((row & 8) >> 1); }
-__device__ __forceinline__ int swz_vt(int row) { return row & 7; }
+#ifndef FA_FWD_RESCALE_LOG2
+#define FA_FWD_RESCALE_LOG2 8.0f
+#endif
+#ifndef FA_FWD_KPAD
+#define FA_FWD_KPAD 8        // K row padding (bf16 elements)
+#endif
+#ifndef FA_FWD_VPAD
+#define FA_FWD_VPAD 16       // V row padding (bf16 elements)
+#endif
+#ifndef FA_FWD_PRIO
+#define FA_FWD_PRIO 0        // raise wave priority while issuing MFMA chains
+#endif
+
+__device__ __forceinline__ void prio_hi() {
+#if FA_FWD_PRIO
+    __builtin_amdgcn_s_setprio(1);
+#endif
+}
+__device__ __forceinline__ void prio_lo() {
+#if FA_FWD_PRIO
+    __builtin_amdgcn_s_setprio(0);
+#endif
+}
+
+template <int N_> using ic = std::integral_constant<int, N_>;
 
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
@@ -45,12 +78,12 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int N, float scale_log2, float tau,
     int n_qtiles) {
     constexpr int BR = 128, BC = 64;
-    constexpr int KCH = D / 8;             // 16-byte chunks per K row
-    constexpr int KPT = BC * KCH / 256;    // K chunks staged per thread
-    constexpr int VPT = KCH / 4;           // V chunks staged per thread
-    constexpr int VTCH = BC / 8;           // 16-byte chunks per V^T row
-    __shared__ u32x4 sK[BC * KCH];
-    __shared__ u32x4 sVt[D * VTCH];
+    constexpr int KCH = D / 8;             // 16-byte chunks per row
+    constexpr int KSTR = D + FA_FWD_KPAD;  // K row stride (elements), padded against bank conflicts
+    constexpr int VSTR = D + FA_FWD_VPAD;  // V row stride (elements)
+    constexpr int CPT = BC * KCH / 256;    // chunks of K (and of V) staged per thread
+    __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[2][BC * VSTR];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 31, hf = lane >> 5;
@@ -71,119 +104,158 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] = 0.f;
-    float m = neg_inf(), l = 0.f;
+    float m = neg_inf(), l = 0.f;   // reference max (raw score units) and lane-partial sum
 
     const int kend = CAUSAL ? min(N, q0 + BR) : N;
     const int ntiles = (kend + BC - 1) / BC;
-    const int prow = kperm(ln);
+    const int nfull = N / BC;       // tiles with no key past N
 
-    u32x4 kreg[KPT], vreg[VPT];
+    // Staging: thread -> (row, chunk) pairs, 16 threads per d=128 row.  Rows
+    // past N (tail tile only) are clamped to row N-1: their scores are masked
+    // to -inf and their V rows meet p = 0, so any finite row will do.
+    const int srow = tid / KCH, sch = tid % KCH;   // + 256/KCH rows per u
+    const uint16_t* kg = K + base + (size_t)srow * D + sch * 8;
+    const uint16_t* vg = V + base + (size_t)srow * D + sch * 8;
+    u32x4 kreg[CPT], vreg[CPT];
     auto gload = [&](int j) {
         const int k0 = j * BC;
+        if (j < nfull) {
 #pragma unroll
-        for (int u = 0; u < KPT; ++u) {
-            const int idx = tid + 256 * u, row = idx / KCH, ch = idx % KCH, key = k0 + row;
-            kreg[u] = key < N ? ld16(K + base + (size_t)key * D + ch * 8) : u32x4{0, 0, 0, 0};
-        }
+            for (int u = 0; u < CPT; ++u) {
+                const size_t off = (size_t)(k0 + u * (256 / KCH)) * D;
+                kreg[u] = ld16(kg + off);
+                vreg[u] = ld16(vg + off);
+            }
+        } else {
 #pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-            const int ch = wave + 4 * u, key = k0 + lane;
-            vreg[u] = key < N ? ld16(V + base + (size_t)key * D + ch * 8) : u32x4{0, 0, 0, 0};
-        }
-    };
-    auto lstore = [&]() {
-#pragma unroll
-        for (int u = 0; u < KPT; ++u) {
-            const int idx = tid + 256 * u, row = idx / KCH, ch = idx % KCH;
-            sK[row * KCH + (ch ^ swz_k(row))] = kreg[u];
-        }
-        uint16_t* vt = reinterpret_cast<uint16_t*>(sVt);
-#pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-            const int ch = wave + 4 * u;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int d = ch * 8 + e;
-                const uint32_t w = vreg[u][e >> 1];
-                vt[d * BC + (((lane >> 3) ^ swz_vt(d)) << 3) + (lane & 7)] =
-                    (uint16_t)((e & 1) ? (w >> 16) : (w & 0xffff));
+            for (int u = 0; u < CPT; ++u) {
+                const size_t off = (size_t)(min(k0 + srow + u * (256 / KCH), N - 1) - srow) * D;
+                kreg[u] = ld16(kg + off);
+                vreg[u] = ld16(vg + off);
             }
         }
     };
+    // LDS element offsets of this thread's staging stores (K rows permuted)
+    int kst[CPT], vst[CPT];
+#pragma unroll
+    for (int u = 0; u < CPT; ++u) {
+        const int row = srow + u * (256 / KCH);
+        kst[u] = ((row & ~31) + kperm_inv(row & 31)) * KSTR + sch * 8;
+        vst[u] = row * VSTR + sch * 8;
+    }
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int u = 0; u < CPT; ++u) {
+            st16(&sK[buf][kst[u]], kreg[u]);
+            st16(&sV[buf][vst[u]], vreg[u]);
+        }
+    };
+    // Per-lane offsets of the operand reads.  K: physical row kb*32 + ln.
+    // V (transposing read): lane s of 16-lane group G reads key 8*(G/2) + s/4
+    // (+4 for slots 4..7), columns 16*(G%2) + 4*(s%4).
+    const int k_off = ln * KSTR + hf * 8;
+    const int G = lane >> 4, sl = lane & 15;
+    const int v_off = (8 * (G >> 1) + (sl >> 2)) * VSTR + 16 * (G & 1) + 4 * (sl & 3);
 
-    gload(0);
-    for (int j = 0; j < ntiles; ++j) {
-        lstore();
-        __syncthreads();
-        if (j + 1 < ntiles) gload(j + 1);
-        const int k0 = j * BC;
-        const bool active = !CAUSAL || k0 <= qw + 31;
-        if (active) {
-            f32x16 s[2];
+    // One key tile from LDS buffer BUF; MASK selects the masked variant (tail
+    // tile, or a tile crossing this wave's diagonal under the causal mask).
+    auto compute = [&](int buf, auto maskc, int k0) {
+        constexpr bool MASK = decltype(maskc)::value != 0;
+        f32x16 s[2];
+        prio_hi();
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
-                const int row = kb * 32 + prow;
+            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
+            u32x4 ka[D / 16];   // all operands of the block first, then the MFMA chain
 #pragma unroll
-                for (int ks = 0; ks < D / 16; ++ks) {
-                    const u32x4 a = sK[row * KCH + ((ks * 2 + hf) ^ swz_k(row))];
-                    s[kb] = mfma32x32x16(a, qf[ks], s[kb]);
-                }
-            }
-            const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw);
-            if (need_mask) {
+            for (int ks = 0; ks < D / 16; ++ks) ka[ks] = ld16(&sK[buf][k_off + kb * 32 * KSTR + ks * 16]);
 #pragma unroll
-                for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7);
-                        if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = neg_inf();
-                    }
-            }
-            float mx = s[0][0];
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-            mx = fmaxf(mx, xor32(mx));
-            const float mnew = fmaxf(m, mx);
-            const float alpha = fast_exp2((m - mnew) * scale_log2);
-            const float mc = mnew * scale_log2;
-            float rs = 0.f;
+            for (int ks = 0; ks < D / 16; ++ks) s[kb] = mfma32x32x16(ka[ks], qf[ks], s[kb]);
+        }
+        prio_lo();
+        if constexpr (MASK) {
 #pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    const float p = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, -mc));
-                    s[kb][r] = p;
-                    rs += p;
+                    const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7);
+                    if (key >= N || (CAUSAL && key > qrow)) s[kb][r] = neg_inf();
                 }
-            l = l * alpha + rs;
-            m = mnew;
+        }
+        float mx = s[0][0];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+        mx = fmaxf(mx, xor32(mx));
+        // Move the reference max only when some score exceeds it by more than
+        // 2^FA_FWD_RESCALE_LOG2 (then P <= 2^8 stays well inside fp32/bf16 range).
+        const bool grow = (mx - m) * scale_log2 > FA_FWD_RESCALE_LOG2;
+        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+            const float mnew = fmaxf(m, mx);
+            const float alpha = fast_exp2((m - mnew) * scale_log2);
+            l *= alpha;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) {
-                    u32x4 pf;
-#pragma unroll
-                    for (int w = 0; w < 4; ++w)
-                        pf[w] = pack_bf16x2(s[kb][8 * t + 2 * w], s[kb][8 * t + 2 * w + 1]);
-                    const int vch = kb * 4 + 2 * t + hf;
-#pragma unroll
-                    for (int db = 0; db < D / 32; ++db) {
-                        const int d = db * 32 + ln;
-                        const u32x4 a = sVt[d * VTCH + (vch ^ swz_vt(d))];
-                        oacc[db] = mfma32x32x16(a, pf, oacc[db]);
-                    }
-                }
+            m = mnew;
         }
+        const float mc = m * scale_log2;
+        u32x4 pf[2][2];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const int r = 8 * t + 2 * w;
+                    const float p0 = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, -mc));
+                    const float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], scale_log2, -mc));
+                    pf[kb][t][w] = pack_bf16x2(p0, p1);
+                    l += p0 + p1;
+                }
+        prio_hi();
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int vb = v_off + (kb * 32 + 16 * t) * VSTR;
+                u32x4 va[D / 32];
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    const u32x2 lo = lds_read_tr16(&sV[buf][vb + db * 32]);
+                    const u32x2 hi = lds_read_tr16(&sV[buf][vb + db * 32 + 4 * VSTR]);
+                    va[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                }
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) oacc[db] = mfma32x32x16(va[db], pf[kb][t], oacc[db]);
+            }
+        prio_lo();
+    };
+
+    auto tile = [&](int j, auto maskc) {
+        const int buf = j & 1;
+        if (j + 1 < ntiles) gload(j + 1);
+        const int k0 = j * BC;
+        if constexpr (decltype(maskc)::value != 0) {
+            if (!CAUSAL || k0 <= qw + 31) compute(buf, maskc, k0);   // rows all before the tile: skip
+        } else {
+            compute(buf, maskc, k0);
+        }
+        if (j + 1 < ntiles) lstore(buf ^ 1);
         __syncthreads();
-    }
+    };
+    // Tiles before jsplit need no mask in any wave: no key past N and, under
+    // the causal mask, every key precedes the workgroup's first query row.
+    const int jsplit = min(CAUSAL ? q0 / BC : ntiles, nfull);
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    int j = 0;
+    for (; j < jsplit; ++j) tile(j, ic<0>{});
+    for (; j < ntiles; ++j) tile(j, ic<1>{});
 
     l += xor32(l);
     const float inv = 1.f / l;
