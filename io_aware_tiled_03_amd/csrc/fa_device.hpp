@@ -108,6 +108,27 @@ __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
 }
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
+
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 descriptor word 3 =
+// 0x00020000).  Loads at byte offsets at or past `bytes` return zero, so a
+// tile that runs past the end of a tensor needs no branch and no clamp.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                             0x00020000);
+}
+__device__ __forceinline__ u32x4 buf_ld16(rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
+}
+// Direct global -> LDS copy of 16 bytes per lane: lane i's bytes land at
+// lds_base + 16*i (lds_base must be the same for the whole wave).  Completion
+// is tracked by vmcnt, not by any register: wait with wait_vmem() before a
+// barrier that publishes the data.
+__device__ __forceinline__ void buf_ld16_lds(rsrc_t r, uint32_t byte_off, void* lds_base) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
+                                             byte_off, 0, 0, 0);
+}
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 }  // namespace fa

@@ -110,45 +110,39 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     const int ntiles = (kend + BC - 1) / BC;
     const int nfull = N / BC;       // tiles with no key past N
 
-    // Staging: thread -> (row, chunk) pairs, 16 threads per d=128 row.  Rows
-    // past N (tail tile only) are clamped to row N-1: their scores are masked
-    // to -inf and their V rows meet p = 0, so any finite row will do.
-    const int srow = tid / KCH, sch = tid % KCH;   // + 256/KCH rows per u
-    const uint16_t* kg = K + base + (size_t)srow * D + sch * 8;
-    const uint16_t* vg = V + base + (size_t)srow * D + sch * 8;
-    u32x4 kreg[CPT], vreg[CPT];
-    auto gload = [&](int j) {
-        const int k0 = j * BC;
-        if (j < nfull) {
+    // Staging: direct global -> LDS copies.  A wave instruction fills 1 KB of
+    // LDS (lane i -> 16 bytes at +16*i), so each lane loads whichever global
+    // 16-byte chunk belongs at its LDS position: K rows are stored permuted
+    // (physical row p holds key kperm(p)), rows are padded, and padding
+    // positions load a duplicate chunk that is never read.  Rows past N read
+    // as zeros through the buffer descriptor (their scores are masked to -inf
+    // and their V rows meet p = 0).  Wave w issues instructions w, w+4, ...
+    constexpr int KCPR = KSTR / 8, VCPR = VSTR / 8;      // 16-byte chunks per padded row
+    constexpr int KNI = BC * KCPR / 64, VNI = BC * VCPR / 64;   // wave instructions per tile
+    constexpr int KPW = (KNI + 3) / 4, VPW = (VNI + 3) / 4;     // per wave (upper bound)
+    static_assert(BC * KCPR % 64 == 0 && BC * VCPR % 64 == 0, "whole wave instructions");
+    const rsrc_t krs = make_rsrc(K + base, (uint32_t)N * D * 2);
+    const rsrc_t vrs = make_rsrc(V + base, (uint32_t)N * D * 2);
+    uint32_t kgo[KPW], vgo[VPW];   // byte offsets inside a tile (tile start added per tile)
 #pragma unroll
-            for (int u = 0; u < CPT; ++u) {
-                const size_t off = (size_t)(k0 + u * (256 / KCH)) * D;
-                kreg[u] = ld16(kg + off);
-                vreg[u] = ld16(vg + off);
-            }
-        } else {
-#pragma unroll
-            for (int u = 0; u < CPT; ++u) {
-                const size_t off = (size_t)(min(k0 + srow + u * (256 / KCH), N - 1) - srow) * D;
-                kreg[u] = ld16(kg + off);
-                vreg[u] = ld16(vg + off);
-            }
-        }
-    };
-    // LDS element offsets of this thread's staging stores (K rows permuted)
-    int kst[CPT], vst[CPT];
-#pragma unroll
-    for (int u = 0; u < CPT; ++u) {
-        const int row = srow + u * (256 / KCH);
-        kst[u] = ((row & ~31) + kperm_inv(row & 31)) * KSTR + sch * 8;
-        vst[u] = row * VSTR + sch * 8;
+    for (int t = 0; t < KPW; ++t) {
+        const int pos = (wave + 4 * t) * 64 + lane, prow = pos / KCPR, c = pos % KCPR;
+        const int key = (prow & ~31) + kperm(prow & 31);
+        kgo[t] = (uint32_t)(key * D + (c < KCH ? c : 0) * 8) * 2;
     }
-    auto lstore = [&](int buf) {
 #pragma unroll
-        for (int u = 0; u < CPT; ++u) {
-            st16(&sK[buf][kst[u]], kreg[u]);
-            st16(&sV[buf][vst[u]], vreg[u]);
-        }
+    for (int t = 0; t < VPW; ++t) {
+        const int pos = (wave + 4 * t) * 64 + lane, row = pos / VCPR, c = pos % VCPR;
+        vgo[t] = (uint32_t)(row * D + (c < KCH ? c : 0) * 8) * 2;
+    }
+    auto stage = [&](int j, int buf) {   // issue the copies of tile j into buffer buf
+        const uint32_t t0 = (uint32_t)j * (BC * D * 2);
+#pragma unroll
+        for (int t = 0; t < KPW; ++t)
+            if (wave + 4 * t < KNI) buf_ld16_lds(krs, kgo[t] + t0, &sK[buf][(wave + 4 * t) * 512]);
+#pragma unroll
+        for (int t = 0; t < VPW; ++t)
+            if (wave + 4 * t < VNI) buf_ld16_lds(vrs, vgo[t] + t0, &sV[buf][(wave + 4 * t) * 512]);
     };
     // Per-lane offsets of the operand reads.  K: physical row kb*32 + ln.
     // V (transposing read): lane s of 16-lane group G reads key 8*(G/2) + s/4
@@ -237,21 +231,21 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
 
     auto tile = [&](int j, auto maskc) {
         const int buf = j & 1;
-        if (j + 1 < ntiles) gload(j + 1);
+        stage(j + 1, buf ^ 1);   // past the last tile: zeros or unused rows, never read back
         const int k0 = j * BC;
         if constexpr (decltype(maskc)::value != 0) {
             if (!CAUSAL || k0 <= qw + 31) compute(buf, maskc, k0);   // rows all before the tile: skip
         } else {
             compute(buf, maskc, k0);
         }
-        if (j + 1 < ntiles) lstore(buf ^ 1);
+        wait_vmem();
         __syncthreads();
     };
     // Tiles before jsplit need no mask in any wave: no key past N and, under
     // the causal mask, every key precedes the workgroup's first query row.
     const int jsplit = min(CAUSAL ? q0 / BC : ntiles, nfull);
-    gload(0);
-    lstore(0);
+    stage(0, 0);
+    wait_vmem();
     __syncthreads();
     int j = 0;
     for (; j < jsplit; ++j) tile(j, ic<0>{});
@@ -341,8 +335,8 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(
 
 template <int D, bool C>
 void launch_bf16(const FwdArgs& a, hipStream_t st) {
-    const int nq = (a.N + 127) / 128;
     const int bh = a.B * a.H;
+    const int nq = (a.N + 127) / 128;
     hipLaunchKernelGGL((fwd_bf16_kernel<D, C>), dim3(nq * bh), dim3(256), 0, st,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.o, a.lse, bh, a.N, a.tau * kLog2e, a.tau, nq);
