@@ -11,16 +11,22 @@
 //  bwd_pre_kernel  : D for every row, an inner product of length d.
 //  bwd_dkdv_kernel : one workgroup per 128-key tile (32 keys per wave, K and V
 //                    of those keys held in registers); loops over 64-query
-//                    tiles staged in LDS both row-major (for S = Q K^T and
-//                    dP = dO V^T, whose results put one key per lane) and
-//                    transposed (for dV^T += dO^T P and dK^T += Q^T dS, whose B
-//                    operands are P and dS straight from registers).
+//                    tiles of Q and dO copied straight into LDS (double
+//                    buffered, one barrier per tile).  S = Q K^T and dP = dO V^T
+//                    read their A operands row-wise (one key per result lane);
+//                    dV^T += dO^T P and dK^T += Q^T dS read dO^T and Q^T with
+//                    the transposing LDS read and take P and dS straight from
+//                    registers as B operands.
 //  bwd_dq_kernel   : one workgroup per 128-query tile (32 queries per wave, Q
-//                    and dO rows in registers); loops over 64-key tiles up to
-//                    the diagonal, recomputing S^T = K Q^T and dP^T = V dO^T
-//                    (one query per lane) and accumulating dQ^T += K^T dS^T.
-// Query rows are read from LDS in the kperm order so that the C registers of
-// each lane half hold 8 consecutive rows, ready to be packed as a B operand.
+//                    and dO rows in registers); loops over 64-key tiles of K
+//                    and V up to the diagonal, recomputing S^T = K Q^T and
+//                    dP^T = V dO^T (one query per lane) and accumulating
+//                    dQ^T += K^T dS^T with K^T from the transposing read.
+// A-operand rows are read in the kperm order so that the C registers of each
+// lane half hold 8 consecutive rows, ready to be packed as a B operand.  Only
+// tiles that cross the causal diagonal run the masked variant.
+#include <type_traits>
+
 #include "fa_device.hpp"
 #include "fa_internal.h"
 
@@ -31,13 +37,6 @@ namespace {
 __device__ __forceinline__ int kperm(int m) {
     const int j = 4 * (m >> 3) + (m & 3);
     return 16 * (j >> 3) + 8 * ((m >> 2) & 1) + (j & 7);
-}
-__device__ __forceinline__ int swz_k(int row) { return (row & 3) | ((row & 8) >> 1); }
-__device__ __forceinline__ int swz_t(int row) { return row & 7; }
-
-__device__ __forceinline__ uint16_t half_of(const u32x4& w, int e) {
-    const uint32_t x = w[e >> 1];
-    return (uint16_t)((e & 1) ? (x >> 16) : (x & 0xffff));
 }
 
 // D_i = sum_d dO_id O_id in fp32; D/8 lanes per row.
@@ -61,6 +60,33 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict
     if (row < rows && c == 0) Dv[row] = acc;
 }
 
+template <int N_> using ic = std::integral_constant<int, N_>;
+
+// Direct global -> LDS staging of a tile of ROWS rows of a [N, D] bf16 matrix
+// into padded LDS rows of STR elements (STR*2 = 16 * odd bytes).  One wave
+// instruction fills 1 KB of LDS; every lane loads the 16-byte chunk that
+// belongs at its LDS position (padding positions load a duplicate chunk that
+// is never read).  Rows past N read as zeros through the buffer descriptor.
+template <int ROWS, int D, int STR, int NWAVES>
+struct TileCopy {
+    static constexpr int CPR = STR / 8, NI = ROWS * CPR / 64, PW = (NI + NWAVES - 1) / NWAVES;
+    static_assert(ROWS * CPR % 64 == 0, "whole wave instructions");
+    uint32_t off[PW];
+    __device__ void init(int wave, int lane) {
+#pragma unroll
+        for (int t = 0; t < PW; ++t) {
+            const int pos = (wave + NWAVES * t) * 64 + lane, row = pos / CPR, c = pos % CPR;
+            off[t] = (uint32_t)(row * D + (c < D / 8 ? c : 0) * 8) * 2;
+        }
+    }
+    __device__ void issue(rsrc_t rs, int row0, uint16_t* lds, int wave) const {
+        const uint32_t t0 = (uint32_t)row0 * (D * 2);
+#pragma unroll
+        for (int t = 0; t < PW; ++t)
+            if (wave + NWAVES * t < NI) buf_ld16_lds(rs, off[t] + t0, lds + (wave + NWAVES * t) * 512);
+    }
+};
+
 template <int D, bool CAUSAL>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -68,9 +94,11 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int N, float scale_log2,
     float tau) {
     constexpr int BC = 128, BR = 64;
-    constexpr int KCH = D / 8, TCH = BR / 8, SPT = KCH / 4;
-    __shared__ u32x4 sQ[BR * KCH], sdO[BR * KCH], sQt[D * TCH], sdOt[D * TCH];
-    __shared__ float sL[BR], sD[BR];
+    constexpr int STR = D + 8;                 // padded row (16 * odd bytes)
+    __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BR * STR];
+    __shared__ __attribute__((aligned(16))) uint16_t sdO[2][BR * STR];
+    __shared__ __attribute__((aligned(16))) float sL[2][BR];
+    __shared__ __attribute__((aligned(16))) float sD[2][BR];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 31, hf = lane >> 5;
@@ -92,80 +120,123 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) { dvacc[db][r] = 0.f; dkacc[db][r] = 0.f; }
 
-    const int prow = kperm(ln);
+    const rsrc_t qrs = make_rsrc(Q + base, (uint32_t)N * D * 2);
+    const rsrc_t ors = make_rsrc(dO + base, (uint32_t)N * D * 2);
+    TileCopy<BR, D, STR, 4> cp;
+    cp.init(wave, lane);
+    // operand read offsets: A operand rows (queries) in kperm order; transposed
+    // operands via the transposing read (lane s of 16-lane group G: row
+    // 8*(G/2) + s/4 (+4), column 16*(G%2) + 4*(s%4))
+    const int a_off = kperm(ln) * STR + hf * 8;
+    const int G = lane >> 4, sl = lane & 15;
+    const int t_off = (8 * (G >> 1) + (sl >> 2)) * STR + 16 * (G & 1) + 4 * (sl & 3);
+
     const int n_qt = (N + BR - 1) / BR;
     const int qt0 = CAUSAL ? k0 / BR : 0;
-    uint16_t* sQt16 = reinterpret_cast<uint16_t*>(sQt);
-    uint16_t* sdOt16 = reinterpret_cast<uint16_t*>(sdOt);
-
-    for (int qt = qt0; qt < n_qt; ++qt) {
+    float ld_l = 0.f, ld_d = 0.f;   // this thread's LSE/D value of the next tile (threads < 128)
+    auto stage = [&](int qt, int buf) {
         const int q0 = qt * BR;
-        __syncthreads();
-        {
-            const int q = q0 + lane;
-#pragma unroll
-            for (int u = 0; u < SPT; ++u) {
-                const int c = wave + 4 * u;
-                const size_t off = base + (size_t)q * D + c * 8;
-                const u32x4 a = q < N ? ld16(Q + off) : u32x4{0, 0, 0, 0};
-                const u32x4 b = q < N ? ld16(dO + off) : u32x4{0, 0, 0, 0};
-                sQ[lane * KCH + (c ^ swz_k(lane))] = a;
-                sdO[lane * KCH + (c ^ swz_k(lane))] = b;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int d = c * 8 + e;
-                    const int pos = d * BR + (((lane >> 3) ^ swz_t(d)) << 3) + (lane & 7);
-                    sQt16[pos] = half_of(a, e);
-                    sdOt16[pos] = half_of(b, e);
-                }
-            }
-            if (wave == 0) sL[lane] = q < N ? LSE[(size_t)bh * N + q] * kLog2e : __builtin_inff();
-            if (wave == 1) sD[lane] = q < N ? Dv[(size_t)bh * N + q] : 0.f;
+        cp.issue(qrs, q0, &sQ[buf][0], wave);
+        cp.issue(ors, q0, &sdO[buf][0], wave);
+        if (tid < 2 * BR) {
+            const int q = q0 + (tid & (BR - 1));
+            if (tid < BR) ld_l = q < N ? LSE[(size_t)bh * N + q] * kLog2e : __builtin_inff();
+            else ld_d = q < N ? Dv[(size_t)bh * N + q] : 0.f;
         }
-        __syncthreads();
-        if (CAUSAL && q0 + BR - 1 < kw) continue;
+    };
+    auto stage_ld = [&](int buf) {
+        if (tid < BR) sL[buf][tid] = ld_l;
+        else if (tid < 2 * BR) sD[buf][tid - BR] = ld_d;
+    };
+
+    auto compute = [&](int buf, int q0, auto maskc) {
+        constexpr bool MASK = decltype(maskc)::value != 0;
+        const uint16_t* q_lds = &sQ[buf][0];
+        const uint16_t* o_lds = &sdO[buf][0];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             const int qs = q0 + qb * 32;
-            if (CAUSAL && qs + 31 < kw) continue;
-            f32x16 s, dp;
+            if (MASK && CAUSAL && qs + 31 < kw) continue;   // all these queries precede the keys
+            f32x16 sacc, dp;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
-            const int row = qb * 32 + prow;
+            for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; dp[r] = 0.f; }
+            u32x4 qa[D / 16], oa[D / 16];
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks) {
-                const int ch = row * KCH + ((ks * 2 + hf) ^ swz_k(row));
-                s = mfma32x32x16(sQ[ch], kf[ks], s);
-                dp = mfma32x32x16(sdO[ch], vf[ks], dp);
+                qa[ks] = ld16(q_lds + qb * 32 * STR + a_off + ks * 16);
+                oa[ks] = ld16(o_lds + qb * 32 * STR + a_off + ks * 16);
             }
-            const bool mask = CAUSAL && (kw + 31 > qs);
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) {
+                sacc = mfma32x32x16(qa[ks], kf[ks], sacc);
+                dp = mfma32x32x16(oa[ks], vf[ks], dp);
+            }
+            // register r holds query qb*32 + 16*(r/8) + 8*hf + r%8 (key = this lane's)
+            f32x4 lq[4], dq4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lq[i] = *reinterpret_cast<const f32x4*>(&sL[buf][qb * 32 + 16 * (i >> 1) + 8 * hf + 4 * (i & 1)]);
+                dq4[i] = *reinterpret_cast<const f32x4*>(&sD[buf][qb * 32 + 16 * (i >> 1) + 8 * hf + 4 * (i & 1)]);
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int ql = qb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7);
-                float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -sL[ql]));
-                if (mask && key > q0 + ql) p = 0.f;
-                s[r] = p;
-                dp[r] = p * (dp[r] - sD[ql]);
+                float p = fast_exp2(__builtin_fmaf(sacc[r], scale_log2, -lq[r >> 2][r & 3]));
+                if constexpr (MASK) {
+                    const int q = qs + 16 * (r >> 3) + 8 * hf + (r & 7);
+                    if (CAUSAL && key > q) p = 0.f;
+                }
+                sacc[r] = p;
+                dp[r] = p * (dp[r] - dq4[r >> 2][r & 3]);
             }
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 u32x4 pf, dsf;
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
-                    pf[w] = pack_bf16x2(s[8 * t + 2 * w], s[8 * t + 2 * w + 1]);
+                    pf[w] = pack_bf16x2(sacc[8 * t + 2 * w], sacc[8 * t + 2 * w + 1]);
                     dsf[w] = pack_bf16x2(dp[8 * t + 2 * w], dp[8 * t + 2 * w + 1]);
                 }
-                const int ch = qb * 4 + 2 * t + hf;
+                const int tb = t_off + (qb * 32 + 16 * t) * STR;
+                u32x4 ot[D / 32], qt4[D / 32];
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const int d = db * 32 + ln;
-                    const int idx = d * TCH + (ch ^ swz_t(d));
-                    dvacc[db] = mfma32x32x16(sdOt[idx], pf, dvacc[db]);
-                    dkacc[db] = mfma32x32x16(sQt[idx], dsf, dkacc[db]);
+                    const u32x2 a0 = lds_read_tr16(o_lds + tb + db * 32);
+                    const u32x2 a1 = lds_read_tr16(o_lds + tb + db * 32 + 4 * STR);
+                    const u32x2 b0 = lds_read_tr16(q_lds + tb + db * 32);
+                    const u32x2 b1 = lds_read_tr16(q_lds + tb + db * 32 + 4 * STR);
+                    ot[db] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+                    qt4[db] = u32x4{b0[0], b0[1], b1[0], b1[1]};
+                }
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    dvacc[db] = mfma32x32x16(ot[db], pf, dvacc[db]);
+                    dkacc[db] = mfma32x32x16(qt4[db], dsf, dkacc[db]);
                 }
             }
         }
+    };
+
+    if (qt0 < n_qt) {
+        stage(qt0, 0);
+        stage_ld(0);
+        wait_vmem();
+        __syncthreads();
     }
+    // query tiles that reach into this workgroup's keys need the causal mask
+    const int qmask_end = CAUSAL ? min(n_qt, (k0 + BC + BR - 1) / BR) : qt0;
+    auto tile = [&](int qt, auto maskc) {
+        const int buf = (qt - qt0) & 1;
+        if (qt + 1 < n_qt) stage(qt + 1, buf ^ 1);
+        const int q0 = qt * BR;
+        if (!(CAUSAL && q0 + BR - 1 < kw)) compute(buf, q0, maskc);
+        if (qt + 1 < n_qt) stage_ld(buf ^ 1);
+        wait_vmem();
+        __syncthreads();
+    };
+    int qt = qt0;
+    for (; qt < qmask_end; ++qt) tile(qt, ic<1>{});
+    for (; qt < n_qt; ++qt) tile(qt, ic<0>{});
+
     if (key < N) {
         uint16_t* dkr = dK + base + (size_t)key * D;
         uint16_t* dvr = dV + base + (size_t)key * D;
@@ -191,8 +262,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
     uint16_t* __restrict__ dQ, int BH, int N, float scale_log2, float tau, int n_qtiles) {
     constexpr int BR = 128, BC = 64;
-    constexpr int KCH = D / 8, TCH = BC / 8, SPT = KCH / 4;
-    __shared__ u32x4 sK[BC * KCH], sV[BC * KCH], sKt[D * TCH];
+    constexpr int STR = D + 8;
+    __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * STR];
+    __shared__ __attribute__((aligned(16))) uint16_t sV[2][BC * STR];
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int ln = lane & 31, hf = lane >> 5;
@@ -216,69 +288,92 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) dqacc[db][r] = 0.f;
 
-    const int prow = kperm(ln);
+    const rsrc_t krs = make_rsrc(K + base, (uint32_t)N * D * 2);
+    const rsrc_t vrs = make_rsrc(V + base, (uint32_t)N * D * 2);
+    TileCopy<BC, D, STR, 4> cp;
+    cp.init(wave, lane);
+    const int a_off = kperm(ln) * STR + hf * 8;
+    const int G = lane >> 4, sl = lane & 15;
+    const int t_off = (8 * (G >> 1) + (sl >> 2)) * STR + 16 * (G & 1) + 4 * (sl & 3);
+
     const int kend = CAUSAL ? min(N, q0 + BR) : N;
     const int ntiles = (kend + BC - 1) / BC;
-    uint16_t* sKt16 = reinterpret_cast<uint16_t*>(sKt);
 
-    for (int j = 0; j < ntiles; ++j) {
-        const int k0 = j * BC;
-        __syncthreads();
-        {
-            const int kr = k0 + lane;
-#pragma unroll
-            for (int u = 0; u < SPT; ++u) {
-                const int c = wave + 4 * u;
-                const size_t off = base + (size_t)kr * D + c * 8;
-                const u32x4 a = kr < N ? ld16(K + off) : u32x4{0, 0, 0, 0};
-                const u32x4 b = kr < N ? ld16(V + off) : u32x4{0, 0, 0, 0};
-                sK[lane * KCH + (c ^ swz_k(lane))] = a;
-                sV[lane * KCH + (c ^ swz_k(lane))] = b;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int d = c * 8 + e;
-                    sKt16[d * BC + (((lane >> 3) ^ swz_t(d)) << 3) + (lane & 7)] = half_of(a, e);
-                }
-            }
-        }
-        __syncthreads();
-        if (CAUSAL && k0 > qw + 31) continue;
-        const bool need_mask = (k0 + BC > N) || (CAUSAL && k0 + BC - 1 > qw);
+    // Keys past N are zero rows (buffer descriptor), so their dS meets K = 0
+    // in dQ += dS K and needs no mask; only the causal diagonal is masked.
+    auto compute = [&](int buf, int k0, auto maskc) {
+        constexpr bool MASK = decltype(maskc)::value != 0;
+        const uint16_t* k_lds = &sK[buf][0];
+        const uint16_t* v_lds = &sV[buf][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            f32x16 s, dp;
+            f32x16 sacc, dp;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) { s[r] = 0.f; dp[r] = 0.f; }
-            const int row = kb * 32 + prow;
+            for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; dp[r] = 0.f; }
+            u32x4 ka[D / 16], va[D / 16];
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks) {
-                const int ch = row * KCH + ((ks * 2 + hf) ^ swz_k(row));
-                s = mfma32x32x16(sK[ch], qf[ks], s);
-                dp = mfma32x32x16(sV[ch], df[ks], dp);
+                ka[ks] = ld16(k_lds + kb * 32 * STR + a_off + ks * 16);
+                va[ks] = ld16(v_lds + kb * 32 * STR + a_off + ks * 16);
+            }
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) {
+                sacc = mfma32x32x16(ka[ks], qf[ks], sacc);
+                dp = mfma32x32x16(va[ks], df[ks], dp);
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                float p = fast_exp2(__builtin_fmaf(s[r], scale_log2, -lse2));
-                if (need_mask) {
-                    const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7);
-                    if (key >= N || (CAUSAL && key > qrow)) p = 0.f;
+                float p = fast_exp2(__builtin_fmaf(sacc[r], scale_log2, -lse2));
+                if constexpr (MASK) {
+                    const int kk = k0 + kb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7);
+                    if (CAUSAL && kk > qrow) p = 0.f;
                 }
-                s[r] = p * (dp[r] - Dq);
+                sacc[r] = p * (dp[r] - Dq);
             }
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 u32x4 dsf;
 #pragma unroll
-                for (int w = 0; w < 4; ++w) dsf[w] = pack_bf16x2(s[8 * t + 2 * w], s[8 * t + 2 * w + 1]);
-                const int ch = kb * 4 + 2 * t + hf;
+                for (int w = 0; w < 4; ++w) dsf[w] = pack_bf16x2(sacc[8 * t + 2 * w], sacc[8 * t + 2 * w + 1]);
+                const int tb = t_off + (kb * 32 + 16 * t) * STR;
+                u32x4 kt4[D / 32];
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const int d = db * 32 + ln;
-                    dqacc[db] = mfma32x32x16(sKt[d * TCH + (ch ^ swz_t(d))], dsf, dqacc[db]);
+                    const u32x2 a0 = lds_read_tr16(k_lds + tb + db * 32);
+                    const u32x2 a1 = lds_read_tr16(k_lds + tb + db * 32 + 4 * STR);
+                    kt4[db] = u32x4{a0[0], a0[1], a1[0], a1[1]};
                 }
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) dqacc[db] = mfma32x32x16(kt4[db], dsf, dqacc[db]);
             }
         }
-    }
+    };
+
+    cp.issue(krs, 0, &sK[0][0], wave);
+    cp.issue(vrs, 0, &sV[0][0], wave);
+    wait_vmem();
+    __syncthreads();
+    // tiles before jsplit precede every query of the workgroup: no mask
+    const int jsplit = CAUSAL ? min(ntiles, q0 / BC) : ntiles;
+    auto tile = [&](int j, auto maskc) {
+        const int buf = j & 1;
+        if (j + 1 < ntiles) {
+            cp.issue(krs, (j + 1) * BC, &sK[buf ^ 1][0], wave);
+            cp.issue(vrs, (j + 1) * BC, &sV[buf ^ 1][0], wave);
+        }
+        const int k0 = j * BC;
+        if constexpr (decltype(maskc)::value != 0) {
+            if (!(CAUSAL && k0 > qw + 31)) compute(buf, k0, maskc);
+        } else {
+            compute(buf, k0, maskc);
+        }
+        wait_vmem();
+        __syncthreads();
+    };
+    int j = 0;
+    for (; j < jsplit; ++j) tile(j, ic<0>{});
+    for (; j < ntiles; ++j) tile(j, ic<1>{});
+
     if (qrow < N) {
         uint16_t* dqr = dQ + base + (size_t)qrow * D;
 #pragma unroll

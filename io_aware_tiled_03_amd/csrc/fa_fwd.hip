@@ -8,7 +8,7 @@
 // tile and O, LSE once ("FlashAttention e o gargalo real de inferência",
 // "FlashAttention: eliminar a viagem").
 //
-// bf16 kernel layout (one workgroup = 4 waves = 128 query rows, key tile 64):
+// bf16 kernel layout (one workgroup = NW waves of 32 query rows, key tile BC):
 //  * each wave owns 32 query rows; its Q rows sit in registers as the B
 //    operand of S^T = K Q^T, so in the result every lane holds one query
 //    (column) and 16 keys per 32-key block (rows): the row max/sum of the
@@ -72,16 +72,16 @@ __device__ __forceinline__ void prio_lo() {
 
 template <int N_> using ic = std::integral_constant<int, N_>;
 
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
+// BC keys per tile, NW waves per workgroup (32 query rows each).
+template <int D, bool CAUSAL, int BC, int NW>
+__global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int N, float scale_log2, float tau,
     int n_qtiles) {
-    constexpr int BR = 128, BC = 64;
+    constexpr int BR = 32 * NW, NKB = BC / 32;
     constexpr int KCH = D / 8;             // 16-byte chunks per row
     constexpr int KSTR = D + FA_FWD_KPAD;  // K row stride (elements), padded against bank conflicts
     constexpr int VSTR = D + FA_FWD_VPAD;  // V row stride (elements)
-    constexpr int CPT = BC * KCH / 256;    // chunks of K (and of V) staged per thread
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * KSTR];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2][BC * VSTR];
 
@@ -119,30 +119,30 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     // and their V rows meet p = 0).  Wave w issues instructions w, w+4, ...
     constexpr int KCPR = KSTR / 8, VCPR = VSTR / 8;      // 16-byte chunks per padded row
     constexpr int KNI = BC * KCPR / 64, VNI = BC * VCPR / 64;   // wave instructions per tile
-    constexpr int KPW = (KNI + 3) / 4, VPW = (VNI + 3) / 4;     // per wave (upper bound)
+    constexpr int KPW = (KNI + NW - 1) / NW, VPW = (VNI + NW - 1) / NW;   // per wave (upper bound)
     static_assert(BC * KCPR % 64 == 0 && BC * VCPR % 64 == 0, "whole wave instructions");
     const rsrc_t krs = make_rsrc(K + base, (uint32_t)N * D * 2);
     const rsrc_t vrs = make_rsrc(V + base, (uint32_t)N * D * 2);
     uint32_t kgo[KPW], vgo[VPW];   // byte offsets inside a tile (tile start added per tile)
 #pragma unroll
     for (int t = 0; t < KPW; ++t) {
-        const int pos = (wave + 4 * t) * 64 + lane, prow = pos / KCPR, c = pos % KCPR;
+        const int pos = (wave + NW * t) * 64 + lane, prow = pos / KCPR, c = pos % KCPR;
         const int key = (prow & ~31) + kperm(prow & 31);
         kgo[t] = (uint32_t)(key * D + (c < KCH ? c : 0) * 8) * 2;
     }
 #pragma unroll
     for (int t = 0; t < VPW; ++t) {
-        const int pos = (wave + 4 * t) * 64 + lane, row = pos / VCPR, c = pos % VCPR;
+        const int pos = (wave + NW * t) * 64 + lane, row = pos / VCPR, c = pos % VCPR;
         vgo[t] = (uint32_t)(row * D + (c < KCH ? c : 0) * 8) * 2;
     }
     auto stage = [&](int j, int buf) {   // issue the copies of tile j into buffer buf
         const uint32_t t0 = (uint32_t)j * (BC * D * 2);
 #pragma unroll
         for (int t = 0; t < KPW; ++t)
-            if (wave + 4 * t < KNI) buf_ld16_lds(krs, kgo[t] + t0, &sK[buf][(wave + 4 * t) * 512]);
+            if (wave + NW * t < KNI) buf_ld16_lds(krs, kgo[t] + t0, &sK[buf][(wave + NW * t) * 512]);
 #pragma unroll
         for (int t = 0; t < VPW; ++t)
-            if (wave + 4 * t < VNI) buf_ld16_lds(vrs, vgo[t] + t0, &sV[buf][(wave + 4 * t) * 512]);
+            if (wave + NW * t < VNI) buf_ld16_lds(vrs, vgo[t] + t0, &sV[buf][(wave + NW * t) * 512]);
     };
     // Per-lane offsets of the operand reads.  K: physical row kb*32 + ln.
     // V (transposing read): lane s of 16-lane group G reads key 8*(G/2) + s/4
@@ -155,10 +155,10 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
     // tile, or a tile crossing this wave's diagonal under the causal mask).
     auto compute = [&](int buf, auto maskc, int k0) {
         constexpr bool MASK = decltype(maskc)::value != 0;
-        f32x16 s[2];
+        f32x16 s[NKB];
         prio_hi();
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
+        for (int kb = 0; kb < NKB; ++kb) {
 #pragma unroll
             for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
             u32x4 ka[D / 16];   // all operands of the block first, then the MFMA chain
@@ -170,7 +170,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
         prio_lo();
         if constexpr (MASK) {
 #pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
+            for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7);
@@ -179,7 +179,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
         }
         float mx = s[0][0];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
         mx = fmaxf(mx, xor32(mx));
@@ -197,9 +197,9 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
             m = mnew;
         }
         const float mc = m * scale_log2;
-        u32x4 pf[2][2];
+        u32x4 pf[NKB][2];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(256, 2) void fwd_bf16_kernel(
                 }
         prio_hi();
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
                 const int vb = v_off + (kb * 32 + 16 * t) * VSTR;
@@ -333,11 +333,18 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(
     }
 }
 
+// Tile shapes measured on MI355X: d=128 runs 128-key tiles in 8-wave (256-row)
+// workgroups, one per CU (143 KB of LDS); d=64 runs 64-key tiles in 4-wave
+// workgroups, several per CU.
+template <int D> struct FwdShape { static constexpr int BC = 64, NW = 4; };
+template <> struct FwdShape<128> { static constexpr int BC = 128, NW = 8; };
+
 template <int D, bool C>
 void launch_bf16(const FwdArgs& a, hipStream_t st) {
+    constexpr int BC = FwdShape<D>::BC, NW = FwdShape<D>::NW;
     const int bh = a.B * a.H;
-    const int nq = (a.N + 127) / 128;
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, C>), dim3(nq * bh), dim3(256), 0, st,
+    const int nq = (a.N + 32 * NW - 1) / (32 * NW);
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, C, BC, NW>), dim3(nq * bh), dim3(64 * NW), 0, st,
                        (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.o, a.lse, bh, a.N, a.tau * kLog2e, a.tau, nq);
 }
