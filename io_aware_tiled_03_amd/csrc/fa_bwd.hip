@@ -100,7 +100,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     __shared__ __attribute__((aligned(16))) float sL[2][BR];
     __shared__ __attribute__((aligned(16))) float sD[2][BR];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
     const int ln = lane & 31, hf = lane >> 5;
     const int kt = (int)(blockIdx.x / BH);      // causal: low key tiles carry the most work
     const int bh = (int)(blockIdx.x % BH);
@@ -157,17 +158,16 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         for (int qb = 0; qb < 2; ++qb) {
             const int qs = q0 + qb * 32;
             if (MASK && CAUSAL && qs + 31 < kw) continue;   // all these queries precede the keys
-            f32x16 sacc, dp;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; dp[r] = 0.f; }
             u32x4 qa[D / 16], oa[D / 16];
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks) {
                 qa[ks] = ld16(q_lds + qb * 32 * STR + a_off + ks * 16);
                 oa[ks] = ld16(o_lds + qb * 32 * STR + a_off + ks * 16);
             }
+            f32x16 sacc = mfma32x32x16_zero(qa[0], kf[0]);
+            f32x16 dp = mfma32x32x16_zero(oa[0], vf[0]);
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
+            for (int ks = 1; ks < D / 16; ++ks) {
                 sacc = mfma32x32x16(qa[ks], kf[ks], sacc);
                 dp = mfma32x32x16(oa[ks], vf[ks], dp);
             }
@@ -200,12 +200,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                 u32x4 ot[D / 32], qt4[D / 32];
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const u32x2 a0 = lds_read_tr16(o_lds + tb + db * 32);
-                    const u32x2 a1 = lds_read_tr16(o_lds + tb + db * 32 + 4 * STR);
-                    const u32x2 b0 = lds_read_tr16(q_lds + tb + db * 32);
-                    const u32x2 b1 = lds_read_tr16(q_lds + tb + db * 32 + 4 * STR);
-                    ot[db] = u32x4{a0[0], a0[1], a1[0], a1[1]};
-                    qt4[db] = u32x4{b0[0], b0[1], b1[0], b1[1]};
+                    ot[db] = lds_read_tr16_x2(o_lds + tb + db * 32, o_lds + tb + db * 32 + 4 * STR);
+                    qt4[db] = lds_read_tr16_x2(q_lds + tb + db * 32, q_lds + tb + db * 32 + 4 * STR);
                 }
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
@@ -266,7 +262,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * STR];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2][BC * STR];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
     const int ln = lane & 31, hf = lane >> 5;
     const int qt = n_qtiles - 1 - (int)(blockIdx.x / BH);
     const int bh = (int)(blockIdx.x % BH);
@@ -307,17 +304,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         const uint16_t* v_lds = &sV[buf][0];
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-            f32x16 sacc, dp;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) { sacc[r] = 0.f; dp[r] = 0.f; }
             u32x4 ka[D / 16], va[D / 16];
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks) {
                 ka[ks] = ld16(k_lds + kb * 32 * STR + a_off + ks * 16);
                 va[ks] = ld16(v_lds + kb * 32 * STR + a_off + ks * 16);
             }
+            f32x16 sacc = mfma32x32x16_zero(ka[0], qf[0]);
+            f32x16 dp = mfma32x32x16_zero(va[0], df[0]);
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) {
+            for (int ks = 1; ks < D / 16; ++ks) {
                 sacc = mfma32x32x16(ka[ks], qf[ks], sacc);
                 dp = mfma32x32x16(va[ks], df[ks], dp);
             }
@@ -339,9 +335,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
                 u32x4 kt4[D / 32];
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const u32x2 a0 = lds_read_tr16(k_lds + tb + db * 32);
-                    const u32x2 a1 = lds_read_tr16(k_lds + tb + db * 32 + 4 * STR);
-                    kt4[db] = u32x4{a0[0], a0[1], a1[0], a1[1]};
+                    kt4[db] = lds_read_tr16_x2(k_lds + tb + db * 32, k_lds + tb + db * 32 + 4 * STR);
                 }
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) dqacc[db] = mfma32x32x16(kt4[db], dsf, dqacc[db]);

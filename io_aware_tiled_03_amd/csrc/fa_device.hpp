@@ -29,6 +29,12 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float neg_inf() { return -__builtin_inff(); }
 
+// First product of an accumulation chain: C = 0 as the inline constant operand.
+__device__ __forceinline__ f32x16 mfma32x32x16_zero(const u32x4& a, const u32x4& b) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), f32x16{}, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x16 mfma32x32x16(const u32x4& a, const u32x4& b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                     __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -98,6 +104,15 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void* lds) {
     typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
     const v4i16 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)(lds));
     return __builtin_bit_cast(u32x2, r);
+}
+
+// An MFMA A operand (8 bf16: four keys of one column, then the next four) from
+// two transposing reads, assembled in place.
+__device__ __forceinline__ u32x4 lds_read_tr16_x2(const void* lds_lo, const void* lds_hi) {
+    u32x4 r;
+    r.xy = lds_read_tr16(lds_lo);
+    r.zw = lds_read_tr16(lds_hi);
+    return r;
 }
 
 // a.lo*b.lo + a.hi*b.hi + c for packed bf16 pairs, fp32 accumulation.

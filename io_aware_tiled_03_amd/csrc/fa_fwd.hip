@@ -85,7 +85,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * KSTR];
     __shared__ __attribute__((aligned(16))) uint16_t sV[2][BC * VSTR];
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
     const int ln = lane & 31, hf = lane >> 5;
     const int qt = n_qtiles - 1 - (int)(blockIdx.x / BH);   // heaviest tiles first
     const int bh = (int)(blockIdx.x % BH);
@@ -159,13 +160,12 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
         prio_hi();
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) s[kb][r] = 0.f;
             u32x4 ka[D / 16];   // all operands of the block first, then the MFMA chain
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks) ka[ks] = ld16(&sK[buf][k_off + kb * 32 * KSTR + ks * 16]);
+            s[kb] = mfma32x32x16_zero(ka[0], qf[0]);
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) s[kb] = mfma32x32x16(ka[ks], qf[ks], s[kb]);
+            for (int ks = 1; ks < D / 16; ++ks) s[kb] = mfma32x32x16(ka[ks], qf[ks], s[kb]);
         }
         prio_lo();
         if constexpr (MASK) {
@@ -219,9 +219,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
                 u32x4 va[D / 32];
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    const u32x2 lo = lds_read_tr16(&sV[buf][vb + db * 32]);
-                    const u32x2 hi = lds_read_tr16(&sV[buf][vb + db * 32 + 4 * VSTR]);
-                    va[db] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+                    va[db] = lds_read_tr16_x2(&sV[buf][vb + db * 32], &sV[buf][vb + db * 32 + 4 * VSTR]);
                 }
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) oacc[db] = mfma32x32x16(va[db], pf[kb][t], oacc[db]);
