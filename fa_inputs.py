@@ -161,3 +161,39 @@ def workload_decode_inputs(w: Workload, B=None) -> dict:
     Bn = w.B if B is None else B
     seqlens = decode_seqlens(w.B, w.lmin, w.lmax, w.seed + SEED_OFFSET["seqlens"])[:Bn]
     return decode_inputs(Bn, w.H, w.N, w.d, w.dtype, w.seed, seqlens)
+
+
+def paged_decode_inputs(B, Hq, Hkv, page_size, d, dtype, seed, seqlens):
+    """Q [B,Hq,1,d] and a paged KV cache for sequences of the given lengths.
+
+    Pages: [num_pages, Hkv, page_size, d]; each sequence gets ceil(L_b /
+    page_size) pages, the page table assigns them a random permutation of the
+    page indices (seeded), and rows past L_b in a sequence's last page are NaN.
+    Values: the same per-sequence draws as the dense decode recipe,
+    decode_cache_rows(seed + offset, b, Hkv, L_b, d), scattered into pages.
+    Returns dict(q, k_pages, v_pages, block_table [B, max_pages] int32, seqlens).
+    """
+    seqlens = np.asarray(seqlens, dtype=np.int32)
+    npb = [(int(L) + page_size - 1) // page_size for L in seqlens]
+    max_pages = max(1, max(npb))
+    num_pages = max(1, sum(npb))
+    rng = np.random.Generator(np.random.PCG64(seed + 500))
+    perm = rng.permutation(num_pages).astype(np.int32)
+    table = np.zeros((B, max_pages), dtype=np.int32)
+    nan = BF16_NAN if dtype == "bf16" else np.float32(np.nan)
+    store = np.uint16 if dtype == "bf16" else np.float32
+    pages = {n: np.full((num_pages, Hkv, page_size, d), nan, dtype=store) for n in ("k", "v")}
+    nxt = 0
+    for b in range(B):
+        L = int(seqlens[b])
+        ids = perm[nxt:nxt + npb[b]]
+        nxt += npb[b]
+        table[b, :len(ids)] = ids
+        for n in ("k", "v"):
+            rows = decode_cache_rows(seed + SEED_OFFSET[n], b, Hkv, L, d, dtype).raw
+            for pi, pid in enumerate(ids):
+                a, e = pi * page_size, min(L, (pi + 1) * page_size)
+                pages[n][pid, :, :e - a] = rows[:, a:e]
+    q = draw((B, Hq, 1, d), seed + SEED_OFFSET["q"], dtype)
+    return {"q": q, "k_pages": HostTensor(pages["k"], dtype), "v_pages": HostTensor(pages["v"], dtype),
+            "block_table": table, "seqlens": seqlens}

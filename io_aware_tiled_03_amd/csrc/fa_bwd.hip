@@ -95,10 +95,13 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     float tau) {
     constexpr int BC = 128, BR = 64;
     constexpr int STR = D + 8;                 // padded row (16 * odd bytes)
-    __shared__ __attribute__((aligned(16))) uint16_t sQ[2][BR * STR];
-    __shared__ __attribute__((aligned(16))) uint16_t sdO[2][BR * STR];
-    __shared__ __attribute__((aligned(16))) float sL[2][BR];
-    __shared__ __attribute__((aligned(16))) float sD[2][BR];
+    // Double buffers as distinct LDS variables picked at compile time, so that
+    // reads of one buffer are not made to wait for the copies landing in the
+    // other (see the forward kernel).
+    __shared__ __attribute__((aligned(16))) uint16_t sQ0[BR * STR], sQ1[BR * STR];
+    __shared__ __attribute__((aligned(16))) uint16_t sdO0[BR * STR], sdO1[BR * STR];
+    __shared__ __attribute__((aligned(16))) float sL0[BR], sL1[BR];
+    __shared__ __attribute__((aligned(16))) float sD0[BR], sD1[BR];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
@@ -135,25 +138,30 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const int n_qt = (N + BR - 1) / BR;
     const int qt0 = CAUSAL ? k0 / BR : 0;
     float ld_l = 0.f, ld_d = 0.f;   // this thread's LSE/D value of the next tile (threads < 128)
-    auto stage = [&](int qt, int buf) {
+    auto stage = [&](int qt, auto bufc) __attribute__((always_inline)) {
+        constexpr bool B1 = decltype(bufc)::value != 0;
         const int q0 = qt * BR;
-        cp.issue(qrs, q0, &sQ[buf][0], wave);
-        cp.issue(ors, q0, &sdO[buf][0], wave);
+        cp.issue(qrs, q0, B1 ? sQ1 : sQ0, wave);
+        cp.issue(ors, q0, B1 ? sdO1 : sdO0, wave);
         if (tid < 2 * BR) {
             const int q = q0 + (tid & (BR - 1));
             if (tid < BR) ld_l = q < N ? LSE[(size_t)bh * N + q] * kLog2e : __builtin_inff();
             else ld_d = q < N ? Dv[(size_t)bh * N + q] : 0.f;
         }
     };
-    auto stage_ld = [&](int buf) {
-        if (tid < BR) sL[buf][tid] = ld_l;
-        else if (tid < 2 * BR) sD[buf][tid - BR] = ld_d;
+    auto stage_ld = [&](auto bufc) __attribute__((always_inline)) {
+        constexpr bool B1 = decltype(bufc)::value != 0;
+        if (tid < BR) (B1 ? sL1 : sL0)[tid] = ld_l;
+        else if (tid < 2 * BR) (B1 ? sD1 : sD0)[tid - BR] = ld_d;
     };
 
-    auto compute = [&](int buf, int q0, auto maskc) {
+    auto compute = [&](auto bufc, int q0, auto maskc) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(maskc)::value != 0;
-        const uint16_t* q_lds = &sQ[buf][0];
-        const uint16_t* o_lds = &sdO[buf][0];
+        constexpr bool B1 = decltype(bufc)::value != 0;
+        const uint16_t* q_lds = B1 ? sQ1 : sQ0;
+        const uint16_t* o_lds = B1 ? sdO1 : sdO0;
+        const float* l_lds = B1 ? sL1 : sL0;
+        const float* d_lds = B1 ? sD1 : sD0;
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
             const int qs = q0 + qb * 32;
@@ -175,8 +183,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
             f32x4 lq[4], dq4[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                lq[i] = *reinterpret_cast<const f32x4*>(&sL[buf][qb * 32 + 16 * (i >> 1) + 8 * hf + 4 * (i & 1)]);
-                dq4[i] = *reinterpret_cast<const f32x4*>(&sD[buf][qb * 32 + 16 * (i >> 1) + 8 * hf + 4 * (i & 1)]);
+                lq[i] = *reinterpret_cast<const f32x4*>(&l_lds[qb * 32 + 16 * (i >> 1) + 8 * hf + 4 * (i & 1)]);
+                dq4[i] = *reinterpret_cast<const f32x4*>(&d_lds[qb * 32 + 16 * (i >> 1) + 8 * hf + 4 * (i & 1)]);
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -213,25 +221,35 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     };
 
     if (qt0 < n_qt) {
-        stage(qt0, 0);
-        stage_ld(0);
+        stage(qt0, ic<0>{});
+        stage_ld(ic<0>{});
         wait_vmem();
         __syncthreads();
     }
     // query tiles that reach into this workgroup's keys need the causal mask
     const int qmask_end = CAUSAL ? min(n_qt, (k0 + BC + BR - 1) / BR) : qt0;
-    auto tile = [&](int qt, auto maskc) {
-        const int buf = (qt - qt0) & 1;
-        if (qt + 1 < n_qt) stage(qt + 1, buf ^ 1);
+    auto tile_b = [&](int qt, auto bufc, auto maskc) __attribute__((always_inline)) {   // query tile qt lives in buffer bufc
+        constexpr ic<1 - decltype(bufc)::value> other{};
+        if (qt + 1 < n_qt) stage(qt + 1, other);
         const int q0 = qt * BR;
-        if (!(CAUSAL && q0 + BR - 1 < kw)) compute(buf, q0, maskc);
-        if (qt + 1 < n_qt) stage_ld(buf ^ 1);
+        if (!(CAUSAL && q0 + BR - 1 < kw)) compute(bufc, q0, maskc);
+        if (qt + 1 < n_qt) stage_ld(other);
         wait_vmem();
         __syncthreads();
     };
-    int qt = qt0;
-    for (; qt < qmask_end; ++qt) tile(qt, ic<1>{});
-    for (; qt < n_qt; ++qt) tile(qt, ic<0>{});
+    // Query tiles [tb, te), tile qt in buffer (qt - qt0) % 2: an odd first
+    // tile alone, then pairs, then an even last tile (buffers fixed at compile time).
+    auto phase = [&](int tb, int te, auto maskc) __attribute__((always_inline)) {
+        int qt = tb;
+        if (qt < te && ((qt - qt0) & 1)) { tile_b(qt, ic<1>{}, maskc); ++qt; }
+        for (; qt + 1 < te; qt += 2) {
+            tile_b(qt, ic<0>{}, maskc);
+            tile_b(qt + 1, ic<1>{}, maskc);
+        }
+        if (qt < te) tile_b(qt, ic<0>{}, maskc);
+    };
+    phase(qt0, qmask_end, ic<1>{});
+    phase(max(qt0, qmask_end), n_qt, ic<0>{});
 
     if (key < N) {
         uint16_t* dkr = dK + base + (size_t)key * D;
@@ -259,8 +277,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     uint16_t* __restrict__ dQ, int BH, int N, float scale_log2, float tau, int n_qtiles) {
     constexpr int BR = 128, BC = 64;
     constexpr int STR = D + 8;
-    __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * STR];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[2][BC * STR];
+    __shared__ __attribute__((aligned(16))) uint16_t sK0[BC * STR], sK1[BC * STR];
+    __shared__ __attribute__((aligned(16))) uint16_t sV0[BC * STR], sV1[BC * STR];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
@@ -298,10 +316,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
     // Keys past N are zero rows (buffer descriptor), so their dS meets K = 0
     // in dQ += dS K and needs no mask; only the causal diagonal is masked.
-    auto compute = [&](int buf, int k0, auto maskc) {
+    auto compute = [&](auto bufc, int k0, auto maskc) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(maskc)::value != 0;
-        const uint16_t* k_lds = &sK[buf][0];
-        const uint16_t* v_lds = &sV[buf][0];
+        const uint16_t* k_lds = decltype(bufc)::value ? sK1 : sK0;
+        const uint16_t* v_lds = decltype(bufc)::value ? sV1 : sV0;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             u32x4 ka[D / 16], va[D / 16];
@@ -343,30 +361,39 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         }
     };
 
-    cp.issue(krs, 0, &sK[0][0], wave);
-    cp.issue(vrs, 0, &sV[0][0], wave);
+    cp.issue(krs, 0, sK0, wave);
+    cp.issue(vrs, 0, sV0, wave);
     wait_vmem();
     __syncthreads();
     // tiles before jsplit precede every query of the workgroup: no mask
     const int jsplit = CAUSAL ? min(ntiles, q0 / BC) : ntiles;
-    auto tile = [&](int j, auto maskc) {
-        const int buf = j & 1;
+    auto tile_b = [&](int j, auto bufc, auto maskc) __attribute__((always_inline)) {   // key tile j lives in buffer bufc
+        constexpr bool B1 = decltype(bufc)::value != 0;
         if (j + 1 < ntiles) {
-            cp.issue(krs, (j + 1) * BC, &sK[buf ^ 1][0], wave);
-            cp.issue(vrs, (j + 1) * BC, &sV[buf ^ 1][0], wave);
+            cp.issue(krs, (j + 1) * BC, B1 ? sK0 : sK1, wave);
+            cp.issue(vrs, (j + 1) * BC, B1 ? sV0 : sV1, wave);
         }
         const int k0 = j * BC;
         if constexpr (decltype(maskc)::value != 0) {
-            if (!(CAUSAL && k0 > qw + 31)) compute(buf, k0, maskc);
+            if (!(CAUSAL && k0 > qw + 31)) compute(bufc, k0, maskc);
         } else {
-            compute(buf, k0, maskc);
+            compute(bufc, k0, maskc);
         }
         wait_vmem();
         __syncthreads();
     };
-    int j = 0;
-    for (; j < jsplit; ++j) tile(j, ic<0>{});
-    for (; j < ntiles; ++j) tile(j, ic<1>{});
+    // Key tiles [jb, je), tile j in buffer j % 2 (buffers fixed at compile time).
+    auto phase = [&](int jb, int je, auto maskc) __attribute__((always_inline)) {
+        int j = jb;
+        if (j < je && (j & 1)) { tile_b(j, ic<1>{}, maskc); ++j; }
+        for (; j + 1 < je; j += 2) {
+            tile_b(j, ic<0>{}, maskc);
+            tile_b(j + 1, ic<1>{}, maskc);
+        }
+        if (j < je) tile_b(j, ic<0>{}, maskc);
+    };
+    phase(0, jsplit, ic<0>{});
+    phase(jsplit, ntiles, ic<1>{});
 
     if (qrow < N) {
         uint16_t* dqr = dQ + base + (size_t)qrow * D;

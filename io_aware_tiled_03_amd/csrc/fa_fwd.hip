@@ -82,8 +82,14 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
     constexpr int KCH = D / 8;             // 16-byte chunks per row
     constexpr int KSTR = D + FA_FWD_KPAD;  // K row stride (elements), padded against bank conflicts
     constexpr int VSTR = D + FA_FWD_VPAD;  // V row stride (elements)
-    __shared__ __attribute__((aligned(16))) uint16_t sK[2][BC * KSTR];
-    __shared__ __attribute__((aligned(16))) uint16_t sV[2][BC * VSTR];
+    // Two staging buffers per operand, as distinct LDS variables chosen at
+    // compile time: the compiler then knows a read of one buffer cannot alias
+    // the direct-to-LDS copies still landing in the other, and does not wait
+    // for those copies before the reads.  (With one array indexed by a run-time
+    // buffer number it waits for every outstanding copy, serialising the next
+    // tile's load with this tile's compute.)
+    __shared__ __attribute__((aligned(16))) uint16_t sK0[BC * KSTR], sK1[BC * KSTR];
+    __shared__ __attribute__((aligned(16))) uint16_t sV0[BC * VSTR], sV1[BC * VSTR];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
@@ -136,14 +142,17 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
         const int pos = (wave + NW * t) * 64 + lane, row = pos / VCPR, c = pos % VCPR;
         vgo[t] = (uint32_t)(row * D + (c < KCH ? c : 0) * 8) * 2;
     }
-    auto stage = [&](int j, int buf) {   // issue the copies of tile j into buffer buf
+    auto stage = [&](int j, auto bufc) __attribute__((always_inline)) {   // issue the copies of tile j into buffer bufc
+        constexpr bool B1 = decltype(bufc)::value != 0;
+        uint16_t* const sk = B1 ? sK1 : sK0;
+        uint16_t* const sv = B1 ? sV1 : sV0;
         const uint32_t t0 = (uint32_t)j * (BC * D * 2);
 #pragma unroll
         for (int t = 0; t < KPW; ++t)
-            if (wave + NW * t < KNI) buf_ld16_lds(krs, kgo[t] + t0, &sK[buf][(wave + NW * t) * 512]);
+            if (wave + NW * t < KNI) buf_ld16_lds(krs, kgo[t] + t0, &sk[(wave + NW * t) * 512]);
 #pragma unroll
         for (int t = 0; t < VPW; ++t)
-            if (wave + NW * t < VNI) buf_ld16_lds(vrs, vgo[t] + t0, &sV[buf][(wave + NW * t) * 512]);
+            if (wave + NW * t < VNI) buf_ld16_lds(vrs, vgo[t] + t0, &sv[(wave + NW * t) * 512]);
     };
     // Per-lane offsets of the operand reads.  K: physical row kb*32 + ln.
     // V (transposing read): lane s of 16-lane group G reads key 8*(G/2) + s/4
@@ -154,15 +163,17 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
 
     // One key tile from LDS buffer BUF; MASK selects the masked variant (tail
     // tile, or a tile crossing this wave's diagonal under the causal mask).
-    auto compute = [&](int buf, auto maskc, int k0) {
+    auto compute = [&](auto bufc, auto maskc, int k0) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(maskc)::value != 0;
+        const uint16_t* const sk = decltype(bufc)::value ? sK1 : sK0;
+        const uint16_t* const sv = decltype(bufc)::value ? sV1 : sV0;
         f32x16 s[NKB];
         prio_hi();
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             u32x4 ka[D / 16];   // all operands of the block first, then the MFMA chain
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) ka[ks] = ld16(&sK[buf][k_off + kb * 32 * KSTR + ks * 16]);
+            for (int ks = 0; ks < D / 16; ++ks) ka[ks] = ld16(&sk[k_off + kb * 32 * KSTR + ks * 16]);
             s[kb] = mfma32x32x16_zero(ka[0], qf[0]);
 #pragma unroll
             for (int ks = 1; ks < D / 16; ++ks) s[kb] = mfma32x32x16(ka[ks], qf[ks], s[kb]);
@@ -219,7 +230,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
                 u32x4 va[D / 32];
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    va[db] = lds_read_tr16_x2(&sV[buf][vb + db * 32], &sV[buf][vb + db * 32 + 4 * VSTR]);
+                    va[db] = lds_read_tr16_x2(&sv[vb + db * 32], &sv[vb + db * 32 + 4 * VSTR]);
                 }
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) oacc[db] = mfma32x32x16(va[db], pf[kb][t], oacc[db]);
@@ -227,27 +238,39 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
         prio_lo();
     };
 
-    auto tile = [&](int j, auto maskc) {
-        const int buf = j & 1;
-        stage(j + 1, buf ^ 1);   // past the last tile: zeros or unused rows, never read back
+    // Tile j lives in buffer j % 2 (bufc); the copies of tile j + 1 go to the
+    // other buffer while tile j is computed.
+    auto tile = [&](int j, auto bufc, auto maskc) __attribute__((always_inline)) {
+        stage(j + 1, ic<1 - decltype(bufc)::value>{});   // past the last tile: never read back
         const int k0 = j * BC;
         if constexpr (decltype(maskc)::value != 0) {
-            if (!CAUSAL || k0 <= qw + 31) compute(buf, maskc, k0);   // rows all before the tile: skip
+            if (!CAUSAL || k0 <= qw + 31) compute(bufc, maskc, k0);   // rows all before the tile: skip
         } else {
-            compute(buf, maskc, k0);
+            compute(bufc, maskc, k0);
         }
         wait_vmem();
         __syncthreads();
     };
+    // Tiles [jb, je) with tile j in buffer j % 2: an odd first tile alone,
+    // then pairs, then an even last tile, so every buffer choice is fixed at
+    // compile time.
+    auto phase = [&](int jb, int je, auto maskc) __attribute__((always_inline)) {
+        int j = jb;
+        if (j < je && (j & 1)) { tile(j, ic<1>{}, maskc); ++j; }
+        for (; j + 1 < je; j += 2) {
+            tile(j, ic<0>{}, maskc);
+            tile(j + 1, ic<1>{}, maskc);
+        }
+        if (j < je) tile(j, ic<0>{}, maskc);
+    };
     // Tiles before jsplit need no mask in any wave: no key past N and, under
     // the causal mask, every key precedes the workgroup's first query row.
     const int jsplit = min(CAUSAL ? q0 / BC : ntiles, nfull);
-    stage(0, 0);
+    stage(0, ic<0>{});
     wait_vmem();
     __syncthreads();
-    int j = 0;
-    for (; j < jsplit; ++j) tile(j, ic<0>{});
-    for (; j < ntiles; ++j) tile(j, ic<1>{});
+    phase(0, jsplit, ic<0>{});
+    phase(jsplit, ntiles, ic<1>{});
 
     l += xor32(l);
     const float inv = 1.f / l;

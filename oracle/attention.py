@@ -38,6 +38,7 @@ import numpy as np
 __all__ = [
     "scores", "probs", "attention_fwd_head", "attention_fwd", "attention_bwd_head",
     "attention_bwd", "decode_fwd", "tiled_fwd_literal", "split_kv_decode",
+    "gather_pages", "decode_paged",
 ]
 
 
@@ -225,4 +226,42 @@ def split_kv_decode(q, k, v, tau, bounds):
     mx = lses.max()
     lse = mx + np.log(np.exp(lses - mx).sum())
     o = sum(np.exp(ls - lse) * p[0] for ls, p in zip(lses, parts))
+    return o, lse
+
+
+def gather_pages(pages, block_table_row, kv_head, length, page_size):
+    """Rows [0, length) of one sequence's cache for one KV head, read through
+    its page table: key t lives in page block_table_row[t // page_size], row
+    t % page_size.  pages: [num_pages, Hkv, page_size, d]."""
+    idx = np.arange(length)
+    page = np.asarray(block_table_row)[idx // page_size]
+    return pages[page, kv_head, idx % page_size]
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seqlens, tau):
+    """Decode with grouped KV heads over a paged cache.
+
+    "Atenção eficiente — FlashAttention, sparse e híbrida": section
+    "FlashAttention não acelera o decode token a token" (decode is bound by
+    reading the KV cache, which MQA/GQA shrink; see also the page's "Veja
+    também" list) and the table of section "Sparse e híbrida" (Paged Attention
+    keeps the KV cache in memory pages).  Readings: query head h of Hq uses KV
+    head h // (Hq / Hkv); key t of sequence b sits in page
+    block_table[b, t // page_size] at row t % page_size.  Each (b, h) is then
+    plain decode: one query against its L_b keys.
+    q: [B, Hq, 1, d]; k_pages, v_pages: [num_pages, Hkv, page_size, d];
+    block_table: [B, max_pages]; seqlens: [B].  Returns O [B,Hq,1,d], LSE [B,Hq].
+    """
+    B, Hq = q.shape[0], q.shape[1]
+    Hkv, page_size = k_pages.shape[1], k_pages.shape[2]
+    G = Hq // Hkv
+    o = np.empty((B, Hq, 1, v_pages.shape[-1]))
+    lse = np.empty((B, Hq))
+    for b in range(B):
+        L = int(seqlens[b])
+        for h in range(Hq):
+            kk = gather_pages(k_pages, block_table[b], h // G, L, page_size)
+            vv = gather_pages(v_pages, block_table[b], h // G, L, page_size)
+            oo, ll = attention_fwd_head(q[b, h], kk, vv, tau, False)
+            o[b, h], lse[b, h] = oo, ll[0]
     return o, lse

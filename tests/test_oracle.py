@@ -318,3 +318,55 @@ def test_decode_inputs_poison_padding():
     assert np.all(np.isnan(kf[1, :, 39:])) and np.all(np.isfinite(kf[2]))
     s = fa_inputs.decode_seqlens(64, 1024, 8192, 1404)
     assert s.min() >= 1024 and s.max() <= 8192
+
+
+# --- grouped KV heads and the paged cache ---------------------------------
+
+def test_paged_decode_equals_dense_decode_of_the_gathered_cache():
+    """Reading through the page table gives the same keys as a dense cache:
+    with one KV head per query head (G = 1) paged decode is dense decode."""
+    seqlens = [1, 17, 40, 64]
+    x = fa_inputs.paged_decode_inputs(4, 2, 2, 16, 8, "f32", 77, seqlens)
+    dense = fa_inputs.decode_inputs(4, 2, 64, 8, "f32", 77, seqlens=seqlens)
+    o1, l1 = orc.decode_paged(x["q"].f64(), x["k_pages"].f64(), x["v_pages"].f64(),
+                              x["block_table"], x["seqlens"], 0.3)
+    o2, l2 = orc.decode_fwd(dense["q"].f64(), dense["k"].f64(), dense["v"].f64(), seqlens, 0.3)
+    np.testing.assert_allclose(o1, o2, atol=0)
+    np.testing.assert_allclose(l1, l2, atol=0)
+
+
+def test_grouped_heads_share_kv_and_mqa_matches_repeated_heads():
+    """Query heads of one group see the same keys: with all query heads equal
+    inside a group the outputs coincide, and MQA (one KV head) equals MHA with
+    that KV head repeated for every query head."""
+    seqlens = [30, 5]
+    x = fa_inputs.paged_decode_inputs(2, 4, 1, 16, 8, "f32", 78, seqlens)
+    q = x["q"].f64()
+    kp, vp = x["k_pages"].f64(), x["v_pages"].f64()
+    o, l = orc.decode_paged(q, kp, vp, x["block_table"], x["seqlens"], 0.5)
+    rep_k = np.repeat(kp, 4, axis=1)
+    rep_v = np.repeat(vp, 4, axis=1)
+    o2, l2 = orc.decode_paged(q, rep_k, rep_v, x["block_table"], x["seqlens"], 0.5)
+    np.testing.assert_allclose(o, o2, atol=0)
+    q_same = np.repeat(q[:, :1], 4, axis=1)
+    o3, _ = orc.decode_paged(q_same, kp, vp, x["block_table"], x["seqlens"], 0.5)
+    for h in range(1, 4):
+        np.testing.assert_allclose(o3[:, h], o3[:, 0], atol=0)
+    # hand check of the grouping rule h -> h // G with two KV heads
+    x2 = fa_inputs.paged_decode_inputs(1, 4, 2, 16, 8, "f32", 79, [9])
+    o4, _ = orc.decode_paged(x2["q"].f64(), x2["k_pages"].f64(), x2["v_pages"].f64(),
+                             x2["block_table"], x2["seqlens"], 0.5)
+    for h in range(4):
+        kk = x2["k_pages"].f64()[x2["block_table"][0, 0], h // 2, :9]
+        vv = x2["v_pages"].f64()[x2["block_table"][0, 0], h // 2, :9]
+        oo, _ = orc.attention_fwd_head(x2["q"].f64()[0, h], kk, vv, 0.5, False)
+        np.testing.assert_allclose(o4[0, h], oo, atol=1e-14)
+
+
+def test_paged_inputs_poison_unused_rows():
+    x = fa_inputs.paged_decode_inputs(2, 2, 1, 16, 8, "bf16", 80, [20, 16])
+    kp = x["k_pages"].f64()
+    t = x["block_table"]
+    assert np.all(np.isfinite(kp[t[0, 0]])) and np.all(np.isfinite(kp[t[0, 1], :, :4]))
+    assert np.all(np.isnan(kp[t[0, 1], :, 4:]))
+    assert sorted(t[0, :2].tolist() + t[1, :1].tolist()) == [0, 1, 2]
