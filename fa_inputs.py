@@ -64,6 +64,36 @@ WORKLOADS = {
 SEED_OFFSET = {"q": 0, "k": 100, "v": 200, "do": 300, "seqlens": 400}
 
 
+@dataclasses.dataclass(frozen=True)
+class PagedWorkload:
+    """Decode over a paged cache with grouped KV heads: Hq query heads share
+    Hkv KV heads; key lengths are those of the dense decode workload."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    page_size: int
+    d: int
+    lmin: int
+    lmax: int
+    seed: int
+    seqlens_seed: int
+
+    @property
+    def tau(self) -> float:
+        return 1.0 / math.sqrt(self.d)
+
+    @property
+    def max_pages(self) -> int:
+        return (self.lmax + self.page_size - 1) // self.page_size
+
+
+# Llama-style grouping (4 query heads per KV head), 16-token pages, the dense
+# decode workload's batch, head count, head size and key lengths.
+PAGED_WORKLOAD = PagedWorkload("decode-paged-gqa", 64, 32, 8, 16, 128, 1024, 8192, 1006,
+                               1004 + 400)
+
+
 def normal_f32(shape, seed) -> np.ndarray:
     """fp32 standard normal draws from PCG64(seed)."""
     rng = np.random.Generator(np.random.PCG64(seed))
@@ -163,7 +193,15 @@ def workload_decode_inputs(w: Workload, B=None) -> dict:
     return decode_inputs(Bn, w.H, w.N, w.d, w.dtype, w.seed, seqlens)
 
 
-def paged_decode_inputs(B, Hq, Hkv, page_size, d, dtype, seed, seqlens):
+def paged_workload_inputs(w: PagedWorkload = PAGED_WORKLOAD, B=None) -> dict:
+    """Inputs of a paged workload (optionally only the first B sequences)."""
+    Bn = w.B if B is None else B
+    seqlens = decode_seqlens(w.B, w.lmin, w.lmax, w.seqlens_seed)[:Bn]
+    return paged_decode_inputs(Bn, w.Hq, w.Hkv, w.page_size, w.d, "bf16", w.seed, seqlens,
+                               max_pages=w.max_pages)
+
+
+def paged_decode_inputs(B, Hq, Hkv, page_size, d, dtype, seed, seqlens, max_pages=None):
     """Q [B,Hq,1,d] and a paged KV cache for sequences of the given lengths.
 
     Pages: [num_pages, Hkv, page_size, d]; each sequence gets ceil(L_b /
@@ -175,7 +213,7 @@ def paged_decode_inputs(B, Hq, Hkv, page_size, d, dtype, seed, seqlens):
     """
     seqlens = np.asarray(seqlens, dtype=np.int32)
     npb = [(int(L) + page_size - 1) // page_size for L in seqlens]
-    max_pages = max(1, max(npb))
+    max_pages = max(1, max(npb)) if max_pages is None else max_pages
     num_pages = max(1, sum(npb))
     rng = np.random.Generator(np.random.PCG64(seed + 500))
     perm = rng.permutation(num_pages).astype(np.int32)

@@ -121,6 +121,56 @@ int fa_decode(const void* q, const void* k, const void* v, const int* seqlens_k,
               int dtype, void* stream);
 
 /*
+ * fa_decode_paged_num_splits / fa_decode_paged_workspace_bytes - the split
+ * count fa_decode_paged uses (num_splits = 0: chosen from B, Hkv, the head
+ * groups and page_size * max_pages; otherwise num_splits) and the workspace
+ * it needs, 4 * splits * B * Hq * (d + 1) bytes.  Both return 0 for sizes
+ * fa_decode_paged would reject.
+ */
+int fa_decode_paged_num_splits(int B, int Hq, int Hkv, int page_size, int max_pages, int d,
+                               int num_splits);
+size_t fa_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int page_size, int max_pages,
+                                       int d, int num_splits);
+
+/*
+ * fa_decode_paged - decode with grouped KV heads over a paged KV cache.
+ *
+ * Decode reads the whole KV cache once per generated token ("Atenção
+ * eficiente — FlashAttention, sparse e híbrida", section "FlashAttention não
+ * acelera o decode token a token"); sharing each KV head among several query
+ * heads (MQA, GQA: the page's "Veja também" list) shrinks that cache, and
+ * Paged Attention keeps it in fixed-size pages located through a per-sequence
+ * table (table of section "Sparse e híbrida").  Per (b, h) the result is
+ * exactly fa_decode's: one query against keys [0, L_b), split over the keys
+ * and merged by LSE.
+ *
+ * q           : [B, Hq, 1, d] bfloat16.
+ * k_pages,
+ * v_pages     : [num_pages, Hkv, page_size, d] bfloat16.  Query head h uses
+ *               KV head h / (Hq / Hkv); Hq must be a multiple of Hkv (Hkv = Hq
+ *               is multi-head, Hkv = 1 multi-query attention).
+ * block_table : device int32 [B, max_pages]: key t of sequence b is row
+ *               t % page_size of page block_table[b][t / page_size].  Entries
+ *               past the sequence's last page are never read; a page id
+ *               outside [0, num_pages) is clamped into that range (the reads
+ *               stay inside the cache; the result for that sequence is then
+ *               meaningless).
+ * seqlens_k   : device int32 [B], L_b, clamped on the device to
+ *               [0, page_size * max_pages]; L_b = 0 yields O = 0, LSE = -inf.
+ *               Rows of a page at or beyond L_b are never read.
+ * page_size   : a power of two in [16, 65536]; page_size * max_pages <= 2^20.
+ * o           : [B, Hq, 1, d] bfloat16 output; lse: [B, Hq] float output.
+ * num_splits  : 0 = automatic, else 1..1024 (chunks are multiples of 128 keys).
+ * workspace   : >= fa_decode_paged_workspace_bytes(...) bytes, 16-byte aligned.
+ * dtype       : FA_BF16 only (FA_ERR_UNSUPPORTED otherwise).
+ */
+int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                    const int* block_table, const int* seqlens_k, int B, int Hq, int Hkv,
+                    int num_pages, int page_size, int max_pages, int d, float tau, void* o,
+                    float* lse, int num_splits, void* workspace, size_t workspace_bytes,
+                    int dtype, void* stream);
+
+/*
  * fa_bwd_workspace_bytes - workspace of fa_bwd: D, B*H*N floats.
  */
 size_t fa_bwd_workspace_bytes(int B, int H, int N);

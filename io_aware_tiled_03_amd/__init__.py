@@ -8,6 +8,7 @@ elsewhere.
 
     o, lse = fwd(q, k, v, tau=None, causal=False)
     o, lse = decode(q, k, v, seqlens_k, tau=None, num_splits=0)
+    o, lse = decode_paged(q, k_pages, v_pages, block_table, seqlens_k, tau=None)
     dq, dk, dv = bwd(q, k, v, o, lse, do, tau=None, causal=False)
 
 Tensors are contiguous [B, H, N, d] on the GPU, dtype bfloat16 or float32.
@@ -33,6 +34,10 @@ SIGNATURES = {
     "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "fa_decode_num_splits": (_I, [_I, _I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _I, _P, _Z, _I, _P]),
+    "fa_decode_paged_num_splits": (_I, [_I, _I, _I, _I, _I, _I, _I]),
+    "fa_decode_paged_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
+    "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _I, _P,
+                             _Z, _I, _P]),
     "fa_bwd_workspace_bytes": (_Z, [_I, _I, _I]),
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _Z, _I, _P]),
     "fa_bwd_stage": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _Z,
@@ -132,6 +137,46 @@ def decode(q, k, v, seqlens_k, tau=None, num_splits=0, o=None, lse=None, workspa
                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                          _dtype_code(q), _stream(q))
     check("fa_decode", st)
+    return o, lse
+
+
+def decode_paged_num_splits(B, Hq, Hkv, page_size, max_pages, d, num_splits=0):
+    return int(lib().fa_decode_paged_num_splits(B, Hq, Hkv, page_size, max_pages, d, num_splits))
+
+
+def decode_paged_workspace_bytes(B, Hq, Hkv, page_size, max_pages, d, num_splits=0):
+    return int(lib().fa_decode_paged_workspace_bytes(B, Hq, Hkv, page_size, max_pages, d,
+                                                     num_splits))
+
+
+def decode_paged(q, k_pages, v_pages, block_table, seqlens_k, tau=None, num_splits=0, o=None,
+                 lse=None, workspace=None):
+    """Decode with grouped KV heads over a paged cache, via fa_decode_paged.
+
+    q [B, Hq, 1, d]; k_pages, v_pages [num_pages, Hkv, page_size, d];
+    block_table int32 [B, max_pages]; seqlens_k int32 [B]."""
+    import torch
+    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"),
+                 (block_table, "block_table"), (seqlens_k, "seqlens_k")):
+        _need(t, n)
+    if block_table.dtype != torch.int32 or seqlens_k.dtype != torch.int32:
+        raise TypeError("block_table and seqlens_k must be int32")
+    B, Hq, _, d = q.shape
+    num_pages, Hkv, page_size, _ = k_pages.shape
+    max_pages = block_table.shape[1]
+    tau = 1.0 / math.sqrt(d) if tau is None else float(tau)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    need = decode_paged_workspace_bytes(B, Hq, Hkv, page_size, max_pages, d, num_splits)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    st = lib().fa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                               block_table.data_ptr(), seqlens_k.data_ptr(), B, Hq, Hkv,
+                               num_pages, page_size, max_pages, d, tau, o.data_ptr(),
+                               lse.data_ptr(), int(num_splits), workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), _dtype_code(q),
+                               _stream(q))
+    check("fa_decode_paged", st)
     return o, lse
 
 

@@ -88,6 +88,63 @@ int fa_decode(const void* q, const void* k, const void* v, const int* seqlens_k,
     return after_launch();
 }
 
+// Paged cache sizes: returns FA_OK or the status fa_decode_paged reports.
+static int check_paged(int B, int Hq, int Hkv, int page_size, int max_pages, int d) {
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return FA_ERR_SHAPE;
+    if ((long long)B * Hq > 0x7fffffffLL) return FA_ERR_SHAPE;
+    if (page_size < 16 || page_size > 65536 || (page_size & (page_size - 1)) != 0) return FA_ERR_SHAPE;
+    if (max_pages < 1 || (long long)page_size * max_pages > (1LL << 20)) return FA_ERR_SHAPE;
+    if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+    return FA_OK;
+}
+
+int fa_decode_paged_num_splits(int B, int Hq, int Hkv, int page_size, int max_pages, int d,
+                               int num_splits) {
+    if (check_paged(B, Hq, Hkv, page_size, max_pages, d) != FA_OK) return 0;
+    if (num_splits < 0 || num_splits > 1024) return 0;
+    return fa::decode_paged_splits(B, Hq, Hkv, page_size * max_pages, num_splits);
+}
+
+size_t fa_decode_paged_workspace_bytes(int B, int Hq, int Hkv, int page_size, int max_pages, int d,
+                                       int num_splits) {
+    const int s = fa_decode_paged_num_splits(B, Hq, Hkv, page_size, max_pages, d, num_splits);
+    if (s == 0) return 0;
+    return fa::decode_ws_bytes(B, Hq, d, s);
+}
+
+int fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                    const int* block_table, const int* seqlens_k, int B, int Hq, int Hkv,
+                    int num_pages, int page_size, int max_pages, int d, float tau, void* o,
+                    float* lse, int num_splits, void* workspace, size_t workspace_bytes,
+                    int dtype, void* stream) {
+    if (!q || !k_pages || !v_pages || !block_table || !seqlens_k || !o || !lse) return FA_ERR_NULL;
+    int st = check_paged(B, Hq, Hkv, page_size, max_pages, d);
+    if (st != FA_OK) return st;
+    if (num_pages < 1) return FA_ERR_SHAPE;
+    if ((double)num_pages * Hkv * page_size * d * 2.0 > 9.0e18) return FA_ERR_SHAPE;
+    if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (!(tau > 0.f) || !isfinite(tau)) return FA_ERR_ARG;
+    if (num_splits < 0 || num_splits > 1024) return FA_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k_pages) || !aligned16(v_pages) || !aligned16(o) ||
+        !aligned4(lse) || !aligned4(block_table) || !aligned4(seqlens_k))
+        return FA_ERR_ALIGN;
+    const int max_keys = page_size * max_pages;
+    const int S = fa::decode_paged_splits(B, Hq, Hkv, max_keys, num_splits);
+    const size_t need = fa::decode_ws_bytes(B, Hq, d, S);
+    if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return FA_ERR_ALIGN;
+    const long long groups = (Hq / Hkv + 15) / 16;
+    if (!grid_ok((long long)S * B * Hkv * groups, 256)) return FA_ERR_SHAPE;
+    float* ws = (float*)workspace;
+    const size_t n_o = (size_t)S * B * Hq * d;
+    fa::PagedDecodeArgs a{q, k_pages, v_pages, block_table, seqlens_k, B, Hq, Hkv, num_pages,
+                          page_size, max_pages, d, tau, o, lse, S,
+                          fa::decode_paged_chunk(max_keys, S), ws, ws + n_o};
+    (void)hipGetLastError();
+    fa::launch_decode_paged(a, (hipStream_t)stream);
+    return after_launch();
+}
+
 size_t fa_bwd_workspace_bytes(int B, int H, int N) {
     if (B < 1 || H < 1 || N < 1) return 0;
     return (size_t)B * H * N * sizeof(float);

@@ -20,6 +20,8 @@ namespace fa {
 
 namespace {
 
+template <int N_> using ic = std::integral_constant<int, N_>;
+
 template <typename T> struct Elem;
 template <> struct Elem<uint16_t> {   // bf16: 8 elements per 16-byte piece
     static constexpr int PER16 = 8;
@@ -259,6 +261,248 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
     if (t == 0) LSE[bh] = (M == neg_inf()) ? neg_inf() : M + __logf(sum);
 }
 
+// ---------------------------------------------------------------------------
+// Paged cache, grouped KV heads.  One workgroup serves up to 16 query heads
+// that share one KV head (h0 .. h0+15 of the group), for one sequence and one
+// split, so each KV byte is read from HBM once per group.  Each wave streams
+// its own 32-key blocks (blocks w, w+4, ... of the split) into registers,
+// two blocks in flight (the next block's loads are issued before the current
+// one is consumed), and computes
+//   S^T [32 keys x 16 heads] = K Q^T     (16x16x32 MFMA; the K registers are
+//                                         loaded directly in A-operand layout)
+//   O^T [d x 16 heads]      += V^T P^T   (16x16x32 MFMA; V goes through a
+//                                         per-wave LDS tile for the transposing
+//                                         read, P^T comes straight from S^T's
+//                                         accumulator registers)
+// with the running max / sum per head kept in the lanes of that head.  The
+// four waves are merged through LDS at the end as in decode_split_kernel.
+// With G query heads per KV head these are G-row contractions; heads beyond
+// G in the last group of 16 carry Q = 0 and are never stored.
+constexpr int kPagedBK = 32;   // keys per wave block
+
+template <int D>
+struct PagedShape {
+    static constexpr int LGD = D == 64 ? 6 : 7;
+    static constexpr int VSTR = D + 16;          // padded LDS row of the V tile (elements)
+    static constexpr int CPR = D / 8;            // 16-byte pieces per row
+    static constexpr int VRPI = 64 / CPR;        // V rows per wave load instruction
+    static constexpr int NVL = kPagedBK / VRPI;  // V load instructions per block
+};
+
+template <int D>
+struct PagedRegs {
+    u32x4 k[2][D / 32];                 // K, A-operand layout: half mm, d slice kk
+    u32x4 v[PagedShape<D>::NVL];        // V rows, 16 bytes per lane per instruction
+};
+
+template <int D>
+__global__ __launch_bounds__(256, 2) void decode_paged_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kp, const uint16_t* __restrict__ Vp,
+    const int* __restrict__ table, const int* __restrict__ seqlens, int B, int Hq, int Hkv, int G,
+    int NG, int num_pages, int lgP, int max_pages, int chunk, float scale_log2, float tau,
+    float* __restrict__ ws_o, float* __restrict__ ws_lse) {
+    using S = PagedShape<D>;
+    constexpr int TILE = kPagedBK * S::VSTR;   // V tile elements per wave
+    __shared__ __attribute__((aligned(16))) uint16_t sv[4 * TILE];
+
+    // Grid: (b, kv head, head group) fastest, then the split, so consecutive
+    // workgroups (dealt round-robin to the XCDs) belong to different sequences.
+    const int per_s = B * Hkv * NG;
+    const int s = (int)(blockIdx.x / (unsigned)per_s);
+    int rem = (int)(blockIdx.x % (unsigned)per_s);
+    const int hg = rem % NG;
+    rem /= NG;
+    const int hkv = rem % Hkv, b = rem / Hkv;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int hl = lane & 15, gq = lane >> 4;
+    const int pmask = (1 << lgP) - 1;
+    const int L = min(max(seqlens[b], 0), max_pages << lgP);
+    const int kb = s * chunk, ke = min(L, kb + chunk);
+    const int h0 = hkv * G + hg * 16;          // first query head served here
+    const int nh = min(16, G - hg * 16);       // query heads served here
+    const size_t ws_row0 = (size_t)s * B * Hq + (size_t)b * Hq + h0;
+
+    if (kb >= ke) {   // empty split: contributes nothing to the merge
+        for (int i = tid; i < nh * D; i += 256) ws_o[ws_row0 * D + i] = 0.f;
+        if (tid < nh) ws_lse[ws_row0 + tid] = neg_inf();
+        return;
+    }
+
+    // B operand of S^T = K Q^T: lane i holds head i%16, the same d slots as K.
+    u32x4 qf[D / 32];
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk)
+        qf[kk] = hl < nh ? ld16(Q + ((size_t)b * Hq + h0 + hl) * D + 32 * kk + 8 * gq)
+                         : u32x4{0, 0, 0, 0};
+
+    const int* trow = table + (size_t)b * max_pages;
+    const size_t page_stride = (size_t)Hkv << (lgP + S::LGD);   // elements per page
+    const size_t head_off = (size_t)hkv << (lgP + S::LGD);
+    const int vr = lane / S::CPR, vc = (lane % S::CPR) * 8;      // V load: row in group, column
+
+    // Page bases (elements) of the two 16-key halves of the block at key k0.
+    // Each half lies in one page (page_size >= 16, halves start at multiples
+    // of 16), so its base is wave-uniform.  Page ids are clamped into
+    // [0, num_pages) so that any table content keeps the reads in the cache.
+    struct PageBases { size_t b[2]; };
+    auto pages = [&](int k0) __attribute__((always_inline)) {
+        PageBases pb;
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+            const int kf = min(k0 + 16 * mm, ke - 1);
+            pb.b[mm] = (size_t)min(max(trow[kf >> lgP], 0), num_pages - 1) * page_stride + head_off;
+        }
+        return pb;
+    };
+    // Loads of the block at key k0 (page bases fetched one block earlier);
+    // rows past ke repeat row ke - 1.
+    auto load = [&](PagedRegs<D>& R, int k0, const PageBases& pb) __attribute__((always_inline)) {
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+            const int key = min(k0 + 16 * mm + hl, ke - 1);
+            const uint16_t* src = Kp + pb.b[mm] + ((size_t)(key & pmask) << S::LGD) + 8 * gq;
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) R.k[mm][kk] = ld16_stream(src + 32 * kk);
+        }
+#pragma unroll
+        for (int t = 0; t < S::NVL; ++t) {
+            const int mm = t * S::VRPI / 16;
+            const int key = min(k0 + t * S::VRPI + vr, ke - 1);
+            R.v[t] = ld16_stream(Vp + pb.b[mm] + ((size_t)(key & pmask) << S::LGD) + vc);
+        }
+    };
+
+    // V^T operand: lane s of 16-lane group gq addresses key 4 gq + s/4 (and
+    // 16 + 4 gq + s/4), columns 16 db + 4 (s%4); the transposing read hands
+    // lane i keys 4 gq .. 4 gq + 3 (and 16 + ...) of column 16 db + i%16, the
+    // keys whose probabilities S^T's accumulator registers leave in lane i.
+    uint16_t* const tile = sv + wave * TILE;
+    const int voff = (4 * gq + (hl >> 2)) * S::VSTR + 4 * (hl & 3);
+    f32x4 oacc[D / 16];
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db) oacc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float m = neg_inf(), l = 0.f;   // running max (raw score units), lane-partial sum
+
+    auto consume = [&](const PagedRegs<D>& R, int k0) __attribute__((always_inline)) {
+#pragma unroll
+        for (int t = 0; t < S::NVL; ++t) st16(tile + (t * S::VRPI + vr) * S::VSTR + vc, R.v[t]);
+        f32x4 sc[2];   // register r of half mm: key 16 mm + 4 gq + r, head hl
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm) {
+            sc[mm] = mfma16x16x32_zero(R.k[mm][0], qf[0]);
+#pragma unroll
+            for (int kk = 1; kk < D / 32; ++kk) sc[mm] = mfma16x16x32(R.k[mm][kk], qf[kk], sc[mm]);
+        }
+        if (k0 + kPagedBK > ke) {
+#pragma unroll
+            for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (k0 + 16 * mm + 4 * gq + r >= ke) sc[mm][r] = neg_inf();
+        }
+        float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        const float mnew = fmaxf(m, mx);
+        const float alpha = fast_exp2((m - mnew) * scale_log2);
+        m = mnew;
+        l *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) oacc[db] *= alpha;
+        const float mc = mnew * scale_log2;
+        float p[2][4];
+#pragma unroll
+        for (int mm = 0; mm < 2; ++mm)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[mm][r] = fast_exp2(__builtin_fmaf(sc[mm][r], scale_log2, -mc));
+                l += p[mm][r];
+            }
+        u32x4 pf;
+        pf[0] = pack_bf16x2(p[0][0], p[0][1]);
+        pf[1] = pack_bf16x2(p[0][2], p[0][3]);
+        pf[2] = pack_bf16x2(p[1][0], p[1][1]);
+        pf[3] = pack_bf16x2(p[1][2], p[1][3]);
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db) {
+            const u32x4 va = lds_read_tr16_x2(tile + voff + 16 * db, tile + voff + 16 * S::VSTR + 16 * db);
+            oacc[db] = mfma16x16x32(va, pf, oacc[db]);
+        }
+    };
+
+    // Blocks of this wave: keys kb + 32 (wave + 4 i), i < nbw.  Two register
+    // sets; the loads of block i + 1 are issued before block i is consumed.
+    // The loads are unconditional (past the last block they repeat it, from
+    // cache) so that every wait the compiler places is exact.
+    const int nblk = (ke - kb + kPagedBK - 1) / kPagedBK;
+    const int nbw = nblk > wave ? (nblk - wave + 3) / 4 : 0;
+    // A scheduling barrier after each batch of loads keeps the compiler from
+    // sinking them below the previous block's MFMAs.
+    if (nbw > 0) {
+        auto key0 = [&](int i) { return kb + kPagedBK * (wave + 4 * min(i, nbw - 1)); };
+        PagedRegs<D> ra, rb;
+        load(ra, key0(0), pages(key0(0)));
+        PageBases pn = pages(key0(1));
+        for (int i = 0; i < nbw; i += 2) {
+            load(rb, key0(i + 1), pn);
+            pn = pages(key0(i + 2));
+            __builtin_amdgcn_sched_barrier(0);
+            consume(ra, key0(i));
+            if (i + 1 >= nbw) break;
+            load(ra, key0(i + 2), pn);
+            pn = pages(key0(i + 3));
+            __builtin_amdgcn_sched_barrier(0);
+            consume(rb, key0(i + 1));
+        }
+    }
+    l += __shfl_xor(l, 16, 64);
+    l += __shfl_xor(l, 32, 64);
+
+    // Merge the four waves through LDS (reusing the V tiles).
+    __syncthreads();
+    float* sm = reinterpret_cast<float*>(sv);   // [4][16] maxima
+    float* sl = sm + 64;                        // [4][16] sums
+    float* so = sl + 64;                        // [4][16][D] outputs
+    static_assert(sizeof(sv) >= (128 + 64 * D) * sizeof(float), "merge area fits");
+    if (gq == 0) {
+        sm[wave * 16 + hl] = m;
+        sl[wave * 16 + hl] = l;
+    }
+#pragma unroll
+    for (int db = 0; db < D / 16; ++db)
+        *reinterpret_cast<f32x4*>(&so[(wave * 16 + hl) * D + 16 * db + 4 * gq]) = oacc[db];
+    __syncthreads();
+    for (int i = tid; i < nh * D; i += 256) {
+        const int h = i / D, dd = i % D;
+        const float M = fmaxf(fmaxf(sm[h], sm[16 + h]), fmaxf(sm[32 + h], sm[48 + h]));
+        float lt = 0.f, ot = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            const float mw = sm[w * 16 + h];
+            const float a = mw == neg_inf() ? 0.f : fast_exp2((mw - M) * scale_log2);
+            lt += sl[w * 16 + h] * a;
+            ot += so[(w * 16 + h) * D + dd] * a;
+        }
+        ws_o[ws_row0 * D + i] = ot / lt;
+        if (dd == 0) ws_lse[ws_row0 + h] = M * tau + __logf(lt);
+    }
+}
+
+template <int D>
+void launch_paged(const PagedDecodeArgs& a, hipStream_t st) {
+    const int G = a.Hq / a.Hkv, NG = (G + 15) / 16;
+    const int lgP = __builtin_ctz((unsigned)a.page_size);
+    const unsigned grid = (unsigned)a.num_splits * a.B * a.Hkv * NG;
+    hipLaunchKernelGGL((decode_paged_kernel<D>), dim3(grid), dim3(256), 0, st,
+                       (const uint16_t*)a.q, (const uint16_t*)a.k_pages, (const uint16_t*)a.v_pages,
+                       a.block_table, a.seqlens, a.B, a.Hq, a.Hkv, G, NG, a.num_pages, lgP,
+                       a.max_pages, a.chunk, a.tau * kLog2e, a.tau, a.ws_o, a.ws_lse);
+    hipLaunchKernelGGL((decode_merge_kernel<uint16_t, D>), dim3(a.B * a.Hq), dim3(64), 0, st,
+                       a.ws_o, a.ws_lse, a.num_splits, a.B * a.Hq, (uint16_t*)a.o, a.lse);
+}
+
 template <typename T, int D>
 void launch(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(a.num_splits * a.B * a.H), dim3(256), 0, st,
@@ -291,6 +535,29 @@ int decode_splits(int B, int H, int N_max, int d, int requested) {
 
 size_t decode_ws_bytes(int B, int H, int d, int splits) {
     return (size_t)splits * B * H * (size_t)(d + 1) * sizeof(float);
+}
+
+int decode_paged_chunk(int max_keys, int splits) {
+    const int c = (max_keys + splits - 1) / splits;
+    return (c + 127) / 128 * 128;
+}
+
+int decode_paged_splits(int B, int Hq, int Hkv, int max_keys, int requested) {
+    if (requested > 0) {
+        const int c = decode_paged_chunk(max_keys, requested);
+        return (max_keys + c - 1) / c;
+    }
+    // Automatic: the shortest chunk (>= 512 keys) that keeps the grid at or
+    // below 4096 workgroups (each workgroup holds a whole CU's worth of LDS).
+    const long units = (long)B * Hkv * ((Hq / Hkv + 15) / 16);
+    int c = 512;
+    while (c < max_keys && units * ((max_keys + c - 1) / c) > 4096) c *= 2;
+    c = decode_paged_chunk(max_keys, (max_keys + c - 1) / c);
+    return (max_keys + c - 1) / c;
+}
+
+void launch_decode_paged(const PagedDecodeArgs& a, hipStream_t st) {
+    a.d == 64 ? launch_paged<64>(a, st) : launch_paged<128>(a, st);
 }
 
 void launch_decode(const DecodeArgs& a, hipStream_t st) {

@@ -40,6 +40,25 @@ __device__ __forceinline__ f32x16 mfma32x32x16(const u32x4& a, const u32x4& b, c
                                                     __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// v_mfma_f32_16x16x32_bf16: A (16 x 32): lane i holds row i%16, eight k-slots
+// of group i/16; B (32 x 16): column i%16, the same k-slots; C (16 x 16) fp32:
+// lane i, register r holds row 4*(i/16) + r, column i%16.
+__device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma16x16x32_zero(const u32x4& a, const u32x4& b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                    __builtin_bit_cast(bf16x8, b), f32x4{}, 0, 0, 0);
+}
+
+// v_mfma_f32_16x16x16_bf16: as above with four k-slots per lane (k = 4*(i/16) + j).
+__device__ __forceinline__ f32x4 mfma16x16x16(const u32x2& a, const u32x2& b, const f32x4& c) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(v4i16, a),
+                                                      __builtin_bit_cast(v4i16, b), c, 0, 0, 0);
+}
+
 __device__ __forceinline__ f32x16 mfma32x32x2f32(float a, float b, const f32x16& c) {
     return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
 }
@@ -143,7 +162,26 @@ __device__ __forceinline__ void buf_ld16_lds(rsrc_t r, uint32_t byte_off, void* 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
                                              byte_off, 0, 0, 0);
 }
+// Direct global -> LDS copy of 16 bytes per lane from a per-lane 64-bit
+// address (no 4 GiB descriptor limit); lane i's bytes land at lds_base + 16*i
+// (lds_base wave-uniform, passed in M0).  Issued as inline assembly so that
+// the compiler keeps no bookkeeping of it: where such bookkeeping meets a
+// branch it is merged conservatively into a wait for every outstanding copy
+// before the next LDS read.  The caller orders the copy itself: wait_vmem_le
+// before reading the data, wait_lgkm before refilling a buffer whose reads
+// may still be in flight.
+__device__ __forceinline__ void glb_ld16_lds_async(const void* src, void* lds_base) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base;
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+__device__ __forceinline__ void wait_lgkm() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+    static_assert(N >= 0 && N < 64, "vmcnt field");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 }  // namespace fa

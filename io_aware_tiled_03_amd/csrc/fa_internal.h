@@ -37,6 +37,23 @@ int decode_splits(int B, int H, int N_max, int d, int requested);
 int decode_chunk(int N_max, int splits);
 size_t decode_ws_bytes(int B, int H, int d, int splits);
 
+struct PagedDecodeArgs {
+    const void *q, *k_pages, *v_pages;
+    const int* block_table;   // [B, max_pages] page ids
+    const int* seqlens;       // [B]
+    int B, Hq, Hkv, num_pages, page_size, max_pages, d;
+    float tau;
+    void* o;
+    float* lse;
+    int num_splits;           // resolved (>= 1)
+    int chunk;                // keys per split, a multiple of 128
+    float* ws_o;              // [num_splits, B, Hq, d]
+    float* ws_lse;            // [num_splits, B, Hq]
+};
+void launch_decode_paged(const PagedDecodeArgs& a, hipStream_t st);
+int decode_paged_splits(int B, int Hq, int Hkv, int max_keys, int requested);
+int decode_paged_chunk(int max_keys, int splits);
+
 struct BwdArgs {
     const void *q, *k, *v, *o;
     const float* lse;

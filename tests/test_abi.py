@@ -104,6 +104,52 @@ def test_decode_split_rule():
     assert lib.fa_decode_workspace_bytes(1, 1, 100, 96, 0) == 0
 
 
+def _paged(lib, **kw):
+    a = dict(q=P, kp=P, vp=P, bt=P, sl=P, B=2, Hq=8, Hkv=2, npages=10, ps=16, mp=8, d=128,
+             tau=0.1, o=P, lse=P, ns=0, ws=P, wsb=1 << 30, dtype=1)
+    a.update(kw)
+    return lib.fa_decode_paged(a["q"], a["kp"], a["vp"], a["bt"], a["sl"], a["B"], a["Hq"],
+                               a["Hkv"], a["npages"], a["ps"], a["mp"], a["d"], a["tau"], a["o"],
+                               a["lse"], a["ns"], a["ws"], a["wsb"], a["dtype"], None)
+
+
+def test_decode_paged_rejects_bad_arguments():
+    fa, lib = _lib()
+    assert _paged(lib, bt=None) == 1
+    assert _paged(lib, sl=None) == 1
+    assert _paged(lib, Hq=7) == 2          # not a multiple of Hkv
+    assert _paged(lib, Hkv=0) == 2
+    assert _paged(lib, ps=24) == 2         # not a power of two
+    assert _paged(lib, ps=8) == 2          # below 16
+    assert _paged(lib, mp=0) == 2
+    assert _paged(lib, ps=1 << 16, mp=32) == 2   # more than 2^20 keys
+    assert _paged(lib, npages=0) == 2
+    assert _paged(lib, d=96) == 3
+    assert _paged(lib, dtype=0) == 3       # bf16 only
+    assert _paged(lib, tau=-1.0) == 7
+    assert _paged(lib, ns=2000) == 7
+    assert _paged(lib, ws=None) == 4
+    need = lib.fa_decode_paged_workspace_bytes(2, 8, 2, 16, 8, 128, 0)
+    assert need > 0
+    assert _paged(lib, wsb=need - 1) == 4
+    assert _paged(lib, kp=P + 8) == 6
+    assert _paged(lib, bt=P + 2) == 6
+
+
+def test_decode_paged_split_rule():
+    fa, lib = _lib()
+    # automatic: chunks of >= 512 keys, doubled while the grid would exceed
+    # 4096 workgroups; (b, kv head, group of 16 query heads) units
+    assert lib.fa_decode_paged_num_splits(64, 32, 8, 16, 512, 128, 0) == 8
+    assert lib.fa_decode_paged_num_splits(1, 32, 8, 16, 512, 128, 0) == 16
+    assert lib.fa_decode_paged_num_splits(1, 8, 8, 16, 4, 128, 0) == 1
+    # explicit counts: equal chunks rounded up to 128 keys
+    assert lib.fa_decode_paged_num_splits(1, 8, 8, 16, 20, 128, 7) == 3   # 320 keys, chunk 128
+    s = lib.fa_decode_paged_num_splits(64, 32, 8, 16, 512, 128, 0)
+    assert lib.fa_decode_paged_workspace_bytes(64, 32, 8, 16, 512, 128, 0) == s * 64 * 32 * 129 * 4
+    assert lib.fa_decode_paged_workspace_bytes(1, 8, 3, 16, 4, 128, 0) == 0
+
+
 def _bwd(lib, **kw):
     a = dict(q=P, k=P, v=P, o=P, lse=P, do=P, dq=P, dk=P, dv=P, B=1, H=2, N=64, d=64, tau=0.125,
              causal=1, ws=P, wsb=1 << 20, dtype=1)
