@@ -265,20 +265,25 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
 // Paged cache, grouped KV heads.  One workgroup serves up to 16 query heads
 // that share one KV head (h0 .. h0+15 of the group), for one sequence and one
 // split, so each KV byte is read from HBM once per group.  Each wave streams
-// its own 32-key blocks (blocks w, w+4, ... of the split) into registers,
+// its own 16-key blocks (blocks w, w+4, ... of the split) into registers,
 // two blocks in flight (the next block's loads are issued before the current
 // one is consumed), and computes
-//   S^T [32 keys x 16 heads] = K Q^T     (16x16x32 MFMA; the K registers are
+//   S^T [16 keys x 16 heads] = K Q^T     (16x16x32 MFMA; the K registers are
 //                                         loaded directly in A-operand layout)
-//   O^T [d x 16 heads]      += V^T P^T   (16x16x32 MFMA; V goes through a
+//   O^T [d x 16 heads]      += V^T P^T   (16x16x16 MFMA; V goes through a
 //                                         per-wave LDS tile for the transposing
 //                                         read, P^T comes straight from S^T's
 //                                         accumulator registers)
 // with the running max / sum per head kept in the lanes of that head.  The
 // four waves are merged through LDS at the end as in decode_split_kernel.
 // With G query heads per KV head these are G-row contractions; heads beyond
-// G in the last group of 16 carry Q = 0 and are never stored.
-constexpr int kPagedBK = 32;   // keys per wave block
+// G in the last group of 16 carry Q = 0 and are never stored.  A 16-key block
+// starting at a multiple of 16 lies in one page (page_size >= 16), so its
+// page base is wave-uniform.
+constexpr int kPagedBK = 16;   // keys per wave block
+#ifndef FA_PAGED_MINB
+#define FA_PAGED_MINB 2        // workgroups per CU the register budget is sized for
+#endif
 
 template <int D>
 struct PagedShape {
@@ -287,23 +292,25 @@ struct PagedShape {
     static constexpr int CPR = D / 8;            // 16-byte pieces per row
     static constexpr int VRPI = 64 / CPR;        // V rows per wave load instruction
     static constexpr int NVL = kPagedBK / VRPI;  // V load instructions per block
+    static constexpr int TILE = kPagedBK * VSTR; // V tile elements per wave
 };
 
 template <int D>
 struct PagedRegs {
-    u32x4 k[2][D / 32];                 // K, A-operand layout: half mm, d slice kk
+    u32x4 k[D / 32];                    // K rows, A-operand layout (d slice kk)
     u32x4 v[PagedShape<D>::NVL];        // V rows, 16 bytes per lane per instruction
 };
 
 template <int D>
-__global__ __launch_bounds__(256, 2) void decode_paged_kernel(
+__global__ __launch_bounds__(256, FA_PAGED_MINB) void decode_paged_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kp, const uint16_t* __restrict__ Vp,
     const int* __restrict__ table, const int* __restrict__ seqlens, int B, int Hq, int Hkv, int G,
     int NG, int num_pages, int lgP, int max_pages, int chunk, float scale_log2, float tau,
     float* __restrict__ ws_o, float* __restrict__ ws_lse) {
     using S = PagedShape<D>;
-    constexpr int TILE = kPagedBK * S::VSTR;   // V tile elements per wave
-    __shared__ __attribute__((aligned(16))) uint16_t sv[4 * TILE];
+    // V tiles during the sweep; the cross-wave merge reuses the same bytes.
+    constexpr int LDS_BYTES = 4 * S::TILE * 2 > (128 + 64 * D) * 4 ? 4 * S::TILE * 2 : (128 + 64 * D) * 4;
+    __shared__ __attribute__((aligned(16))) unsigned char smem[LDS_BYTES];
 
     // Grid: (b, kv head, head group) fastest, then the split, so consecutive
     // workgroups (dealt round-robin to the XCDs) belong to different sequences.
@@ -339,45 +346,43 @@ __global__ __launch_bounds__(256, 2) void decode_paged_kernel(
     const int* trow = table + (size_t)b * max_pages;
     const size_t page_stride = (size_t)Hkv << (lgP + S::LGD);   // elements per page
     const size_t head_off = (size_t)hkv << (lgP + S::LGD);
-    const int vr = lane / S::CPR, vc = (lane % S::CPR) * 8;      // V load: row in group, column
+    // Per-lane byte offsets inside a block, loop-invariant: K row hl, d slice
+    // 8 gq (+32 kk); V row t * VRPI + lane / CPR, column 8 (lane % CPR).
+    const int vr = lane / S::CPR, vc = (lane % S::CPR) * 8;
+    const uint32_t koff = (uint32_t)(hl * D + 8 * gq) * 2;
+    const uint32_t voff_g = (uint32_t)(vr * D + vc) * 2;
 
-    // Page bases (elements) of the two 16-key halves of the block at key k0.
-    // Each half lies in one page (page_size >= 16, halves start at multiples
-    // of 16), so its base is wave-uniform.  Page ids are clamped into
+    // Buffer descriptors of the block at key k0: base = the block's first
+    // row in its page (a 16-key block starting at a multiple of 16 lies in
+    // one page), size = its rows before ke, so rows past ke read as zero (their
+    // scores are masked; their V rows meet p = 0).  Page ids are clamped into
     // [0, num_pages) so that any table content keeps the reads in the cache.
-    struct PageBases { size_t b[2]; };
-    auto pages = [&](int k0) __attribute__((always_inline)) {
-        PageBases pb;
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-            const int kf = min(k0 + 16 * mm, ke - 1);
-            pb.b[mm] = (size_t)min(max(trow[kf >> lgP], 0), num_pages - 1) * page_stride + head_off;
-        }
-        return pb;
+    // (The block's element offset and size pass through readfirstlane so that
+    // the compiler treats the descriptors as wave-uniform scalars.)
+    struct BlockRsrc { size_t base; uint32_t bytes; };
+    auto block_rsrc = [&](int k0) __attribute__((always_inline)) {
+        const int kc = min(k0, ke - 1);
+        const int pg = min(max(trow[kc >> lgP], 0), num_pages - 1);
+        const size_t base = (size_t)pg * page_stride + head_off + ((size_t)(kc & pmask) << S::LGD);
+        const uint32_t bytes = (uint32_t)max(min(ke - k0, kPagedBK), 0) * (D * 2);
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+        return BlockRsrc{((size_t)hi << 32) | lo, (uint32_t)__builtin_amdgcn_readfirstlane(bytes)};
     };
-    // Loads of the block at key k0 (page bases fetched one block earlier);
-    // rows past ke repeat row ke - 1.
-    auto load = [&](PagedRegs<D>& R, int k0, const PageBases& pb) __attribute__((always_inline)) {
+    auto load = [&](PagedRegs<D>& R, const BlockRsrc& br) __attribute__((always_inline)) {
+        const rsrc_t kr = make_rsrc(Kp + br.base, br.bytes);
+        const rsrc_t vr_ = make_rsrc(Vp + br.base, br.bytes);
 #pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-            const int key = min(k0 + 16 * mm + hl, ke - 1);
-            const uint16_t* src = Kp + pb.b[mm] + ((size_t)(key & pmask) << S::LGD) + 8 * gq;
+        for (int kk = 0; kk < D / 32; ++kk) R.k[kk] = buf_ld16_nt(kr, koff + 64 * kk);
 #pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) R.k[mm][kk] = ld16_stream(src + 32 * kk);
-        }
-#pragma unroll
-        for (int t = 0; t < S::NVL; ++t) {
-            const int mm = t * S::VRPI / 16;
-            const int key = min(k0 + t * S::VRPI + vr, ke - 1);
-            R.v[t] = ld16_stream(Vp + pb.b[mm] + ((size_t)(key & pmask) << S::LGD) + vc);
-        }
+        for (int t = 0; t < S::NVL; ++t) R.v[t] = buf_ld16_nt(vr_, voff_g + t * S::VRPI * D * 2);
     };
 
-    // V^T operand: lane s of 16-lane group gq addresses key 4 gq + s/4 (and
-    // 16 + 4 gq + s/4), columns 16 db + 4 (s%4); the transposing read hands
-    // lane i keys 4 gq .. 4 gq + 3 (and 16 + ...) of column 16 db + i%16, the
-    // keys whose probabilities S^T's accumulator registers leave in lane i.
-    uint16_t* const tile = sv + wave * TILE;
+    // V^T operand: lane s of 16-lane group gq addresses key 4 gq + s/4,
+    // columns 16 db + 4 (s%4); the transposing read hands lane i keys
+    // 4 gq .. 4 gq + 3 of column 16 db + i%16, the keys whose probabilities
+    // S^T's accumulator registers leave in lane i.
+    uint16_t* const tile = reinterpret_cast<uint16_t*>(smem) + wave * S::TILE;
     const int voff = (4 * gq + (hl >> 2)) * S::VSTR + 4 * (hl & 3);
     f32x4 oacc[D / 16];
 #pragma unroll
@@ -387,22 +392,15 @@ __global__ __launch_bounds__(256, 2) void decode_paged_kernel(
     auto consume = [&](const PagedRegs<D>& R, int k0) __attribute__((always_inline)) {
 #pragma unroll
         for (int t = 0; t < S::NVL; ++t) st16(tile + (t * S::VRPI + vr) * S::VSTR + vc, R.v[t]);
-        f32x4 sc[2];   // register r of half mm: key 16 mm + 4 gq + r, head hl
+        f32x4 sc = mfma16x16x32_zero(R.k[0], qf[0]);   // register r: key 4 gq + r, head hl
 #pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-            sc[mm] = mfma16x16x32_zero(R.k[mm][0], qf[0]);
-#pragma unroll
-            for (int kk = 1; kk < D / 32; ++kk) sc[mm] = mfma16x16x32(R.k[mm][kk], qf[kk], sc[mm]);
-        }
+        for (int kk = 1; kk < D / 32; ++kk) sc = mfma16x16x32(R.k[kk], qf[kk], sc);
         if (k0 + kPagedBK > ke) {
 #pragma unroll
-            for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (k0 + 16 * mm + 4 * gq + r >= ke) sc[mm][r] = neg_inf();
+            for (int r = 0; r < 4; ++r)
+                if (k0 + 4 * gq + r >= ke) sc[r] = neg_inf();
         }
-        float mx = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                         fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
         mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
         mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
         const float mnew = fmaxf(m, mx);
@@ -412,47 +410,39 @@ __global__ __launch_bounds__(256, 2) void decode_paged_kernel(
 #pragma unroll
         for (int db = 0; db < D / 16; ++db) oacc[db] *= alpha;
         const float mc = mnew * scale_log2;
-        float p[2][4];
+        float p[4];
 #pragma unroll
-        for (int mm = 0; mm < 2; ++mm)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                p[mm][r] = fast_exp2(__builtin_fmaf(sc[mm][r], scale_log2, -mc));
-                l += p[mm][r];
-            }
-        u32x4 pf;
-        pf[0] = pack_bf16x2(p[0][0], p[0][1]);
-        pf[1] = pack_bf16x2(p[0][2], p[0][3]);
-        pf[2] = pack_bf16x2(p[1][0], p[1][1]);
-        pf[3] = pack_bf16x2(p[1][2], p[1][3]);
-#pragma unroll
-        for (int db = 0; db < D / 16; ++db) {
-            const u32x4 va = lds_read_tr16_x2(tile + voff + 16 * db, tile + voff + 16 * S::VSTR + 16 * db);
-            oacc[db] = mfma16x16x32(va, pf, oacc[db]);
+        for (int r = 0; r < 4; ++r) {
+            p[r] = fast_exp2(__builtin_fmaf(sc[r], scale_log2, -mc));
+            l += p[r];
         }
+        const u32x2 pf = {pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3])};
+#pragma unroll
+        for (int db = 0; db < D / 16; ++db)
+            oacc[db] = mfma16x16x16(lds_read_tr16(tile + voff + 16 * db), pf, oacc[db]);
     };
 
-    // Blocks of this wave: keys kb + 32 (wave + 4 i), i < nbw.  Two register
-    // sets; the loads of block i + 1 are issued before block i is consumed.
-    // The loads are unconditional (past the last block they repeat it, from
-    // cache) so that every wait the compiler places is exact.
+    // Blocks of this wave: keys kb + 16 (wave + 4 i), i < nbw.  Two register
+    // sets; the loads of block i + 1 are issued before block i is consumed,
+    // and block i + 2's descriptors (page id) are fetched meanwhile.  The
+    // loads are unconditional (past the last block they repeat it, from
+    // cache) so that every wait the compiler places is exact, and a
+    // scheduling barrier after each batch keeps them ahead of the MFMAs.
     const int nblk = (ke - kb + kPagedBK - 1) / kPagedBK;
     const int nbw = nblk > wave ? (nblk - wave + 3) / 4 : 0;
-    // A scheduling barrier after each batch of loads keeps the compiler from
-    // sinking them below the previous block's MFMAs.
     if (nbw > 0) {
         auto key0 = [&](int i) { return kb + kPagedBK * (wave + 4 * min(i, nbw - 1)); };
         PagedRegs<D> ra, rb;
-        load(ra, key0(0), pages(key0(0)));
-        PageBases pn = pages(key0(1));
+        load(ra, block_rsrc(key0(0)));
+        BlockRsrc rn = block_rsrc(key0(1));
         for (int i = 0; i < nbw; i += 2) {
-            load(rb, key0(i + 1), pn);
-            pn = pages(key0(i + 2));
+            load(rb, rn);
+            rn = block_rsrc(key0(i + 2));
             __builtin_amdgcn_sched_barrier(0);
             consume(ra, key0(i));
             if (i + 1 >= nbw) break;
-            load(ra, key0(i + 2), pn);
-            pn = pages(key0(i + 3));
+            load(ra, rn);
+            rn = block_rsrc(key0(i + 3));
             __builtin_amdgcn_sched_barrier(0);
             consume(rb, key0(i + 1));
         }
@@ -460,12 +450,11 @@ __global__ __launch_bounds__(256, 2) void decode_paged_kernel(
     l += __shfl_xor(l, 16, 64);
     l += __shfl_xor(l, 32, 64);
 
-    // Merge the four waves through LDS (reusing the V tiles).
+    // Merge the four waves through LDS.
     __syncthreads();
-    float* sm = reinterpret_cast<float*>(sv);   // [4][16] maxima
-    float* sl = sm + 64;                        // [4][16] sums
-    float* so = sl + 64;                        // [4][16][D] outputs
-    static_assert(sizeof(sv) >= (128 + 64 * D) * sizeof(float), "merge area fits");
+    float* sm = reinterpret_cast<float*>(smem);   // [4][16] maxima
+    float* sl = sm + 64;                          // [4][16] sums
+    float* so = sl + 64;                          // [4][16][D] outputs
     if (gq == 0) {
         sm[wave * 16 + hl] = m;
         sl[wave * 16 + hl] = l;

@@ -154,6 +154,11 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ u32x4 buf_ld16(rsrc_t r, uint32_t byte_off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
 }
+// The same load marked non-temporal (data read once: keep it from displacing
+// reused lines in the caches).
+__device__ __forceinline__ u32x4 buf_ld16_nt(rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 2));
+}
 // Direct global -> LDS copy of 16 bytes per lane: lane i's bytes land at
 // lds_base + 16*i (lds_base must be the same for the whole wave).  Completion
 // is tracked by vmcnt, not by any register: wait with wait_vmem() before a
