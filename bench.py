@@ -16,8 +16,10 @@ The line also carries, measured in the same run:
     peak (MFMA bf16 2.5 PFLOP/s; HBM 8 TB/s), with the HBM traffic read from
     the committed rocprofv3 counter summary when it matches the sources;
   * "also_measured": the long causal prefill (1x32x16384x128), the split-KV
-    decode (64x32, L_b ~ U[1024, 8192], d=128) and the causal backward
-    (4x16x4096x64) at full size, each against its roofline (skip: --no-extra);
+    decode (64x32, L_b ~ U[1024, 8192], d=128), the paged decode with grouped
+    KV heads (64 sequences, 32 query / 8 KV heads, 16-token pages, the same
+    key lengths) and the causal backward (4x16x4096x64) at full size, each
+    against its roofline (skip: --no-extra);
   * "cpu_baseline": the float64 oracle on the host over a bounded sample of
     the same step (whole heads, about 10 s of CPU work).
 """
@@ -235,6 +237,47 @@ def bench_extra(fa, reps=20):
                              "ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1),
                              "frac_hbm": round(nbytes / ms / 1e-3 / PEAK_HBM, 4)}
     del q, k, v, o, lse, ws
+
+    # paged decode with grouped KV heads: B=64, Hq=32, Hkv=8, 16-token pages,
+    # d=128, the dense decode's key lengths; pages assigned in a seeded random order
+    import fa_inputs
+    w = fa_inputs.PAGED_WORKLOAD
+    B, Hq, Hkv, P, d = w.B, w.Hq, w.Hkv, w.page_size, w.d
+    seqlens = fa_inputs.decode_seqlens(B, w.lmin, w.lmax, w.seqlens_seed)
+    npb = (seqlens.astype("int64") + P - 1) // P
+    npages, maxp = int(npb.sum()), w.max_pages
+    perm = torch.randperm(npages, generator=torch.Generator().manual_seed(w.seed)).to(torch.int32)
+    table = torch.zeros(B, maxp, dtype=torch.int32)
+    nxt = 0
+    for b in range(B):
+        table[b, :npb[b]] = perm[nxt:nxt + npb[b]]
+        nxt += int(npb[b])
+    table = table.to(dev)
+    g.manual_seed(w.seed)
+    q = torch.randn(B, Hq, 1, d, device=dev, generator=g).to(torch.bfloat16)
+    kp = torch.empty(npages, Hkv, P, d, device=dev, dtype=torch.bfloat16)
+    vp = torch.empty_like(kp)
+    for i in range(0, npages, 4096):
+        n = min(4096, npages - i)
+        kp[i:i + n] = torch.randn(n, Hkv, P, d, device=dev, generator=g).to(torch.bfloat16)
+        vp[i:i + n] = torch.randn(n, Hkv, P, d, device=dev, generator=g).to(torch.bfloat16)
+    sl = torch.from_numpy(seqlens).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(B, Hq, device=dev)
+    ws = torch.empty(fa.decode_paged_workspace_bytes(B, Hq, Hkv, P, maxp, d), dtype=torch.uint8,
+                     device=dev)
+    ms = time_it(lambda: fa.decode_paged(q, kp, vp, table, sl, 1 / math.sqrt(d), 0, o, lse, ws),
+                 reps * 2)
+    if not bool(torch.isfinite(o.float()).all()):
+        raise RuntimeError("paged decode produced non-finite output")
+    nbytes = (float(seqlens.astype("int64").sum()) * Hkv * d * 2 * 2 + 2 * B * Hq * d * 2
+              + B * Hq * 4 + int(npb.sum()) * 4)
+    out["decode_paged_gqa"] = {"shape": {"B": B, "Hq": Hq, "Hkv": Hkv, "page_size": P, "d": d},
+                               "seqlens_sum": int(seqlens.sum()),
+                               "num_splits": fa.decode_paged_num_splits(B, Hq, Hkv, P, maxp, d),
+                               "ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1),
+                               "frac_hbm": round(nbytes / ms / 1e-3 / PEAK_HBM, 4)}
+    del q, kp, vp, o, lse, ws, table
 
     # backward: 4 x 16 x 4096 x 64, causal
     B, H, N, d = 4, 16, 4096, 64

@@ -224,27 +224,39 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     }
 }
 
-// One wave per (b, h): lane t owns head-dim entries t and t + 64.
+// One wave per (b, h): lane t owns head-dim entries t and t + 64 (d = 128) or
+// t (d = 64).  The split LSEs are read by the lanes in parallel (64 at a
+// time) and reduced across the wave; the partial outputs of all splits are
+// then loaded independently, so no load waits on another.
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(
     const float* __restrict__ ws_o, const float* __restrict__ ws_lse, int S, int BH,
     T* __restrict__ O, float* __restrict__ LSE) {
     const int bh = blockIdx.x, t = threadIdx.x;
     float M = neg_inf();
-    for (int s = 0; s < S; ++s) M = fmaxf(M, ws_lse[(size_t)s * BH + bh]);
+    for (int s0 = 0; s0 < S; s0 += 64)
+        if (s0 + t < S) M = fmaxf(M, ws_lse[(size_t)(s0 + t) * BH + bh]);
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
     constexpr int PL = D / 64;
     float acc[PL];
 #pragma unroll
     for (int i = 0; i < PL; ++i) acc[i] = 0.f;
     float sum = 0.f;
     if (M != neg_inf()) {
-        for (int s = 0; s < S; ++s) {
-            const float ls = ws_lse[(size_t)s * BH + bh];
-            if (ls == neg_inf()) continue;
-            const float w = __expf(ls - M);
-            sum += w;
+        for (int s0 = 0; s0 < S; s0 += 64) {
+            // lane t holds the weight of split s0 + t
+            const float ls = s0 + t < S ? ws_lse[(size_t)(s0 + t) * BH + bh] : neg_inf();
+            const float wt = ls == neg_inf() ? 0.f : __expf(ls - M);
+            const int n = min(64, S - s0);
+#pragma unroll 8
+            for (int j = 0; j < n; ++j) {
+                const float w = __shfl(wt, j, 64);
+                sum += w;
+                const float* src = ws_o + ((size_t)(s0 + j) * BH + bh) * D + t;
 #pragma unroll
-            for (int i = 0; i < PL; ++i) acc[i] += w * ws_o[((size_t)s * BH + bh) * D + t + 64 * i];
+                for (int i = 0; i < PL; ++i) acc[i] += w * src[64 * i];
+            }
         }
     }
     const float inv = sum > 0.f ? 1.f / sum : 0.f;
@@ -424,10 +436,11 @@ __global__ __launch_bounds__(256, FA_PAGED_MINB) void decode_paged_kernel(
 
     // Blocks of this wave: keys kb + 16 (wave + 4 i), i < nbw.  Two register
     // sets; the loads of block i + 1 are issued before block i is consumed,
-    // and block i + 2's descriptors (page id) are fetched meanwhile.  The
+    // and block i + 2's descriptor (page id) is fetched meanwhile.  The
     // loads are unconditional (past the last block they repeat it, from
     // cache) so that every wait the compiler places is exact, and a
     // scheduling barrier after each batch keeps them ahead of the MFMAs.
+    // (A third register set, two blocks in flight, measured no faster.)
     const int nblk = (ke - kb + kPagedBK - 1) / kPagedBK;
     const int nbw = nblk > wave ? (nblk - wave + 3) / 4 : 0;
     if (nbw > 0) {
