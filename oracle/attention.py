@@ -23,6 +23,12 @@ Readings where the pages are silent (each listed in the design notes):
   with as many queries as keys; decode sees every valid key of its sequence.
 * the saved statistic is LSE = m + ln(l), natural log, of the tau-scaled
   scores; it replaces the pair (m, l).
+* sliding window with sink tokens ("Atenção eficiente — FlashAttention, sparse
+  e híbrida", sections "Atenção híbrida: local + global intercalados" — local
+  layers attend to a window of w recent tokens — and "Attention sinks — o
+  paradoxo do primeiro token" — StreamingLLM keeps the first few tokens and
+  slides the window over the rest): on top of the causal mask, key j is
+  visible to query i iff i - j < window or j < sinks.
 * the gradients are derived by hand from O = softmax(tau Q K^T) V:
   dV = P^T dO, dP = dO V^T, D = rowsum(P o dP), dS = P o (dP - D),
   dQ = tau dS K, dK = tau dS^T Q.
@@ -38,17 +44,32 @@ import numpy as np
 __all__ = [
     "scores", "probs", "attention_fwd_head", "attention_fwd", "attention_bwd_head",
     "attention_bwd", "decode_fwd", "tiled_fwd_literal", "split_kv_decode",
-    "gather_pages", "decode_paged",
+    "gather_pages", "decode_paged", "visible",
 ]
 
 
-def scores(q_rows, k, tau, row_idx, causal):
-    """S[r, j] = tau * q_rows[r] . k[j], with -inf where key j > query row_idx[r]
-    under the causal mask ("o problema": S = Q K^T; "como funciona": the scale tau)."""
-    s = tau * (np.asarray(q_rows, dtype=np.float64) @ np.asarray(k, dtype=np.float64).T)
+def visible(row_idx, key_idx, causal, window=None, sinks=0):
+    """Boolean [rows, keys]: which keys each query row may attend to.
+
+    causal: key j <= query i.  window (causal only): additionally i - j < window
+    or j < sinks (a sliding window of the `window` most recent keys, the query's
+    own included, plus the first `sinks` keys)."""
+    i = np.asarray(row_idx)[:, None]
+    j = np.asarray(key_idx)[None, :]
+    vis = np.ones((i.shape[0], j.shape[1]), dtype=bool)
     if causal:
-        key_idx = np.arange(k.shape[0])
-        s = np.where(key_idx[None, :] > np.asarray(row_idx)[:, None], -np.inf, s)
+        vis &= j <= i
+    if window is not None:
+        vis &= ((i - j) < window) | (j < sinks)
+    return vis
+
+
+def scores(q_rows, k, tau, row_idx, causal, window=None, sinks=0):
+    """S[r, j] = tau * q_rows[r] . k[j], with -inf where key j is not visible to
+    query row_idx[r] ("o problema": S = Q K^T; "como funciona": the scale tau)."""
+    s = tau * (np.asarray(q_rows, dtype=np.float64) @ np.asarray(k, dtype=np.float64).T)
+    if causal or window is not None:
+        s = np.where(visible(row_idx, np.arange(k.shape[0]), causal, window, sinks), s, -np.inf)
     return s
 
 
@@ -62,7 +83,12 @@ def probs(s):
     return e / l[:, None], m, l
 
 
-def attention_fwd_head(q, k, v, tau, causal, rows=None, chunk=1024):
+def _check_window(causal, window, sinks):
+    if window is not None and (not causal or window < 1 or sinks < 0):
+        raise ValueError("a window needs the causal mask, window >= 1 and sinks >= 0")
+
+
+def attention_fwd_head(q, k, v, tau, causal, rows=None, chunk=1024, window=None, sinks=0):
     """Standard attention for one (batch, head): O[r] and LSE[r] for the requested rows.
 
     q: [Nq, d], k/v: [Nk, d].  The score rows are materialised whole, in chunks
@@ -74,31 +100,33 @@ def attention_fwd_head(q, k, v, tau, causal, rows=None, chunk=1024):
     v = np.asarray(v, dtype=np.float64)
     if causal and q.shape[0] != k.shape[0]:
         raise ValueError("causal attention needs as many queries as keys")
+    _check_window(causal, window, sinks)
     rows = np.arange(q.shape[0]) if rows is None else np.asarray(rows, dtype=np.int64)
     o = np.empty((len(rows), v.shape[1]))
     lse = np.empty(len(rows))
     for a in range(0, len(rows), chunk):
         r = rows[a:a + chunk]
         kmax = (int(r.max()) + 1) if causal else k.shape[0]
-        s = scores(q[r], k[:kmax], tau, r, causal)
+        s = scores(q[r], k[:kmax], tau, r, causal, window, sinks)
         p, m, l = probs(s)
         o[a:a + len(r)] = p @ v[:kmax]
         lse[a:a + len(r)] = m + np.log(l)
     return o, lse
 
 
-def attention_fwd(q, k, v, tau, causal):
+def attention_fwd(q, k, v, tau, causal, window=None, sinks=0):
     """Standard attention over [B, H, N, d] tensors: returns O [B,H,N,d], LSE [B,H,N]."""
     B, H, N, d = q.shape
     o = np.empty((B, H, N, v.shape[-1]))
     lse = np.empty((B, H, N))
     for b in range(B):
         for h in range(H):
-            o[b, h], lse[b, h] = attention_fwd_head(q[b, h], k[b, h], v[b, h], tau, causal)
+            o[b, h], lse[b, h] = attention_fwd_head(q[b, h], k[b, h], v[b, h], tau, causal,
+                                                    window=window, sinks=sinks)
     return o, lse
 
 
-def attention_bwd_head(q, k, v, do, tau, causal):
+def attention_bwd_head(q, k, v, do, tau, causal, window=None, sinks=0):
     """Hand-derived gradients of O = softmax(tau Q K^T [+mask]) V for one head.
 
     With the loss's gradient dO:
@@ -113,8 +141,9 @@ def attention_bwd_head(q, k, v, do, tau, causal):
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     do = np.asarray(do, dtype=np.float64)
+    _check_window(causal, window, sinks)
     n = q.shape[0]
-    s = scores(q, k, tau, np.arange(n), causal)
+    s = scores(q, k, tau, np.arange(n), causal, window, sinks)
     p, m, l = probs(s)
     o = p @ v
     dv = p.T @ do
@@ -127,14 +156,14 @@ def attention_bwd_head(q, k, v, do, tau, causal):
             "D": D, "D_from_o": (do * o).sum(axis=1)}
 
 
-def attention_bwd(q, k, v, do, tau, causal):
+def attention_bwd(q, k, v, do, tau, causal, window=None, sinks=0):
     """attention_bwd_head over [B, H, N, d]; returns dq, dk, dv, D as arrays."""
     B, H, N, d = q.shape
     out = {name: np.empty((B, H, N, d)) for name in ("dq", "dk", "dv")}
     out["D"] = np.empty((B, H, N))
     for b in range(B):
         for h in range(H):
-            g = attention_bwd_head(q[b, h], k[b, h], v[b, h], do[b, h], tau, causal)
+            g = attention_bwd_head(q[b, h], k[b, h], v[b, h], do[b, h], tau, causal, window, sinks)
             for name in ("dq", "dk", "dv", "D"):
                 out[name][b, h] = g[name]
     return out
@@ -161,7 +190,7 @@ def decode_fwd(q, k, v, seqlens, tau, heads=None, batches=None):
     return o, lse
 
 
-def tiled_fwd_literal(q, k, v, tau, causal, Br, Bc):
+def tiled_fwd_literal(q, k, v, tau, causal, Br, Bc, window=None, sinks=0):
     """Self-check of the tiled recurrence, in the page's own loop order.
 
     Follows "como funciona" of the "flash-attention" encyclopedia page: the outer
@@ -171,8 +200,9 @@ def tiled_fwd_literal(q, k, v, tau, causal, Br, Bc):
     m_new = max(m_i, m~), l_new = e^(m_i - m_new) l_i + e^(m~ - m_new) rowsum(P~),
     and O_i = (l_i e^(m_i - m_new) O_i + e^(m~ - m_new) P~ V_j) / l_new.
 
-    Under the causal mask a block row can be fully masked (m~ = -inf); it then
-    contributes no term and that row's statistics are left as they were.
+    Under the causal mask (and a sliding window) a block row can be fully masked
+    (m~ = -inf); it then contributes no term and that row's statistics are left
+    as they were.
     Returns O [N,d] and LSE = m + ln(l) [N] for one head.
     """
     q = np.asarray(q, dtype=np.float64)
@@ -188,9 +218,9 @@ def tiled_fwd_literal(q, k, v, tau, causal, Br, Bc):
             rows = np.arange(i0, min(i0 + Br, nq))
             Qi, Oi, li, mi = q[rows], O[rows].copy(), l[rows].copy(), m[rows].copy()
             Sij = tau * (Qi @ Kj.T)
-            if causal:
+            if causal or window is not None:
                 keys = np.arange(j0, j0 + Kj.shape[0])
-                Sij = np.where(keys[None, :] > rows[:, None], -np.inf, Sij)
+                Sij = np.where(visible(rows, keys, causal, window, sinks), Sij, -np.inf)
             m_til = Sij.max(axis=1)
             live = np.isfinite(m_til)
             if not live.any():

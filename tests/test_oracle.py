@@ -370,3 +370,90 @@ def test_paged_inputs_poison_unused_rows():
     assert np.all(np.isfinite(kp[t[0, 0]])) and np.all(np.isfinite(kp[t[0, 1], :, :4]))
     assert np.all(np.isnan(kp[t[0, 1], :, 4:]))
     assert sorted(t[0, :2].tolist() + t[1, :1].tolist()) == [0, 1, 2]
+
+
+# --- sliding window with sink tokens ---------------------------------------
+
+def _qkv(n, d, seed):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((n, d)), rng.standard_normal((n, d)), rng.standard_normal((n, d))
+
+
+def test_window_covering_everything_is_causal():
+    q, k, v = _qkv(40, 8, 501)
+    o1, l1 = orc.attention_fwd_head(q, k, v, 0.3, True)
+    for w, s in ((40, 0), (1000, 0), (1, 40), (5, 64)):
+        o2, l2 = orc.attention_fwd_head(q, k, v, 0.3, True, window=w, sinks=s)
+        np.testing.assert_array_equal(o1, o2)
+        np.testing.assert_array_equal(l1, l2)
+
+
+def test_window_one_sees_only_itself():
+    """window = 1, no sinks: every query attends to its own key only, so
+    O_i = V_i and LSE_i = tau q_i . k_i."""
+    q, k, v = _qkv(17, 6, 502)
+    o, l = orc.attention_fwd_head(q, k, v, 0.7, True, window=1)
+    np.testing.assert_allclose(o, v, atol=1e-15)
+    np.testing.assert_allclose(l, 0.7 * np.einsum("id,id->i", q, k), atol=1e-13)
+
+
+@pytest.mark.parametrize("w,s", [(1, 1), (3, 0), (3, 2), (7, 4), (20, 3)])
+def test_window_uniform_weights_closed_form(w, s):
+    """Q = 0: uniform weights over the visible set {max(0, i-w+1) .. i} plus
+    the sinks {0 .. min(s, i+1)-1} below it; O_i is that set's mean of V and
+    LSE_i = ln |set|, |set| = min(i+1, w) + max(0, min(s, i-w+1))."""
+    n, d = 30, 5
+    _, k, v = _qkv(n, d, 503)
+    q = np.zeros((n, d))
+    o, l = orc.attention_fwd_head(q, k, v, 0.5, True, window=w, sinks=s)
+    for i in range(n):
+        lo = max(0, i - w + 1)
+        rows = list(range(lo, i + 1)) + list(range(0, min(s, lo)))
+        assert len(rows) == min(i + 1, w) + max(0, min(s, i - w + 1))
+        np.testing.assert_allclose(o[i], v[rows].mean(axis=0), atol=1e-14)
+        np.testing.assert_allclose(l[i], np.log(len(rows)), atol=1e-14)
+
+
+@pytest.mark.parametrize("Br,Bc", [(16, 16), (7, 13), (13, 7), (64, 5)])
+@pytest.mark.parametrize("w,s", [(1, 0), (9, 0), (9, 3), (50, 4)])
+def test_tiled_recurrence_with_window(Br, Bc, w, s):
+    """The tiled recurrence with the window mask (whole block rows masked
+    before and after the window) equals the direct computation."""
+    q, k, v = _qkv(70, 8, 504)
+    o1, l1 = orc.attention_fwd_head(q, k, v, 0.4, True, window=w, sinks=s)
+    o2, l2 = orc.tiled_fwd_literal(q, k, v, 0.4, True, Br, Bc, window=w, sinks=s)
+    np.testing.assert_allclose(o2, o1, atol=1e-12)
+    np.testing.assert_allclose(l2, l1, atol=1e-12)
+
+
+@pytest.mark.parametrize("w,s", [(1, 0), (3, 0), (3, 2), (6, 1)])
+def test_window_gradients_finite_differences(w, s):
+    n, d, tau = 9, 4, 0.6
+    q, k, v = _qkv(n, d, 505)
+    do = np.random.default_rng(506).standard_normal((n, d))
+    g = orc.attention_bwd_head(q, k, v, do, tau, True, window=w, sinks=s)
+    f = lambda qq, kk, vv: float((orc.attention_fwd_head(qq, kk, vv, tau, True, window=w,
+                                                         sinks=s)[0] * do).sum())
+    h = 1e-6
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            args_p = [xp if x is a else a for a in (q, k, v)]
+            args_m = [xm if x is a else a for a in (q, k, v)]
+            num[idx] = (f(*args_p) - f(*args_m)) / (2 * h)
+        np.testing.assert_allclose(g[name], num, rtol=1e-6, atol=1e-8)
+    # the identities hold under any mask that keeps every row non-empty
+    np.testing.assert_allclose(g["D"], g["D_from_o"], atol=1e-12)
+    np.testing.assert_allclose(g["dk"].sum(axis=0), 0, atol=1e-12)
+    np.testing.assert_allclose(g["dv"].sum(axis=0), do.sum(axis=0), atol=1e-12)
+
+
+def test_window_needs_causal():
+    q, k, v = _qkv(4, 2, 507)
+    with pytest.raises(ValueError):
+        orc.attention_fwd_head(q, k, v, 1.0, False, window=2)
+    with pytest.raises(ValueError):
+        orc.attention_fwd_head(q, k, v, 1.0, True, window=0)
