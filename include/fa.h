@@ -79,6 +79,25 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
            int B, int H, int N, int d, float tau, int causal, int dtype, void* stream);
 
 /*
+ * fa_fwd_window - fa_fwd under the causal mask restricted to a sliding window
+ * with sink tokens.
+ *
+ * Local layers of hybrid attention attend to a window of recent tokens only
+ * ("Atenção eficiente — FlashAttention, sparse e híbrida", section "Atenção
+ * híbrida: local + global intercalados"), and StreamingLLM keeps the first
+ * few tokens visible besides the window (same page, "Attention sinks — o
+ * paradoxo do primeiro token").  Key j is visible to query i iff j <= i and
+ * (i - j < window or j < sinks).  Tiles outside every row's window are never
+ * visited.  window >= N with sinks = 0 is exactly fa_fwd with causal = 1.
+ *
+ * window : >= 1 (the query's own key always counts); sinks: >= 0 (FA_ERR_ARG
+ *          otherwise).  Other arguments as fa_fwd; LSE is over the visible keys.
+ */
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int N, int d, float tau, int window, int sinks,
+                  int dtype, void* stream);
+
+/*
  * fa_decode_workspace_bytes - workspace that fa_decode needs.
  *
  * num_splits = 0 asks for the size of the split count that fa_decode chooses

@@ -31,6 +31,7 @@ STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTE
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
 SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
+    "fa_fwd_window": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "fa_decode_num_splits": (_I, [_I, _I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _I, _P, _Z, _I, _P]),
@@ -95,8 +96,11 @@ def _need(t, name):
         raise ValueError("%s must be contiguous" % name)
 
 
-def fwd(q, k, v, tau=None, causal=False, o=None, lse=None):
-    """O = softmax(tau Q K^T [+causal mask]) V and LSE, via fa_fwd."""
+def fwd(q, k, v, tau=None, causal=False, o=None, lse=None, window=None, sinks=0):
+    """O = softmax(tau Q K^T [+causal mask]) V and LSE, via fa_fwd.
+
+    With window (causal only): the causal mask restricted to the `window` most
+    recent keys plus the first `sinks` keys, via fa_fwd_window."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n)
@@ -104,6 +108,14 @@ def fwd(q, k, v, tau=None, causal=False, o=None, lse=None):
     tau = 1.0 / math.sqrt(d) if tau is None else float(tau)
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    if window is not None:
+        if not causal:
+            raise ValueError("a sliding window applies to the causal mask")
+        st = lib().fa_fwd_window(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                 lse.data_ptr(), B, H, N, d, tau, int(window), int(sinks),
+                                 _dtype_code(q), _stream(q))
+        check("fa_fwd_window", st)
+        return o, lse
     st = lib().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
                       B, H, N, d, tau, int(bool(causal)), _dtype_code(q), _stream(q))
     check("fa_fwd", st)

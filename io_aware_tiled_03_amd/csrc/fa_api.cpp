@@ -52,6 +52,24 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int
     return after_launch();
 }
 
+int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                  int N, int d, float tau, int window, int sinks, int dtype, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    int st = check_common(B, H, N, d, tau, dtype);
+    if (st != FA_OK) return st;
+    if (window < 1 || sinks < 0) return FA_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
+        return FA_ERR_ALIGN;
+    const long long bh = (long long)B * H;
+    if (!grid_ok(bh * ((N + 63) / 64), 256)) return FA_ERR_SHAPE;
+    fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, tau, 1, dtype};
+    a.window = window < N ? window : N;   // a window of N or more keys is the causal mask
+    a.sinks = sinks < N ? sinks : N;
+    (void)hipGetLastError();
+    fa::launch_fwd(a, (hipStream_t)stream);
+    return after_launch();
+}
+
 int fa_decode_num_splits(int B, int H, int N_max, int d, int num_splits) {
     if (B < 1 || H < 1 || N_max < 1 || N_max > (1 << 20) || (d != 64 && d != 128)) return 0;
     if (num_splits < 0 || num_splits > 1024) return 0;

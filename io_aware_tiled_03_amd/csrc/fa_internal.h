@@ -16,6 +16,8 @@ struct FwdArgs {
     int B, H, N, d;
     float tau;
     int causal, dtype;
+    int window = 0x40000000;   // causal only: key j visible to query i iff j <= i and
+    int sinks = 0;             // (i - j < window or j < sinks); the defaults give plain causal
 };
 void launch_fwd(const FwdArgs& a, hipStream_t st);
 

@@ -68,6 +68,22 @@ def test_fwd_rejects_bad_arguments():
     assert _fwd(lib, lse=P + 2) == 6
 
 
+def test_fwd_window_rejects_bad_arguments():
+    fa, lib = _lib()
+    args = dict(q=P, k=P, v=P, o=P, lse=P, B=1, H=1, N=16, d=64, tau=0.125, w=4, s=0, dtype=1)
+    def call(**kw):
+        a = dict(args); a.update(kw)
+        return lib.fa_fwd_window(a["q"], a["k"], a["v"], a["o"], a["lse"], a["B"], a["H"], a["N"],
+                                 a["d"], a["tau"], a["w"], a["s"], a["dtype"], None)
+    assert call(v=None) == 1
+    assert call(N=0) == 2
+    assert call(d=32) == 3
+    assert call(w=0) == 7
+    assert call(s=-1) == 7
+    assert call(tau=-0.5) == 7
+    assert call(o=P + 4) == 6
+
+
 def _dec(lib, **kw):
     a = dict(q=P, k=P, v=P, sl=P, B=2, H=2, N=100, d=128, tau=0.1, o=P, lse=P, ns=0, ws=P,
              wsb=1 << 30, dtype=1)
