@@ -53,7 +53,8 @@ typedef enum {
     FA_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required        */
     FA_ERR_HIP = 5,          /* the HIP runtime reported a launch error        */
     FA_ERR_ALIGN = 6,        /* a pointer is not 16-byte aligned               */
-    FA_ERR_ARG = 7           /* tau not finite and positive, or bad split count */
+    FA_ERR_ARG = 7           /* a value out of range: tau, split count, window,
+                                sinks or stage                                  */
 } fa_status;
 
 typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
@@ -215,6 +216,19 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            const void* dout, void* dq, void* dk, void* dv,
            int B, int H, int N, int d, float tau, int causal,
            void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * fa_bwd_window - backward of fa_fwd_window (causal mask with a sliding
+ * window of `window` keys and `sinks` sink keys; same visibility rule).
+ * Query tiles no key of a tile can reach, and key tiles outside every row's
+ * window, are skipped.  Arguments as fa_bwd without `causal`, plus window >= 1
+ * and sinks >= 0 (FA_ERR_ARG otherwise); o and lse must come from
+ * fa_fwd_window with the same window and sinks.
+ */
+int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  const void* dout, void* dq, void* dk, void* dv,
+                  int B, int H, int N, int d, float tau, int window, int sinks,
+                  void* workspace, size_t workspace_bytes, int dtype, void* stream);
 
 /*
  * fa_bwd_stage - enqueue one of fa_bwd's three kernels.

@@ -43,6 +43,8 @@ SIGNATURES = {
     "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _Z, _I, _P]),
     "fa_bwd_stage": (_I, [_I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _Z,
                           _I, _P]),
+    "fa_bwd_window": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _Z,
+                           _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
 }
 
@@ -197,10 +199,11 @@ def bwd_workspace_bytes(B, H, N):
 
 
 def bwd(q, k, v, o, lse, do, tau=None, causal=False, dq=None, dk=None, dv=None, workspace=None,
-        stage=None):
+        stage=None, window=None, sinks=0):
     """dQ, dK, dV of fa_fwd's output given dO, via fa_bwd (workspace holds D on return).
 
-    With stage in (0, 1, 2) only that kernel is enqueued, via fa_bwd_stage."""
+    With stage in (0, 1, 2) only that kernel is enqueued, via fa_bwd_stage.  With
+    window (causal only): the backward of the sliding-window forward, via fa_bwd_window."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (do, "do")):
         _need(t, n)
@@ -216,7 +219,12 @@ def bwd(q, k, v, o, lse, do, tau=None, causal=False, dq=None, dk=None, dv=None, 
             do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, tau,
             int(bool(causal)), workspace.data_ptr(),
             workspace.numel() * workspace.element_size(), _dtype_code(q), _stream(q))
-    if stage is None:
+    if window is not None:
+        if not causal or stage is not None:
+            raise ValueError("a sliding window applies to the causal mask, whole backward only")
+        wargs = args[:14] + (int(window), int(sinks)) + args[15:]
+        check("fa_bwd_window", lib().fa_bwd_window(*wargs))
+    elif stage is None:
         check("fa_bwd", lib().fa_bwd(*args))
     else:
         check("fa_bwd_stage", lib().fa_bwd_stage(int(stage), *args))

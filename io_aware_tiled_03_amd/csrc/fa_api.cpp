@@ -173,7 +173,7 @@ namespace {
 int bwd_common(int stages, const void* q, const void* k, const void* v, const void* o,
                const float* lse, const void* dout, void* dq, void* dk, void* dv, int B, int H,
                int N, int d, float tau, int causal, void* workspace, size_t workspace_bytes,
-               int dtype, void* stream) {
+               int dtype, void* stream, int window = 0, int sinks = 0) {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
     int st = check_common(B, H, N, d, tau, dtype);
     if (st != FA_OK) return st;
@@ -187,6 +187,10 @@ int bwd_common(int stages, const void* q, const void* k, const void* v, const vo
     if (!grid_ok((long long)B * H * ((N + 63) / 64), 256)) return FA_ERR_SHAPE;
     fa::BwdArgs a{q, k, v, o, lse, dout, dq, dk, dv, (float*)workspace, B, H, N, d, tau, causal,
                   dtype};
+    if (window > 0) {   // causal with a sliding window (a window of N or more is the causal mask)
+        a.window = window < N ? window : N;
+        a.sinks = sinks < N ? sinks : N;
+    }
     (void)hipGetLastError();
     fa::launch_bwd(a, stages, (hipStream_t)stream);
     return after_launch();
@@ -199,6 +203,15 @@ int fa_bwd(const void* q, const void* k, const void* v, const void* o, const flo
            int causal, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
     return bwd_common(7, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, tau, causal, workspace,
                       workspace_bytes, dtype, stream);
+}
+
+int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                  const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                  float tau, int window, int sinks, void* workspace, size_t workspace_bytes,
+                  int dtype, void* stream) {
+    if (window < 1 || sinks < 0) return FA_ERR_ARG;
+    return bwd_common(7, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, tau, 1, workspace,
+                      workspace_bytes, dtype, stream, window, sinks);
 }
 
 int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
@@ -219,7 +232,9 @@ const char* fa_status_string(int status) {
         case FA_ERR_WORKSPACE: return "workspace missing or too small";
         case FA_ERR_HIP: return "HIP launch error";
         case FA_ERR_ALIGN: return "a pointer is not aligned (16 bytes for tensors)";
-        case FA_ERR_ARG: return "tau must be finite and positive; num_splits in 0..1024";
+        case FA_ERR_ARG:
+            return "bad argument value (tau finite and > 0, num_splits 0..1024, window >= 1, "
+                   "sinks >= 0, stage 0..2)";
         default: return "unknown status";
     }
 }

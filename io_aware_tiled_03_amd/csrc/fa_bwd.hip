@@ -87,12 +87,17 @@ struct TileCopy {
     }
 };
 
-template <int D, bool CAUSAL>
+// Mask modes: none, causal, causal with a sliding window and sink tokens
+// (key j visible to query i iff j <= i and (i - j < window or j < sinks)).
+enum : int { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2 };
+
+template <int D, int MODE>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int N, float scale_log2,
-    float tau) {
+    float tau, int window, int sinks) {
+    constexpr bool CAUSAL = MODE != kMaskNone, WIN = MODE == kMaskWindow;
     constexpr int BC = 128, BR = 64;
     constexpr int STR = D + 8;                 // padded row (16 * odd bytes)
     // Double buffers as distinct LDS variables picked at compile time, so that
@@ -166,6 +171,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         for (int qb = 0; qb < 2; ++qb) {
             const int qs = q0 + qb * 32;
             if (MASK && CAUSAL && qs + 31 < kw) continue;   // all these queries precede the keys
+            if (MASK && WIN && qs - (kw + 31) >= window && kw >= sinks) continue;   // all past the window
             u32x4 qa[D / 16], oa[D / 16];
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks) {
@@ -191,7 +197,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                 float p = fast_exp2(__builtin_fmaf(sacc[r], scale_log2, -lq[r >> 2][r & 3]));
                 if constexpr (MASK) {
                     const int q = qs + 16 * (r >> 3) + 8 * hf + (r & 7);
-                    if (CAUSAL && key > q) p = 0.f;
+                    if (CAUSAL && (key > q || (WIN && q - key >= window && key >= sinks))) p = 0.f;
                 }
                 sacc[r] = p;
                 dp[r] = p * (dp[r] - dq4[r >> 2][r & 3]);
@@ -228,12 +234,22 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     }
     // query tiles that reach into this workgroup's keys need the causal mask
     const int qmask_end = CAUSAL ? min(n_qt, (k0 + BC + BR - 1) / BR) : qt0;
+    // Under a window: no query past the last key's window sees the tile
+    // unless it holds sink keys (qt_end), and query tiles from qwin on have a
+    // query beyond some key's window (masked).
+    int qt_end = n_qt, qwin = n_qt;
+    if constexpr (WIN) {
+        if (k0 >= sinks) qt_end = min(n_qt, (k0 + BC - 1 + window - 1) / BR + 1);
+        qwin = max(0, (k0 + window - BR + 1 + BR - 1) / BR);
+    }
+    const int qu_end = max(qmask_end, min(qwin, qt_end));   // end of the unmasked query tiles
     auto tile_b = [&](int qt, auto bufc, auto maskc) __attribute__((always_inline)) {   // query tile qt lives in buffer bufc
         constexpr ic<1 - decltype(bufc)::value> other{};
-        if (qt + 1 < n_qt) stage(qt + 1, other);
+        if (qt + 1 < qt_end) stage(qt + 1, other);
         const int q0 = qt * BR;
-        if (!(CAUSAL && q0 + BR - 1 < kw)) compute(bufc, q0, maskc);
-        if (qt + 1 < n_qt) stage_ld(other);
+        if (!(CAUSAL && q0 + BR - 1 < kw) && !(WIN && q0 - (kw + 31) >= window && kw >= sinks))
+            compute(bufc, q0, maskc);
+        if (qt + 1 < qt_end) stage_ld(other);
         wait_vmem();
         __syncthreads();
     };
@@ -249,7 +265,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         if (qt < te) tile_b(qt, ic<0>{}, maskc);
     };
     phase(qt0, qmask_end, ic<1>{});
-    phase(max(qt0, qmask_end), n_qt, ic<0>{});
+    phase(max(qt0, qmask_end), qu_end, ic<0>{});
+    phase(max(qt0, qu_end), qt_end, ic<1>{});
 
     if (key < N) {
         uint16_t* dkr = dK + base + (size_t)key * D;
@@ -270,11 +287,13 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     }
 }
 
-template <int D, bool CAUSAL>
+template <int D, int MODE>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
-    uint16_t* __restrict__ dQ, int BH, int N, float scale_log2, float tau, int n_qtiles) {
+    uint16_t* __restrict__ dQ, int BH, int N, float scale_log2, float tau, int n_qtiles, int window,
+    int sinks) {
+    constexpr bool CAUSAL = MODE != kMaskNone, WIN = MODE == kMaskWindow;
     constexpr int BR = 128, BC = 64;
     constexpr int STR = D + 8;
     __shared__ __attribute__((aligned(16))) uint16_t sK0[BC * STR], sK1[BC * STR];
@@ -340,7 +359,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
                 float p = fast_exp2(__builtin_fmaf(sacc[r], scale_log2, -lse2));
                 if constexpr (MASK) {
                     const int kk = k0 + kb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7);
-                    if (CAUSAL && kk > qrow) p = 0.f;
+                    if (CAUSAL && (kk > qrow || (WIN && qrow - kk >= window && kk >= sinks))) p = 0.f;
                 }
                 sacc[r] = p * (dp[r] - Dq);
             }
@@ -361,39 +380,59 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         }
     };
 
-    cp.issue(krs, 0, sK0, wave);
-    cp.issue(vrs, 0, sV0, wave);
+    // Key tiles in a sequence of positions p (as in the forward): under a
+    // window first the nsk tiles of sink keys below the window, then tiles
+    // tlo .. ntiles-1; masked, unmasked, masked phases.  Position p lives in
+    // buffer p % 2.
+    int nsk = 0, tlo = 0, tfull = 0;
+    if constexpr (WIN) {
+        const int q1 = min(q0 + BR, N) - 1;
+        const int lo_min = q0 - window + 1, lo_max = q1 - window + 1;
+        tlo = max(lo_min, 0) / BC;
+        tfull = max(tlo, (max(lo_max, 0) + BC - 1) / BC);
+        nsk = min((sinks + BC - 1) / BC, tlo);
+    }
+    auto tile_at = [&](int p) { return p < nsk ? p : tlo + (p - nsk); };
+    // tiles in [tfull, tdiag) precede every query of the workgroup and lie
+    // inside every row's window: no mask
+    const int jsplit = CAUSAL ? min(ntiles, q0 / BC) : ntiles;
+    const int tdiag = max(tfull, jsplit);
+    const int p1 = nsk + (tfull - tlo), p2 = nsk + (tdiag - tlo), p3 = nsk + (ntiles - tlo);
+    cp.issue(krs, tile_at(0) * BC, sK0, wave);
+    cp.issue(vrs, tile_at(0) * BC, sV0, wave);
     wait_vmem();
     __syncthreads();
-    // tiles before jsplit precede every query of the workgroup: no mask
-    const int jsplit = CAUSAL ? min(ntiles, q0 / BC) : ntiles;
-    auto tile_b = [&](int j, auto bufc, auto maskc) __attribute__((always_inline)) {   // key tile j lives in buffer bufc
+    auto tile_b = [&](int p, auto bufc, auto maskc) __attribute__((always_inline)) {   // position p lives in buffer bufc
         constexpr bool B1 = decltype(bufc)::value != 0;
-        if (j + 1 < ntiles) {
-            cp.issue(krs, (j + 1) * BC, B1 ? sK0 : sK1, wave);
-            cp.issue(vrs, (j + 1) * BC, B1 ? sV0 : sV1, wave);
+        if (p + 1 < p3) {
+            const int k1 = tile_at(p + 1) * BC;
+            cp.issue(krs, k1, B1 ? sK0 : sK1, wave);
+            cp.issue(vrs, k1, B1 ? sV0 : sV1, wave);
         }
-        const int k0 = j * BC;
+        const int k0 = tile_at(p) * BC;
         if constexpr (decltype(maskc)::value != 0) {
-            if (!(CAUSAL && k0 > qw + 31)) compute(bufc, k0, maskc);
+            const bool sees = !(CAUSAL && k0 > qw + 31) &&
+                              !(WIN && k0 + BC - 1 < qw - window + 1 && k0 >= sinks);
+            if (sees) compute(bufc, k0, maskc);
         } else {
             compute(bufc, k0, maskc);
         }
         wait_vmem();
         __syncthreads();
     };
-    // Key tiles [jb, je), tile j in buffer j % 2 (buffers fixed at compile time).
-    auto phase = [&](int jb, int je, auto maskc) __attribute__((always_inline)) {
-        int j = jb;
-        if (j < je && (j & 1)) { tile_b(j, ic<1>{}, maskc); ++j; }
-        for (; j + 1 < je; j += 2) {
-            tile_b(j, ic<0>{}, maskc);
-            tile_b(j + 1, ic<1>{}, maskc);
+    // Positions [pb, pe), position p in buffer p % 2 (buffers fixed at compile time).
+    auto phase = [&](int pb, int pe, auto maskc) __attribute__((always_inline)) {
+        int p = pb;
+        if (p < pe && (p & 1)) { tile_b(p, ic<1>{}, maskc); ++p; }
+        for (; p + 1 < pe; p += 2) {
+            tile_b(p, ic<0>{}, maskc);
+            tile_b(p + 1, ic<1>{}, maskc);
         }
-        if (j < je) tile_b(j, ic<0>{}, maskc);
+        if (p < pe) tile_b(p, ic<0>{}, maskc);
     };
-    phase(0, jsplit, ic<0>{});
-    phase(jsplit, ntiles, ic<1>{});
+    phase(0, p1, ic<1>{});
+    phase(p1, p2, ic<0>{});
+    phase(p2, p3, ic<1>{});
 
     if (qrow < N) {
         uint16_t* dqr = dQ + base + (size_t)qrow * D;
@@ -410,7 +449,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     }
 }
 
-template <int D, bool C>
+template <int D, int MODE>
 void launch(const BwdArgs& a, int stages, hipStream_t st) {
     const int bh = a.B * a.H;
     if (stages & 1) {
@@ -421,25 +460,31 @@ void launch(const BwdArgs& a, int stages, hipStream_t st) {
     }
     if (stages & 2) {
         const int nk = (a.N + 127) / 128;
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, C>), dim3(nk * bh), dim3(256), 0, st,
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, MODE>), dim3(nk * bh), dim3(256), 0, st,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                            (const uint16_t*)a.dout, a.lse, a.D, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                           bh, a.N, a.tau * kLog2e, a.tau);
+                           bh, a.N, a.tau * kLog2e, a.tau, a.window, a.sinks);
     }
     if (stages & 4) {
         const int nq = (a.N + 127) / 128;
-        hipLaunchKernelGGL((bwd_dq_kernel<D, C>), dim3(nq * bh), dim3(256), 0, st,
+        hipLaunchKernelGGL((bwd_dq_kernel<D, MODE>), dim3(nq * bh), dim3(256), 0, st,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                            (const uint16_t*)a.dout, a.lse, a.D, (uint16_t*)a.dq, bh, a.N,
-                           a.tau * kLog2e, a.tau, nq);
+                           a.tau * kLog2e, a.tau, nq, a.window, a.sinks);
     }
+}
+
+template <int D>
+void launch_d(const BwdArgs& a, int stages, hipStream_t st) {
+    if (!a.causal) launch<D, kMaskNone>(a, stages, st);
+    else if (a.window < a.N || a.sinks > 0) launch<D, kMaskWindow>(a, stages, st);
+    else launch<D, kMaskCausal>(a, stages, st);
 }
 
 }  // namespace
 
 void launch_bwd(const BwdArgs& a, int stages, hipStream_t st) {
-    if (a.d == 64) a.causal ? launch<64, true>(a, stages, st) : launch<64, false>(a, stages, st);
-    else a.causal ? launch<128, true>(a, stages, st) : launch<128, false>(a, stages, st);
+    a.d == 64 ? launch_d<64>(a, stages, st) : launch_d<128>(a, stages, st);
 }
 
 }  // namespace fa

@@ -65,6 +65,8 @@ struct BwdArgs {
     int B, H, N, d;
     float tau;
     int causal, dtype;
+    int window = 0x40000000;   // as in FwdArgs
+    int sinks = 0;
 };
 // stages: bit 0 = D preprocess, bit 1 = dK/dV, bit 2 = dQ (launched in that order)
 void launch_bwd(const BwdArgs& a, int stages, hipStream_t st);

@@ -44,7 +44,7 @@ import numpy as np
 __all__ = [
     "scores", "probs", "attention_fwd_head", "attention_fwd", "attention_bwd_head",
     "attention_bwd", "decode_fwd", "tiled_fwd_literal", "split_kv_decode",
-    "gather_pages", "decode_paged", "visible",
+    "gather_pages", "decode_paged", "visible", "round_to_bf16",
 ]
 
 
@@ -126,7 +126,17 @@ def attention_fwd(q, k, v, tau, causal, window=None, sinks=0):
     return o, lse
 
 
-def attention_bwd_head(q, k, v, do, tau, causal, window=None, sinks=0):
+def round_to_bf16(x):
+    """Nearest bfloat16 value of each entry, as float64: round to float32
+    first (the kernels hold O in fp32), then to 8 significant bits, ties to even."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
+    u = f.view(np.uint32)
+    r = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
+         & np.uint32(0xFFFF0000)).astype(np.uint32)
+    return r.view(np.float32).astype(np.float64)
+
+
+def attention_bwd_head(q, k, v, do, tau, causal, window=None, sinks=0, d_from_saved_bf16=False):
     """Hand-derived gradients of O = softmax(tau Q K^T [+mask]) V for one head.
 
     With the loss's gradient dO:
@@ -135,7 +145,11 @@ def attention_bwd_head(q, k, v, do, tau, causal, window=None, sinks=0):
       dQ = tau dS K;  dK = tau dS^T Q.
     The identity D_i = dO_i . O_i ("como funciona", backward paragraph) is
     returned as a second form of D for the tests to compare.
-    Returns dict(dq, dk, dv, o, lse, D, D_from_o).
+    d_from_saved_bf16: take D_i = dO_i . bf16(O_i) in dS instead, i.e. the
+    identity applied to the output the forward saved when O is stored in
+    bfloat16 (the page's backward keeps only the saved O).  The returned "D"
+    is then that value.
+    Returns dict(dq, dk, dv, o, lse, D, D_from_o, p, ds).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -149,21 +163,24 @@ def attention_bwd_head(q, k, v, do, tau, causal, window=None, sinks=0):
     dv = p.T @ do
     dp = do @ v.T
     D = (p * dp).sum(axis=1)
+    if d_from_saved_bf16:
+        D = (do * round_to_bf16(o)).sum(axis=1)
     ds = p * (dp - D[:, None])
     dq = tau * (ds @ k)
     dk = tau * (ds.T @ q)
     return {"dq": dq, "dk": dk, "dv": dv, "o": o, "lse": m + np.log(l),
-            "D": D, "D_from_o": (do * o).sum(axis=1)}
+            "D": D, "D_from_o": (do * o).sum(axis=1), "p": p, "ds": ds}
 
 
-def attention_bwd(q, k, v, do, tau, causal, window=None, sinks=0):
+def attention_bwd(q, k, v, do, tau, causal, window=None, sinks=0, d_from_saved_bf16=False):
     """attention_bwd_head over [B, H, N, d]; returns dq, dk, dv, D as arrays."""
     B, H, N, d = q.shape
     out = {name: np.empty((B, H, N, d)) for name in ("dq", "dk", "dv")}
     out["D"] = np.empty((B, H, N))
     for b in range(B):
         for h in range(H):
-            g = attention_bwd_head(q[b, h], k[b, h], v[b, h], do[b, h], tau, causal, window, sinks)
+            g = attention_bwd_head(q[b, h], k[b, h], v[b, h], do[b, h], tau, causal, window, sinks,
+                                   d_from_saved_bf16)
             for name in ("dq", "dk", "dv", "D"):
                 out[name][b, h] = g[name]
     return out

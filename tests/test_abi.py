@@ -187,6 +187,20 @@ def test_bwd_rejects_bad_arguments():
     assert lib.fa_bwd_workspace_bytes(1, 2, 64) == 512
 
 
+def test_bwd_window_rejects_bad_arguments():
+    fa, lib = _lib()
+    # every call below fails a host-side check, so nothing is launched on the fake pointers
+    args = [P, P, P, P, P, P, P, P, P, 1, 2, 64, 64, 0.125, 16, 0, P, 1 << 20, 1, None]
+    bad = list(args); bad[14] = 0
+    assert lib.fa_bwd_window(*bad) == 7
+    bad = list(args); bad[15] = -2
+    assert lib.fa_bwd_window(*bad) == 7
+    bad = list(args); bad[18] = 0
+    assert lib.fa_bwd_window(*bad) == 3    # bf16 only
+    bad = list(args); bad[16] = None
+    assert lib.fa_bwd_window(*bad) == 4
+
+
 def test_bwd_stage_rejects_bad_arguments():
     fa, lib = _lib()
     args = (P, P, P, P, P, P, P, P, P, 1, 2, 64, 64, 0.125, 1, P, 1 << 20, 1, None)

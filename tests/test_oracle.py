@@ -457,3 +457,38 @@ def test_window_needs_causal():
         orc.attention_fwd_head(q, k, v, 1.0, False, window=2)
     with pytest.raises(ValueError):
         orc.attention_fwd_head(q, k, v, 1.0, True, window=0)
+
+
+# --- D from the saved bfloat16 output ---------------------------------------
+
+def test_round_to_bf16_matches_torch():
+    """The oracle's rounding equals torch's float32 -> bfloat16 conversion
+    (round to nearest even), ties and subnormal-free range included."""
+    import torch
+    rng = np.random.default_rng(601)
+    x = np.concatenate([rng.standard_normal(5000) * 10.0 ** rng.integers(-6, 6, 5000),
+                        # exact ties between two bf16 neighbours, both parities
+                        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2 ** 20 * (1 + 2 ** -8)])])
+    want = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(orc.round_to_bf16(x), want)
+
+
+def test_d_from_saved_bf16_output():
+    """With window 1 every O row is a V row; with V exactly representable in
+    bf16 the saved output is exact and D equals its exact value, so the
+    gradients agree; with general V the difference obeys the rounding bound."""
+    n, d = 12, 8
+    q, k, _ = _qkv(n, d, 602)
+    v = orc.round_to_bf16(np.random.default_rng(603).standard_normal((n, d)))
+    do = np.random.default_rng(604).standard_normal((n, d))
+    g1 = orc.attention_bwd_head(q, k, v, do, 0.5, True, window=1)
+    g2 = orc.attention_bwd_head(q, k, v, do, 0.5, True, window=1, d_from_saved_bf16=True)
+    for name in ("dq", "dk", "dv", "D"):
+        np.testing.assert_allclose(g2[name], g1[name], atol=1e-12)
+    q, k, v = _qkv(40, d, 605)
+    do = np.random.default_rng(606).standard_normal((40, d))
+    g1 = orc.attention_bwd_head(q, k, v, do, 0.5, True)
+    g2 = orc.attention_bwd_head(q, k, v, do, 0.5, True, d_from_saved_bf16=True)
+    bound = (np.abs(do) * 2.0 ** -8 * np.abs(g1["o"])).sum(axis=1) + 1e-12
+    assert np.all(np.abs(g2["D"] - g1["D"]) <= bound)
+    assert np.abs(g2["D"] - g1["D"]).max() > 0

@@ -76,3 +76,76 @@ def test_window_long_prefill(w, s):
         assert_close(o[0, h, rows], ro, "bf16", "O[h=%d]" % h)
         assert_close(lse[0, h, rows], rl, "bf16", "LSE[h=%d]" % h, kind="lse")
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+def _bwd(x, tau, window, sinks):
+    import io_aware_tiled_03_amd as fa
+    q, k, v, do = (to_device(x[n]) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, tau=tau, causal=True, window=window, sinks=sinks)
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, tau=tau, causal=True, window=window, sinks=sinks)
+    return {"dq": to_f64(dq), "dk": to_f64(dk), "dv": to_f64(dv)}
+
+
+def rounding_allowance(g, q, k, do, tau):
+    """Per-element error allowance of the gradients for the bf16 operands the
+    kernels feed to their MFMA products: P and dS are rounded to bfloat16
+    (relative error <= 2^-9 each, round to nearest) before dV = P^T dO,
+    dK = tau dS^T Q and dQ = tau dS K, so each output can be off by 2^-9 times
+    the sum of the magnitudes of its terms.  The stated absolute bound assumes
+    those sums are of order one; with a window of a few keys plus sinks a sink
+    key's gradient sums hundreds of large terms."""
+    u = 2.0 ** -9
+    return {"dv": u * (np.abs(g["p"]).T @ np.abs(do)),
+            "dk": u * tau * (np.abs(g["ds"]).T @ np.abs(q)),
+            "dq": u * tau * (np.abs(g["ds"]) @ np.abs(k))}
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("w,s", [(1, 0), (2, 1), (16, 0), (100, 4), (129, 0), (200, 130),
+                                 (64, 64), (5000, 0)])
+@pytest.mark.parametrize("N", [7, 130, 300, 600])
+def test_window_bwd_small(N, w, s, d):
+    x = fa_inputs.dense_inputs(2, 2, N, d, "bf16", 14000 + N + w + s, with_do=True)
+    tau = 1.0 / np.sqrt(d)
+    g = _bwd(x, tau, w, s)
+    qf, kf, vf, dof = (x[n].f64() for n in ("q", "k", "v", "do"))
+    for b in range(2):
+        for h in range(2):
+            # D from the saved bf16 output, as the kernels compute it: with a
+            # window of a few keys P is close to one and D's rounding would
+            # otherwise pass into dS undamped.  Entries above |x| = 5 also get
+            # one bf16 ulp (their storage rounding alone exceeds 2e-2).
+            ref = orc.attention_bwd_head(qf[b, h], kf[b, h], vf[b, h], dof[b, h], tau, True,
+                                         window=w, sinks=s, d_from_saved_bf16=True)
+            extra = rounding_allowance(ref, qf[b, h], kf[b, h], dof[b, h], tau)
+            for name in ("dq", "dk", "dv"):
+                assert_close(g[name][b, h], ref[name], "bf16", "%s[%d,%d]" % (name, b, h),
+                             ulp_allow=True, extra=extra[name])
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_window_bwd_covering_everything_is_causal(d):
+    """window >= N and no sinks: the causal backward's bits."""
+    import io_aware_tiled_03_amd as fa
+    import torch
+    x = fa_inputs.dense_inputs(2, 2, 700, d, "bf16", 15000 + d, with_do=True)
+    q, k, v, do = (to_device(x[n]) for n in ("q", "k", "v", "do"))
+    o, lse = fa.fwd(q, k, v, causal=True)
+    g1 = fa.bwd(q, k, v, o, lse, do, causal=True)
+    g2 = fa.bwd(q, k, v, o, lse, do, causal=True, window=700)
+    for a, b in zip(g1, g2):
+        assert torch.equal(a, b)
+
+
+def test_window_bwd_workload():
+    """The backward shape (4x16x4096x64 bf16) as a local layer with a
+    1024-key window and 4 sinks: 3 sampled heads element by element."""
+    wl = fa_inputs.WORKLOADS[5]
+    x = fa_inputs.workload_inputs(wl)
+    g = _bwd(x, wl.tau, 1024, 4)
+    qf, kf, vf, dof = (x[n].f64() for n in ("q", "k", "v", "do"))
+    for b, h in ((0, 3), (1, 10), (3, 15)):
+        ref = orc.attention_bwd_head(qf[b, h], kf[b, h], vf[b, h], dof[b, h], wl.tau, True,
+                                     window=1024, sinks=4, d_from_saved_bf16=True)
+        for name in ("dq", "dk", "dv"):
+            assert_close(g[name][b, h], ref[name], "bf16", "%s[%d,%d]" % (name, b, h))

@@ -29,7 +29,19 @@ def err_stats(got, ref):
     return float(d.max()) if d.size else 0.0, float(d.mean()) if d.size else 0.0
 
 
-def assert_close(got, ref, dtype, what, kind="out"):
+def bf16_ulp(x):
+    """One bf16 unit in the last place at |x| (2^(e-7) for |x| in [2^e, 2^(e+1)))."""
+    ax = np.maximum(np.abs(np.asarray(x, dtype=np.float64)), np.finfo(np.float32).tiny)
+    return np.exp2(np.floor(np.log2(ax)) - 7)
+
+
+def assert_close(got, ref, dtype, what, kind="out", ulp_allow=False, extra=None):
+    """|got - ref| within TOL.  ulp_allow (bf16 outputs only) adds one bf16 unit
+    of the reference value to the max bound per element: an output stored in
+    bf16 can be off by that much through its own rounding, which exceeds the
+    absolute bound once |ref| > 5.12 (outputs of that size arise when a small
+    attention window concentrates the probabilities).  extra: a further
+    per-element allowance (array like ref) derived from the arithmetic."""
     got = np.asarray(got, dtype=np.float64)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
@@ -39,6 +51,12 @@ def assert_close(got, ref, dtype, what, kind="out"):
     if kind == "lse":
         assert mx <= tol["lse"], "%s: max |err| %.3g > %.3g" % (what, mx, tol["lse"])
     else:
-        assert mx <= tol["max"], "%s: max |err| %.3g > %.3g (mean %.3g)" % (what, mx, tol["max"], mean)
+        if (ulp_allow and dtype == "bf16") or extra is not None:
+            allow = tol["max"] + (bf16_ulp(ref) if ulp_allow else 0.0)
+            excess = np.abs(got - ref) - (allow + (0.0 if extra is None else extra))
+            assert excess.max() <= 0, "%s: max |err| %.3g beyond its bound by %.3g (mean %.3g)" % (
+                what, mx, excess.max(), mean)
+        else:
+            assert mx <= tol["max"], "%s: max |err| %.3g > %.3g (mean %.3g)" % (what, mx, tol["max"], mean)
         assert mean <= tol["mean"], "%s: mean |err| %.3g > %.3g" % (what, mean, tol["mean"])
     return mx, mean
