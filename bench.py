@@ -15,7 +15,8 @@ The line also carries, measured in the same run:
   * "roofline": the kernel with the largest share of the step against its
     peak (MFMA bf16 2.5 PFLOP/s; HBM 8 TB/s), with the HBM traffic read from
     the committed rocprofv3 counter summary when it matches the sources;
-  * "also_measured": the long causal prefill (1x32x16384x128), the split-KV
+  * "also_measured": the long causal prefill (1x32x16384x128), the same
+    prefill as a sliding-window (local) layer with a 4096-key window, the split-KV
     decode (64x32, L_b ~ U[1024, 8192], d=128), the paged decode with grouped
     KV heads (64 sequences, 32 query / 8 KV heads, 16-token pages, the same
     key lengths) and the causal backward (4x16x4096x64) at full size, each
@@ -32,6 +33,8 @@ import math
 import os
 import sys
 import time
+
+import numpy as np
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
@@ -105,6 +108,13 @@ def make_step(fa, x, B, H, N, d, tau, timer=None):
             else:
                 timer.run(name, fn)
     return step
+
+
+def window_pairs(N, window, sinks):
+    """Visible (query, key) pairs of one head under the causal mask with a
+    sliding window and sinks: sum_i min(i+1, window) + max(0, min(sinks, i-window+1))."""
+    i = np.arange(N, dtype=np.int64)
+    return float((np.minimum(i + 1, window) + np.maximum(0, np.minimum(sinks, i - window + 1))).sum())
 
 
 def step_work(B, H, N, d):
@@ -211,6 +221,19 @@ def bench_extra(fa, reps=20):
     out["long_causal_prefill"] = {"shape": [B, H, N, d], "causal": True, "ms": round(ms, 4),
                                   "TFLOP/s": round(fl / ms / 1e9, 2),
                                   "frac_mfma_bf16": round(fl / ms / 1e-3 / PEAK_MFMA_BF16, 4)}
+    del q, k, v, o, lse
+
+    # the same prefill as a local (sliding-window) layer: window 4096, no sinks
+    B, H, N, d, wnd = 1, 32, 16384, 128, 4096
+    g.manual_seed(1003)
+    q, k, v = (torch.randn(B, H, N, d, device=dev, generator=g).to(torch.bfloat16) for _ in range(3))
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, N, device=dev)
+    ms = time_it(lambda: fa.fwd(q, k, v, 1 / math.sqrt(d), True, o, lse, window=wnd), reps)
+    fl = 4.0 * B * H * d * window_pairs(N, wnd, 0)
+    out["window_prefill"] = {"shape": [B, H, N, d], "window": wnd, "sinks": 0, "ms": round(ms, 4),
+                             "TFLOP/s": round(fl / ms / 1e9, 2),
+                             "frac_mfma_bf16": round(fl / ms / 1e-3 / PEAK_MFMA_BF16, 4)}
     del q, k, v, o, lse
 
     # decode: 64 x 32 x 8192 x 128, L_b ~ U[1024, 8192]
