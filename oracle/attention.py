@@ -29,6 +29,16 @@ Readings where the pages are silent (each listed in the design notes):
   paradoxo do primeiro token" — StreamingLLM keeps the first few tokens and
   slides the window over the rest): on top of the causal mask, key j is
   visible to query i iff i - j < window or j < sinks.
+* dropout ("flash-attention" page, "o problema" lists dropout among the
+  memory-bound steps of standard attention; "como funciona": the backward keeps
+  the pseudo-random generator's state and regenerates the mask): after the
+  softmax, P_ij is kept with probability 1 - p and scaled by 1/(1 - p), else
+  zeroed; the row statistics (m, l, LSE) are those of the undropped P.  The
+  mask comes from the counter-based generator Philox4x32-10 (Salmon et al.,
+  "Parallel random numbers: as easy as 1, 2, 3", SC11), written here from its
+  published definition: one generator call per 4 x 4 block of (query, key)
+  pairs, counter (j/4, i/4, b*H + h, offset), key = the 64-bit seed; word i%4,
+  byte j%4 is compared with round(256 p) (p is used as that multiple of 1/256).
 * the gradients are derived by hand from O = softmax(tau Q K^T) V:
   dV = P^T dO, dP = dO V^T, D = rowsum(P o dP), dS = P o (dP - D),
   dQ = tau dS K, dK = tau dS^T Q.
@@ -44,7 +54,8 @@ import numpy as np
 __all__ = [
     "scores", "probs", "attention_fwd_head", "attention_fwd", "attention_bwd_head",
     "attention_bwd", "decode_fwd", "tiled_fwd_literal", "split_kv_decode",
-    "gather_pages", "decode_paged", "visible", "round_to_bf16",
+    "gather_pages", "decode_paged", "visible", "round_to_bf16", "philox4x32_10",
+    "dropout_threshold", "dropout_keep", "head_dropout",
 ]
 
 
@@ -83,17 +94,74 @@ def probs(s):
     return e / l[:, None], m, l
 
 
+PHILOX_M = (0xD2511F53, 0xCD9E8D57)   # round multipliers
+PHILOX_W = (0x9E3779B9, 0xBB67AE85)   # key increments between rounds
+
+
+def philox4x32_10(ctr, key):
+    """Philox4x32 with 10 rounds on arrays of counters.
+
+    ctr: uint32-valued array [..., 4]; key: (k0, k1).  Each round multiplies
+    words 0 and 2 by the two constants (64-bit products split into high and
+    low halves) and outputs (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); the key
+    is advanced by the two Weyl constants before every round after the first.
+    Returns the four output words as a uint32 array [..., 4]."""
+    c = np.asarray(ctr, dtype=np.uint64) & np.uint64(0xFFFFFFFF)
+    c0, c1, c2, c3 = c[..., 0], c[..., 1], c[..., 2], c[..., 3]
+    k0, k1 = int(key[0]) & 0xFFFFFFFF, int(key[1]) & 0xFFFFFFFF
+    mask = np.uint64(0xFFFFFFFF)
+    for r in range(10):
+        if r:
+            k0 = (k0 + PHILOX_W[0]) & 0xFFFFFFFF
+            k1 = (k1 + PHILOX_W[1]) & 0xFFFFFFFF
+        p0 = np.uint64(PHILOX_M[0]) * c0
+        p1 = np.uint64(PHILOX_M[1]) * c2
+        hi0, lo0 = p0 >> np.uint64(32), p0 & mask
+        hi1, lo1 = p1 >> np.uint64(32), p1 & mask
+        c0, c1, c2, c3 = hi1 ^ c1 ^ np.uint64(k0), lo1, hi0 ^ c3 ^ np.uint64(k1), lo0
+    return np.stack([c0, c1, c2, c3], axis=-1).astype(np.uint32)
+
+
+def dropout_threshold(p):
+    """The byte threshold t = round(256 p) (0..255); a pair is kept iff its
+    byte >= t, so the drop probability used is t / 256."""
+    t = int(round(float(p) * 256.0))
+    if not (0 <= t <= 255):
+        raise ValueError("dropout probability must round to at most 255/256")
+    return t
+
+
+def dropout_keep(rows, keys, bh, seed, offset, p):
+    """Boolean [len(rows), len(keys)]: which (query, key) pairs of head bh
+    (= b*H + h) survive dropout with probability p, for the given seed/offset."""
+    rows = np.asarray(rows, dtype=np.int64)
+    keys = np.asarray(keys, dtype=np.int64)
+    t = dropout_threshold(p)
+    i = rows[:, None]
+    j = keys[None, :]
+    shape = (len(rows), len(keys))
+    ctr = np.stack([np.broadcast_to(j // 4, shape), np.broadcast_to(i // 4, shape),
+                    np.full(shape, bh), np.full(shape, int(offset) & 0xFFFFFFFF)], axis=-1)
+    words = philox4x32_10(ctr, (int(seed) & 0xFFFFFFFF, (int(seed) >> 32) & 0xFFFFFFFF))
+    word = np.take_along_axis(words, np.broadcast_to(i % 4, shape)[..., None], axis=-1)[..., 0]
+    byte = (word >> (8 * np.broadcast_to(j % 4, shape)).astype(np.uint32)) & np.uint32(0xFF)
+    return byte >= t
+
+
 def _check_window(causal, window, sinks):
     if window is not None and (not causal or window < 1 or sinks < 0):
         raise ValueError("a window needs the causal mask, window >= 1 and sinks >= 0")
 
 
-def attention_fwd_head(q, k, v, tau, causal, rows=None, chunk=1024, window=None, sinks=0):
+def attention_fwd_head(q, k, v, tau, causal, rows=None, chunk=1024, window=None, sinks=0,
+                       drop=None):
     """Standard attention for one (batch, head): O[r] and LSE[r] for the requested rows.
 
     q: [Nq, d], k/v: [Nk, d].  The score rows are materialised whole, in chunks
     of at most ``chunk`` rows; under the causal mask a chunk computes scores only
     against keys up to its last query (the rest are masked, so exp gives 0).
+    drop = (keep, p): dropout with the boolean mask keep(row_indices, key_indices)
+    and probability p: O = (P o keep / (1 - p)) V; LSE is that of the undropped P.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -109,20 +177,34 @@ def attention_fwd_head(q, k, v, tau, causal, rows=None, chunk=1024, window=None,
         kmax = (int(r.max()) + 1) if causal else k.shape[0]
         s = scores(q[r], k[:kmax], tau, r, causal, window, sinks)
         p, m, l = probs(s)
+        if drop is not None:
+            keep, pd = drop
+            p = p * keep(r, np.arange(kmax)) / (1.0 - pd)
         o[a:a + len(r)] = p @ v[:kmax]
         lse[a:a + len(r)] = m + np.log(l)
     return o, lse
 
 
-def attention_fwd(q, k, v, tau, causal, window=None, sinks=0):
-    """Standard attention over [B, H, N, d] tensors: returns O [B,H,N,d], LSE [B,H,N]."""
+def head_dropout(dropout, bh):
+    """(keep, p) of head bh for dropout = (seed, offset, p), or None."""
+    if dropout is None:
+        return None
+    seed, offset, p = dropout
+    pe = dropout_threshold(p) / 256.0
+    return (lambda rows, keys: dropout_keep(rows, keys, bh, seed, offset, p)), pe
+
+
+def attention_fwd(q, k, v, tau, causal, window=None, sinks=0, dropout=None):
+    """Standard attention over [B, H, N, d] tensors: returns O [B,H,N,d], LSE [B,H,N].
+    dropout = (seed, offset, p): the dropout of head b*H + h as in head_dropout."""
     B, H, N, d = q.shape
     o = np.empty((B, H, N, v.shape[-1]))
     lse = np.empty((B, H, N))
     for b in range(B):
         for h in range(H):
             o[b, h], lse[b, h] = attention_fwd_head(q[b, h], k[b, h], v[b, h], tau, causal,
-                                                    window=window, sinks=sinks)
+                                                    window=window, sinks=sinks,
+                                                    drop=head_dropout(dropout, b * H + h))
     return o, lse
 
 
@@ -136,7 +218,8 @@ def round_to_bf16(x):
     return r.view(np.float32).astype(np.float64)
 
 
-def attention_bwd_head(q, k, v, do, tau, causal, window=None, sinks=0, d_from_saved_bf16=False):
+def attention_bwd_head(q, k, v, do, tau, causal, window=None, sinks=0, d_from_saved_bf16=False,
+                       drop=None):
     """Hand-derived gradients of O = softmax(tau Q K^T [+mask]) V for one head.
 
     With the loss's gradient dO:
@@ -149,6 +232,9 @@ def attention_bwd_head(q, k, v, do, tau, causal, window=None, sinks=0, d_from_sa
     identity applied to the output the forward saved when O is stored in
     bfloat16 (the page's backward keeps only the saved O).  The returned "D"
     is then that value.
+    drop = (keep, p): dropout as in attention_fwd_head.  With Z = keep / (1 - p):
+    O = (P o Z) V, dV = (P o Z)^T dO, dS = P o (Z o dP - D) with dP = dO V^T and
+    D_i = sum_j P_ij Z_ij dP_ij = dO_i . O_i.
     Returns dict(dq, dk, dv, o, lse, D, D_from_o, p, ds).
     """
     q = np.asarray(q, dtype=np.float64)
@@ -159,9 +245,10 @@ def attention_bwd_head(q, k, v, do, tau, causal, window=None, sinks=0, d_from_sa
     n = q.shape[0]
     s = scores(q, k, tau, np.arange(n), causal, window, sinks)
     p, m, l = probs(s)
-    o = p @ v
-    dv = p.T @ do
-    dp = do @ v.T
+    z = 1.0 if drop is None else drop[0](np.arange(n), np.arange(k.shape[0])) / (1.0 - drop[1])
+    o = (p * z) @ v
+    dv = (p * z).T @ do
+    dp = z * (do @ v.T)
     D = (p * dp).sum(axis=1)
     if d_from_saved_bf16:
         D = (do * round_to_bf16(o)).sum(axis=1)
@@ -172,7 +259,8 @@ def attention_bwd_head(q, k, v, do, tau, causal, window=None, sinks=0, d_from_sa
             "D": D, "D_from_o": (do * o).sum(axis=1), "p": p, "ds": ds}
 
 
-def attention_bwd(q, k, v, do, tau, causal, window=None, sinks=0, d_from_saved_bf16=False):
+def attention_bwd(q, k, v, do, tau, causal, window=None, sinks=0, d_from_saved_bf16=False,
+                  dropout=None):
     """attention_bwd_head over [B, H, N, d]; returns dq, dk, dv, D as arrays."""
     B, H, N, d = q.shape
     out = {name: np.empty((B, H, N, d)) for name in ("dq", "dk", "dv")}
@@ -180,7 +268,7 @@ def attention_bwd(q, k, v, do, tau, causal, window=None, sinks=0, d_from_saved_b
     for b in range(B):
         for h in range(H):
             g = attention_bwd_head(q[b, h], k[b, h], v[b, h], do[b, h], tau, causal, window, sinks,
-                                   d_from_saved_bf16)
+                                   d_from_saved_bf16, drop=head_dropout(dropout, b * H + h))
             for name in ("dq", "dk", "dv", "D"):
                 out[name][b, h] = g[name]
     return out

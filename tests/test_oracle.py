@@ -492,3 +492,101 @@ def test_d_from_saved_bf16_output():
     bound = (np.abs(do) * 2.0 ** -8 * np.abs(g1["o"])).sum(axis=1) + 1e-12
     assert np.all(np.abs(g2["D"] - g1["D"]) <= bound)
     assert np.abs(g2["D"] - g1["D"]).max() > 0
+
+
+# --- dropout: Philox4x32-10 and the dropped attention -------------------------
+
+GOLDEN_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def test_philox_known_answers():
+    """Philox4x32-10 reproduces the generator's published known-answer vectors."""
+    kat = json.load(open(os.path.join(GOLDEN_DIR, "philox4x32_10_kat.json")))
+    for v in kat["vectors"]:
+        ctr = np.array([int(x, 16) for x in v["ctr"]], dtype=np.uint64)
+        key = [int(x, 16) for x in v["key"]]
+        out = orc.philox4x32_10(ctr[None, :], key)[0]
+        assert [int(x) for x in out] == [int(x, 16) for x in v["out"]]
+
+
+def test_dropout_threshold_and_rate():
+    assert orc.dropout_threshold(0.0) == 0 and orc.dropout_threshold(0.5) == 128
+    assert orc.dropout_threshold(0.1) == 26
+    with pytest.raises(ValueError):
+        orc.dropout_threshold(0.999)
+    keep = orc.dropout_keep(np.arange(256), np.arange(512), 3, 1234567, 0, 0.1)
+    rate = 1 - keep.mean()
+    pe = 26 / 256
+    sigma = np.sqrt(pe * (1 - pe) / keep.size)
+    assert abs(rate - pe) < 5 * sigma
+    # p = 0 keeps everything; other heads, seeds and offsets give other masks
+    assert orc.dropout_keep(np.arange(64), np.arange(64), 0, 9, 0, 0.0).all()
+    base = orc.dropout_keep(np.arange(64), np.arange(64), 0, 9, 0, 0.5)
+    for other in ((1, 9, 0), (0, 10, 0), (0, 9, 1), (0, 9 + (1 << 32), 0)):
+        m = orc.dropout_keep(np.arange(64), np.arange(64), other[0], other[1], other[2], 0.5)
+        assert (m != base).mean() > 0.3
+
+
+def test_dropout_zero_probability_is_plain_attention():
+    q, k, v = _qkv(30, 8, 701)
+    for causal in (False, True):
+        o1, l1 = orc.attention_fwd_head(q, k, v, 0.4, causal)
+        o2, l2 = orc.attention_fwd_head(q, k, v, 0.4, causal, drop=orc.head_dropout((5, 0, 0.0), 0))
+        np.testing.assert_array_equal(o1, o2)
+        np.testing.assert_array_equal(l1, l2)
+
+
+def test_dropout_uniform_weights_closed_form():
+    """Q = 0: P_ij = 1/n_i over the visible keys, so O_i = sum over kept
+    visible keys of V_j / (n_i (1 - p)); the LSE ignores dropout (ln n_i)."""
+    n, d, p = 24, 6, 0.25
+    _, k, v = _qkv(n, d, 702)
+    q = np.zeros((n, d))
+    keep, pe = orc.head_dropout((77, 3, p), 5)
+    o, l = orc.attention_fwd_head(q, k, v, 0.5, True, drop=(keep, pe))
+    km = keep(np.arange(n), np.arange(n))
+    for i in range(n):
+        kept = [j for j in range(i + 1) if km[i, j]]
+        want = v[kept].sum(axis=0) / ((i + 1) * (1 - pe)) if kept else np.zeros(d)
+        np.testing.assert_allclose(o[i], want, atol=1e-14)
+        np.testing.assert_allclose(l[i], np.log(i + 1), atol=1e-14)
+
+
+def test_dropout_expectation():
+    """Averaged over seeds the dropped output tends to the undropped one
+    (E[keep / (1 - p)] = 1)."""
+    q, k, v = _qkv(12, 4, 703)
+    o_ref, _ = orc.attention_fwd_head(q, k, v, 0.5, True)
+    acc = np.zeros_like(o_ref)
+    S = 400
+    for seed in range(S):
+        acc += orc.attention_fwd_head(q, k, v, 0.5, True, drop=orc.head_dropout((seed, 0, 0.3), 0))[0]
+    assert np.abs(acc / S - o_ref).max() < 0.25
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_dropout_gradients_finite_differences(causal):
+    """With the mask fixed (it depends on indices and the seed only) the
+    dropped attention is a smooth function of Q, K, V: central differences
+    match dQ, dK, dV; D = dO . O and sum_j dK_j = 0 still hold."""
+    n, d, tau = 10, 4, 0.7
+    q, k, v = _qkv(n, d, 704)
+    do = np.random.default_rng(705).standard_normal((n, d))
+    drop = orc.head_dropout((31337, 1, 0.4), 2)
+    g = orc.attention_bwd_head(q, k, v, do, tau, causal, drop=drop)
+    f = lambda qq, kk, vv: float((orc.attention_fwd_head(qq, kk, vv, tau, causal, drop=drop)[0]
+                                  * do).sum())
+    h = 1e-6
+    for name, x in (("dq", q), ("dk", k), ("dv", v)):
+        num = np.zeros_like(x)
+        for idx in np.ndindex(*x.shape):
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += h
+            xm[idx] -= h
+            num[idx] = (f(*[xp if x is a else a for a in (q, k, v)])
+                        - f(*[xm if x is a else a for a in (q, k, v)])) / (2 * h)
+        np.testing.assert_allclose(g[name], num, rtol=1e-6, atol=1e-8)
+    np.testing.assert_allclose(g["D"], g["D_from_o"], atol=1e-12)
+    np.testing.assert_allclose(g["dk"].sum(axis=0), 0, atol=1e-12)
+    o_fwd, _ = orc.attention_fwd_head(q, k, v, tau, causal, drop=drop)
+    np.testing.assert_allclose(g["o"], o_fwd, atol=1e-14)
