@@ -19,8 +19,9 @@ The line also carries, measured in the same run:
     prefill as a sliding-window (local) layer with a 4096-key window, the split-KV
     decode (64x32, L_b ~ U[1024, 8192], d=128), the paged decode with grouped
     KV heads (64 sequences, 32 query / 8 KV heads, 16-token pages, the same
-    key lengths) and the causal backward (4x16x4096x64) at full size, each
-    against its roofline (skip: --no-extra);
+    key lengths), the causal backward (4x16x4096x64) and the same shape with
+    dropout p = 0.1 (forward and backward) at full size, each against its
+    roofline (skip: --no-extra);
   * "cpu_baseline": the float64 oracle on the host over a bounded sample of
     the same step (whole heads, about 10 s of CPU work).
 """
@@ -316,6 +317,16 @@ def bench_extra(fa, reps=20):
     out["bwd_recompute"] = {"shape": [B, H, N, d], "causal": True, "ms": round(ms, 4),
                             "TFLOP/s": round(fl / ms / 1e9, 2),
                             "frac_mfma_bf16": round(fl / ms / 1e-3 / PEAK_MFMA_BF16, 4)}
+
+    # the same shape with dropout p = 0.1 (Philox mask regenerated in the backward)
+    drop = (0.1, 1005, 0)
+    ms_f = time_it(lambda: fa.fwd(q, k, v, tau, True, o, lse, dropout=drop), reps)
+    ms_b = time_it(lambda: fa.bwd(q, k, v, o, lse, do, tau, True, dq, dk, dv, ws, dropout=drop),
+                   reps)
+    ffl = 4.0 * B * H * N * N * d / 2
+    out["dropout"] = {"shape": [B, H, N, d], "causal": True, "p": 0.1,
+                      "fwd_ms": round(ms_f, 4), "fwd_TFLOP/s": round(ffl / ms_f / 1e9, 2),
+                      "bwd_ms": round(ms_b, 4), "bwd_TFLOP/s": round(fl / ms_b / 1e9, 2)}
     return out
 
 

@@ -54,7 +54,7 @@ typedef enum {
     FA_ERR_HIP = 5,          /* the HIP runtime reported a launch error        */
     FA_ERR_ALIGN = 6,        /* a pointer is not 16-byte aligned               */
     FA_ERR_ARG = 7           /* a value out of range: tau, split count, window,
-                                sinks or stage                                  */
+                                sinks, stage or dropout probability             */
 } fa_status;
 
 typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
@@ -97,6 +97,30 @@ int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse,
 int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int H, int N, int d, float tau, int window, int sinks,
                   int dtype, void* stream);
+
+/*
+ * fa_fwd_dropout - fa_fwd with dropout on the attention probabilities.
+ *
+ * Standard attention applies dropout to P as one of its memory-bound steps
+ * ("flash-attention" page, "o problema"); the fused kernel applies it on chip
+ * and the backward regenerates the mask from the generator state instead of
+ * storing it (same page, "como funciona", backward paragraph).  After the
+ * softmax each P_ij is kept with probability 1 - p and scaled by 1/(1 - p),
+ * else zeroed; LSE is that of the undropped scores.  The mask is a pure
+ * function of (seed, offset, b, h, i, j): one Philox4x32-10 call (Salmon et
+ * al., "Parallel random numbers: as easy as 1, 2, 3", SC11) per 4 x 4 block of
+ * (query, key) pairs with counter (j/4, i/4, b*H + h, offset) and key = seed
+ * (low word first); the pair is kept iff byte j%4 of output word i%4 is
+ * >= round(256 p).  p is therefore used as a multiple of 1/256.
+ *
+ * p_drop : 0 <= p_drop and round(256 p_drop) <= 255 (FA_ERR_ARG otherwise);
+ *          p_drop = 0 is exactly fa_fwd.
+ * seed, offset : the generator state; fa_bwd_dropout must get the same.
+ * Other arguments as fa_fwd (causal 0 or 1; no sliding window).
+ */
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
+                   int B, int H, int N, int d, float tau, int causal, float p_drop,
+                   unsigned long long seed, unsigned int offset, int dtype, void* stream);
 
 /*
  * fa_decode_workspace_bytes - workspace that fa_decode needs.
@@ -229,6 +253,19 @@ int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, co
                   const void* dout, void* dq, void* dk, void* dv,
                   int B, int H, int N, int d, float tau, int window, int sinks,
                   void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * fa_bwd_dropout - backward of fa_fwd_dropout: regenerates the same mask from
+ * (p_drop, seed, offset); with Z = keep / (1 - p): dV = (P o Z)^T dO,
+ * dS = P o (Z o dP - D) and D_i = dO_i . O_i as before.  o and lse must come
+ * from fa_fwd_dropout with the same arguments.  Arguments as fa_bwd plus the
+ * dropout state (bf16 only).
+ */
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, float tau, int causal, float p_drop,
+                   unsigned long long seed, unsigned int offset,
+                   void* workspace, size_t workspace_bytes, int dtype, void* stream);
 
 /*
  * fa_bwd_stage - enqueue one of fa_bwd's three kernels.

@@ -29,9 +29,11 @@ STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTE
 
 # (name, restype, argtypes) of every symbol that fa.h declares.
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_U64, _U32 = ctypes.c_ulonglong, ctypes.c_uint
 SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa_fwd_window": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
+    "fa_fwd_dropout": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _F, _U64, _U32, _I, _P]),
     "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "fa_decode_num_splits": (_I, [_I, _I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _I, _P, _Z, _I, _P]),
@@ -45,6 +47,8 @@ SIGNATURES = {
                           _I, _P]),
     "fa_bwd_window": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P, _Z,
                            _I, _P]),
+    "fa_bwd_dropout": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _F, _U64,
+                            _U32, _P, _Z, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
 }
 
@@ -98,11 +102,12 @@ def _need(t, name):
         raise ValueError("%s must be contiguous" % name)
 
 
-def fwd(q, k, v, tau=None, causal=False, o=None, lse=None, window=None, sinks=0):
+def fwd(q, k, v, tau=None, causal=False, o=None, lse=None, window=None, sinks=0, dropout=None):
     """O = softmax(tau Q K^T [+causal mask]) V and LSE, via fa_fwd.
 
     With window (causal only): the causal mask restricted to the `window` most
-    recent keys plus the first `sinks` keys, via fa_fwd_window."""
+    recent keys plus the first `sinks` keys, via fa_fwd_window.
+    With dropout = (p, seed, offset): dropout on P, via fa_fwd_dropout."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n)
@@ -110,6 +115,15 @@ def fwd(q, k, v, tau=None, causal=False, o=None, lse=None, window=None, sinks=0)
     tau = 1.0 / math.sqrt(d) if tau is None else float(tau)
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    if dropout is not None:
+        if window is not None:
+            raise ValueError("dropout is supported with no mask or the causal mask")
+        p, seed, offset = dropout
+        st = lib().fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  lse.data_ptr(), B, H, N, d, tau, int(bool(causal)), float(p),
+                                  int(seed), int(offset), _dtype_code(q), _stream(q))
+        check("fa_fwd_dropout", st)
+        return o, lse
     if window is not None:
         if not causal:
             raise ValueError("a sliding window applies to the causal mask")
@@ -199,11 +213,12 @@ def bwd_workspace_bytes(B, H, N):
 
 
 def bwd(q, k, v, o, lse, do, tau=None, causal=False, dq=None, dk=None, dv=None, workspace=None,
-        stage=None, window=None, sinks=0):
+        stage=None, window=None, sinks=0, dropout=None):
     """dQ, dK, dV of fa_fwd's output given dO, via fa_bwd (workspace holds D on return).
 
     With stage in (0, 1, 2) only that kernel is enqueued, via fa_bwd_stage.  With
-    window (causal only): the backward of the sliding-window forward, via fa_bwd_window."""
+    window (causal only): the backward of the sliding-window forward, via fa_bwd_window.
+    With dropout = (p, seed, offset): the backward of fa_fwd_dropout, via fa_bwd_dropout."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (do, "do")):
         _need(t, n)
@@ -219,7 +234,13 @@ def bwd(q, k, v, o, lse, do, tau=None, causal=False, dq=None, dk=None, dv=None, 
             do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, tau,
             int(bool(causal)), workspace.data_ptr(),
             workspace.numel() * workspace.element_size(), _dtype_code(q), _stream(q))
-    if window is not None:
+    if dropout is not None:
+        if window is not None or stage is not None:
+            raise ValueError("dropout backward: no window, whole backward only")
+        p, seed, offset = dropout
+        dargs = args[:15] + (float(p), int(seed), int(offset)) + args[15:]
+        check("fa_bwd_dropout", lib().fa_bwd_dropout(*dargs))
+    elif window is not None:
         if not causal or stage is not None:
             raise ValueError("a sliding window applies to the causal mask, whole backward only")
         wargs = args[:14] + (int(window), int(sinks)) + args[15:]

@@ -70,6 +70,35 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* l
     return after_launch();
 }
 
+// Byte threshold round(256 p) of a dropout probability; -1 if out of range.
+static int drop_threshold(float p) {
+    if (!(p >= 0.f) || !(p < 1.f)) return -1;
+    const int t = (int)lrintf(p * 256.f);
+    return t <= 255 ? t : -1;
+}
+
+int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                   int N, int d, float tau, int causal, float p_drop, unsigned long long seed,
+                   unsigned int offset, int dtype, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    int st = check_common(B, H, N, d, tau, dtype);
+    if (st != FA_OK) return st;
+    if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+    const int thr = drop_threshold(p_drop);
+    if (thr < 0) return FA_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
+        return FA_ERR_ALIGN;
+    const long long bh = (long long)B * H;
+    if (!grid_ok(bh * ((N + 63) / 64), 256)) return FA_ERR_SHAPE;
+    fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, tau, causal, dtype};
+    a.drop_thr = thr;
+    a.seed = seed;
+    a.offset = offset;
+    (void)hipGetLastError();
+    fa::launch_fwd(a, (hipStream_t)stream);
+    return after_launch();
+}
+
 int fa_decode_num_splits(int B, int H, int N_max, int d, int num_splits) {
     if (B < 1 || H < 1 || N_max < 1 || N_max > (1 << 20) || (d != 64 && d != 128)) return 0;
     if (num_splits < 0 || num_splits > 1024) return 0;
@@ -173,7 +202,8 @@ namespace {
 int bwd_common(int stages, const void* q, const void* k, const void* v, const void* o,
                const float* lse, const void* dout, void* dq, void* dk, void* dv, int B, int H,
                int N, int d, float tau, int causal, void* workspace, size_t workspace_bytes,
-               int dtype, void* stream, int window = 0, int sinks = 0) {
+               int dtype, void* stream, int window = 0, int sinks = 0, int drop_thr = 0,
+               unsigned long long seed = 0, unsigned int offset = 0) {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
     int st = check_common(B, H, N, d, tau, dtype);
     if (st != FA_OK) return st;
@@ -191,6 +221,9 @@ int bwd_common(int stages, const void* q, const void* k, const void* v, const vo
         a.window = window < N ? window : N;
         a.sinks = sinks < N ? sinks : N;
     }
+    a.drop_thr = drop_thr;
+    a.seed = seed;
+    a.offset = offset;
     (void)hipGetLastError();
     fa::launch_bwd(a, stages, (hipStream_t)stream);
     return after_launch();
@@ -214,6 +247,17 @@ int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, co
                       workspace_bytes, dtype, stream, window, sinks);
 }
 
+int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
+                   const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                   float tau, int causal, float p_drop, unsigned long long seed,
+                   unsigned int offset, void* workspace, size_t workspace_bytes, int dtype,
+                   void* stream) {
+    const int thr = drop_threshold(p_drop);
+    if (thr < 0) return FA_ERR_ARG;
+    return bwd_common(7, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, tau, causal, workspace,
+                      workspace_bytes, dtype, stream, 0, 0, thr, seed, offset);
+}
+
 int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
                  const float* lse, const void* dout, void* dq, void* dk, void* dv, int B, int H,
                  int N, int d, float tau, int causal, void* workspace, size_t workspace_bytes,
@@ -234,7 +278,7 @@ const char* fa_status_string(int status) {
         case FA_ERR_ALIGN: return "a pointer is not aligned (16 bytes for tensors)";
         case FA_ERR_ARG:
             return "bad argument value (tau finite and > 0, num_splits 0..1024, window >= 1, "
-                   "sinks >= 0, stage 0..2)";
+                   "sinks >= 0, stage 0..2, dropout probability in [0, 255/256])";
         default: return "unknown status";
     }
 }

@@ -91,12 +91,14 @@ struct TileCopy {
 // (key j visible to query i iff j <= i and (i - j < window or j < sinks)).
 enum : int { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2 };
 
-template <int D, int MODE>
+// DROP: the forward dropped P with the mask of Dropout::block; with
+// Z = keep / (1 - p): dV = (P o Z)^T dO and dS = P o (Z o dP - D).
+template <int D, int MODE, bool DROP>
 __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int N, float scale_log2,
-    float tau, int window, int sinks) {
+    float tau, int window, int sinks, Dropout drop) {
     constexpr bool CAUSAL = MODE != kMaskNone, WIN = MODE == kMaskWindow;
     constexpr int BC = 128, BR = 64;
     constexpr int STR = D + 8;                 // padded row (16 * odd bytes)
@@ -192,6 +194,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                 lq[i] = *reinterpret_cast<const f32x4*>(&l_lds[qb * 32 + 16 * (i >> 1) + 8 * hf + 4 * (i & 1)]);
                 dq4[i] = *reinterpret_cast<const f32x4*>(&d_lds[qb * 32 + 16 * (i >> 1) + 8 * hf + 4 * (i & 1)]);
             }
+            // dropout words: 4-query group g = r/4 holds queries
+            // qs + 16 (g/2) + 8 hf + 4 (g%2) + 0..3; word r%4, byte key%4
+            u32x4 dblk[4];
+            if constexpr (DROP) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    dblk[g] = drop.block(key, qs + 16 * (g >> 1) + 8 * hf + 4 * (g & 1), bh);
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float p = fast_exp2(__builtin_fmaf(sacc[r], scale_log2, -lq[r >> 2][r & 3]));
@@ -199,8 +209,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                     const int q = qs + 16 * (r >> 3) + 8 * hf + (r & 7);
                     if (CAUSAL && (key > q || (WIN && q - key >= window && key >= sinks))) p = 0.f;
                 }
-                sacc[r] = p;
-                dp[r] = p * (dp[r] - dq4[r >> 2][r & 3]);
+                if constexpr (DROP) {
+                    const bool kept = drop.keep(dblk[r >> 2][r & 3], key & 3);
+                    sacc[r] = kept ? p : 0.f;
+                    dp[r] = p * ((kept ? dp[r] * drop.scale : 0.f) - dq4[r >> 2][r & 3]);
+                } else {
+                    sacc[r] = p;
+                    dp[r] = p * (dp[r] - dq4[r >> 2][r & 3]);
+                }
             }
 #pragma unroll
             for (int t = 0; t < 2; ++t) {
@@ -279,20 +295,21 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                 u32x2 wk, wv;
                 wk[0] = pack_bf16x2(dkacc[db][4 * g] * tau, dkacc[db][4 * g + 1] * tau);
                 wk[1] = pack_bf16x2(dkacc[db][4 * g + 2] * tau, dkacc[db][4 * g + 3] * tau);
-                wv[0] = pack_bf16x2(dvacc[db][4 * g], dvacc[db][4 * g + 1]);
-                wv[1] = pack_bf16x2(dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]);
+                const float vs = DROP ? drop.scale : 1.f;   // Z's scale, factored out of dV
+                wv[0] = pack_bf16x2(dvacc[db][4 * g] * vs, dvacc[db][4 * g + 1] * vs);
+                wv[1] = pack_bf16x2(dvacc[db][4 * g + 2] * vs, dvacc[db][4 * g + 3] * vs);
                 *reinterpret_cast<u32x2*>(dkr + d) = wk;
                 *reinterpret_cast<u32x2*>(dvr + d) = wv;
             }
     }
 }
 
-template <int D, int MODE>
+template <int D, int MODE, bool DROP>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
     uint16_t* __restrict__ dQ, int BH, int N, float scale_log2, float tau, int n_qtiles, int window,
-    int sinks) {
+    int sinks, Dropout drop) {
     constexpr bool CAUSAL = MODE != kMaskNone, WIN = MODE == kMaskWindow;
     constexpr int BR = 128, BC = 64;
     constexpr int STR = D + 8;
@@ -354,12 +371,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
                 sacc = mfma32x32x16(ka[ks], qf[ks], sacc);
                 dp = mfma32x32x16(va[ks], df[ks], dp);
             }
+            // dropout words of this lane's row for the 4-key groups g = r/4:
+            // keys k0 + 32 kb + 16 (g/2) + 8 hf + 4 (g%2) + 0..3, byte r%4
+            uint32_t dw[4] = {0u, 0u, 0u, 0u};
+            if constexpr (DROP) {
+#pragma unroll
+                for (int g = 0; g < 4; ++g)
+                    dw[g] = Dropout::row_word(
+                        drop.block(k0 + kb * 32 + 16 * (g >> 1) + 8 * hf + 4 * (g & 1), qrow, bh),
+                        qrow & 3);
+            }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float p = fast_exp2(__builtin_fmaf(sacc[r], scale_log2, -lse2));
                 if constexpr (MASK) {
                     const int kk = k0 + kb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7);
                     if (CAUSAL && (kk > qrow || (WIN && qrow - kk >= window && kk >= sinks))) p = 0.f;
+                }
+                if constexpr (DROP) {
+                    const bool kept = drop.keep(dw[r >> 2], r & 3);
+                    dp[r] = kept ? dp[r] * drop.scale : 0.f;
                 }
                 sacc[r] = p * (dp[r] - Dq);
             }
@@ -449,9 +480,15 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     }
 }
 
-template <int D, int MODE>
+template <int D, int MODE, bool DROP>
 void launch(const BwdArgs& a, int stages, hipStream_t st) {
     const int bh = a.B * a.H;
+    Dropout drop;
+    drop.seed_lo = (uint32_t)a.seed;
+    drop.seed_hi = (uint32_t)(a.seed >> 32);
+    drop.offset = a.offset;
+    drop.thr = a.drop_thr;
+    drop.scale = a.drop_thr > 0 ? 256.f / (256.f - (float)a.drop_thr) : 1.f;
     if (stages & 1) {
         const size_t rows = (size_t)bh * a.N;
         const size_t pre_blocks = (rows * (D / 8) + 255) / 256;
@@ -460,25 +497,32 @@ void launch(const BwdArgs& a, int stages, hipStream_t st) {
     }
     if (stages & 2) {
         const int nk = (a.N + 127) / 128;
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, MODE>), dim3(nk * bh), dim3(256), 0, st,
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, MODE, DROP>), dim3(nk * bh), dim3(256), 0, st,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                            (const uint16_t*)a.dout, a.lse, a.D, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                           bh, a.N, a.tau * kLog2e, a.tau, a.window, a.sinks);
+                           bh, a.N, a.tau * kLog2e, a.tau, a.window, a.sinks, drop);
     }
     if (stages & 4) {
         const int nq = (a.N + 127) / 128;
-        hipLaunchKernelGGL((bwd_dq_kernel<D, MODE>), dim3(nq * bh), dim3(256), 0, st,
+        hipLaunchKernelGGL((bwd_dq_kernel<D, MODE, DROP>), dim3(nq * bh), dim3(256), 0, st,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                            (const uint16_t*)a.dout, a.lse, a.D, (uint16_t*)a.dq, bh, a.N,
-                           a.tau * kLog2e, a.tau, nq, a.window, a.sinks);
+                           a.tau * kLog2e, a.tau, nq, a.window, a.sinks, drop);
     }
 }
 
 template <int D>
 void launch_d(const BwdArgs& a, int stages, hipStream_t st) {
-    if (!a.causal) launch<D, kMaskNone>(a, stages, st);
-    else if (a.window < a.N || a.sinks > 0) launch<D, kMaskWindow>(a, stages, st);
-    else launch<D, kMaskCausal>(a, stages, st);
+    if (a.drop_thr > 0) {   // dropout: with no mask or the plain causal mask
+        a.causal ? launch<D, kMaskCausal, true>(a, stages, st)
+                 : launch<D, kMaskNone, true>(a, stages, st);
+    } else if (!a.causal) {
+        launch<D, kMaskNone, false>(a, stages, st);
+    } else if (a.window < a.N || a.sinks > 0) {
+        launch<D, kMaskWindow, false>(a, stages, st);
+    } else {
+        launch<D, kMaskCausal, false>(a, stages, st);
+    }
 }
 
 }  // namespace

@@ -159,6 +159,53 @@ __device__ __forceinline__ u32x4 buf_ld16(rsrc_t r, uint32_t byte_off) {
 __device__ __forceinline__ u32x4 buf_ld16_nt(rsrc_t r, uint32_t byte_off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 2));
 }
+// Philox4x32 with 10 rounds (J. K. Salmon et al., "Parallel random numbers:
+// as easy as 1, 2, 3", SC11): each round multiplies counter words 0 and 2 by
+// the two round constants (one 32x32 -> 64-bit product each) and outputs
+// (hi1 ^ c1 ^ k0, lo1, hi0 ^ c3 ^ k1, lo0); the key advances by the two Weyl
+// constants before every round after the first.
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3,
+                                               uint32_t k0, uint32_t k1) {
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        if (r) {
+            k0 += 0x9E3779B9u;
+            k1 += 0xBB67AE85u;
+        }
+        const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u;
+        const uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
+        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        c1 = (uint32_t)p1;
+        c3 = (uint32_t)p0;
+        c0 = n0;
+        c2 = n2;
+    }
+    return u32x4{c0, c1, c2, c3};
+}
+
+// Dropout of the (query, key) pairs of one 4 x 4 block: one Philox call with
+// counter (key/4, query/4, b*H + h, offset) and key = the 64-bit seed; pair
+// (query, key) is kept iff byte key%4 of word query%4 is >= thr.
+struct Dropout {
+    uint32_t seed_lo, seed_hi, offset;
+    int thr;        // round(256 p), 1..255 when dropout is on
+    float scale;    // 1 / (1 - thr/256)
+    __device__ __forceinline__ u32x4 block(int key, int query, int bh) const {
+        return philox4x32_10((uint32_t)key >> 2, (uint32_t)query >> 2, (uint32_t)bh, offset,
+                             seed_lo, seed_hi);
+    }
+    // The word of a fixed query row (query % 4 = row): keep bits of keys 4k..4k+3.
+    __device__ __forceinline__ static uint32_t row_word(const u32x4& w, int row) {
+        const uint32_t a = (row & 1) ? w[1] : w[0];
+        const uint32_t b = (row & 1) ? w[3] : w[2];
+        return (row & 2) ? b : a;
+    }
+    __device__ __forceinline__ bool keep(uint32_t word, int byte) const {
+        return (int)((word >> (8 * byte)) & 0xFFu) >= thr;
+    }
+};
+
 // Direct global -> LDS copy of 16 bytes per lane: lane i's bytes land at
 // lds_base + 16*i (lds_base must be the same for the whole wave).  Completion
 // is tracked by vmcnt, not by any register: wait with wait_vmem() before a

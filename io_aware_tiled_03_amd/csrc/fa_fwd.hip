@@ -85,11 +85,13 @@ enum : int { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2 };
 
 // BC keys per tile, NW waves per workgroup (32 query rows each); MODE is one
 // of the mask modes (kMaskWindow: causal with a sliding window and sinks).
-template <int D, int MODE, int BC, int NW>
+// DROP: dropout on P after the softmax (mask from Dropout::block); the row
+// sum l and the LSE use the undropped P, O is scaled by 1/(1 - p) at the end.
+template <int D, int MODE, int BC, int NW, bool DROP>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int N, float scale_log2, float tau,
-    int n_qtiles, int window, int sinks) {
+    int n_qtiles, int window, int sinks, Dropout drop) {
     constexpr bool CAUSAL = MODE != kMaskNone, WIN = MODE == kMaskWindow;
     constexpr int BR = 32 * NW, NKB = BC / 32;
     constexpr int KCH = D / 8;             // 16-byte chunks per row
@@ -231,15 +233,28 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-            for (int t = 0; t < 2; ++t)
+            for (int t = 0; t < 2; ++t) {
+                // dropout words of this lane's row for keys k0+32kb+16t+8hf+0..3 and +4..7
+                uint32_t dw[2] = {0u, 0u};
+                if constexpr (DROP) {
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh)
+                        dw[hh] = Dropout::row_word(
+                            drop.block(k0 + kb * 32 + 16 * t + 8 * hf + 4 * hh, qrow, bh), qrow & 3);
+                }
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
                     const int r = 8 * t + 2 * w;
-                    const float p0 = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, -mc));
-                    const float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], scale_log2, -mc));
-                    pf[kb][t][w] = pack_bf16x2(p0, p1);
+                    float p0 = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, -mc));
+                    float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], scale_log2, -mc));
                     l += p0 + p1;
+                    if constexpr (DROP) {   // keys 2(w%2), 2(w%2)+1 of the 4-key group w/2
+                        p0 = drop.keep(dw[w >> 1], 2 * (w & 1)) ? p0 : 0.f;
+                        p1 = drop.keep(dw[w >> 1], 2 * (w & 1) + 1) ? p1 : 0.f;
+                    }
+                    pf[kb][t][w] = pack_bf16x2(p0, p1);
                 }
+            }
         prio_hi();
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -314,7 +329,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
     phase(p2, p3, ic<1>{});
 
     l += xor32(l);
-    const float inv = 1.f / l;
+    const float inv = (DROP ? drop.scale : 1.f) / l;
     if (qrow < N) {
         uint16_t* orow = O + base + (size_t)qrow * D;
 #pragma unroll
@@ -337,7 +352,7 @@ template <int D, bool CAUSAL>
 __global__ __launch_bounds__(64) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int BH, int N, float scale_log2, float tau,
-    int n_qtiles, int window, int sinks) {
+    int n_qtiles, int window, int sinks, Dropout drop) {
     constexpr int BR = 64, BC = 32;
     __shared__ float sK[BC][D];
     __shared__ float sV[BC][D];
@@ -382,15 +397,19 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(
 #pragma unroll
         for (int d = 0; d < D; ++d) o[d] *= alpha;
         for (int c = 0; c < BC; ++c) {
-            const float p = fast_exp2(__builtin_fmaf(s[c], scale_log2, -mc));
+            float p = fast_exp2(__builtin_fmaf(s[c], scale_log2, -mc));
             l += p;
+            if (drop.thr > 0) {   // dropout after the softmax; l keeps the undropped sum
+                const uint32_t w = Dropout::row_word(drop.block(k0 + c, row, bh), row & 3);
+                p = drop.keep(w, (k0 + c) & 3) ? p : 0.f;
+            }
 #pragma unroll
             for (int d = 0; d < D; ++d) o[d] = __builtin_fmaf(p, sV[c][d], o[d]);
         }
         m = mnew;
     }
     if (row < N) {
-        const float inv = 1.f / l;
+        const float inv = (drop.thr > 0 ? drop.scale : 1.f) / l;
 #pragma unroll
         for (int d = 0; d < D; ++d) O[base + (size_t)row * D + d] = o[d] * inv;
         LSE[(size_t)bh * N + row] = m * tau + logf(l);
@@ -403,15 +422,25 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(
 template <int D> struct FwdShape { static constexpr int BC = 64, NW = 4; };
 template <> struct FwdShape<128> { static constexpr int BC = 128, NW = 8; };
 
-template <int D, int MODE>
+Dropout make_dropout(int thr, unsigned long long seed, unsigned int offset) {
+    Dropout d;
+    d.seed_lo = (uint32_t)seed;
+    d.seed_hi = (uint32_t)(seed >> 32);
+    d.offset = offset;
+    d.thr = thr;
+    d.scale = thr > 0 ? 256.f / (256.f - (float)thr) : 1.f;
+    return d;
+}
+
+template <int D, int MODE, bool DROP>
 void launch_bf16(const FwdArgs& a, hipStream_t st) {
     constexpr int BC = FwdShape<D>::BC, NW = FwdShape<D>::NW;
     const int bh = a.B * a.H;
     const int nq = (a.N + 32 * NW - 1) / (32 * NW);
-    hipLaunchKernelGGL((fwd_bf16_kernel<D, MODE, BC, NW>), dim3(nq * bh), dim3(64 * NW), 0, st,
-                       (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+    hipLaunchKernelGGL((fwd_bf16_kernel<D, MODE, BC, NW, DROP>), dim3(nq * bh), dim3(64 * NW), 0,
+                       st, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.o, a.lse, bh, a.N, a.tau * kLog2e, a.tau, nq, a.window,
-                       a.sinks);
+                       a.sinks, make_dropout(a.drop_thr, a.seed, a.offset));
 }
 
 template <int D, bool C>
@@ -420,26 +449,32 @@ void launch_f32(const FwdArgs& a, hipStream_t st) {
     const int bh = a.B * a.H;
     hipLaunchKernelGGL((fwd_f32_kernel<D, C>), dim3(nq * bh), dim3(64), 0, st, (const float*)a.q,
                        (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, bh, a.N,
-                       a.tau * kLog2e, a.tau, nq, a.window, a.sinks);
+                       a.tau * kLog2e, a.tau, nq, a.window, a.sinks,
+                       make_dropout(a.drop_thr, a.seed, a.offset));
+}
+
+template <int D>
+void launch_bf16_d(const FwdArgs& a, hipStream_t st) {
+    const bool win = a.causal && (a.window < a.N || a.sinks > 0);
+    if (a.drop_thr > 0) {   // dropout: with no mask or the plain causal mask
+        a.causal ? launch_bf16<D, kMaskCausal, true>(a, st) : launch_bf16<D, kMaskNone, true>(a, st);
+    } else if (!a.causal) {
+        launch_bf16<D, kMaskNone, false>(a, st);
+    } else if constexpr (D == 128) {
+        // d = 128 runs plain causal attention through the window variant
+        // (window = N, no sinks: the same mask).  Its register allocation
+        // has no spills and measured 3% faster on the long causal prefill.
+        launch_bf16<D, kMaskWindow, false>(a, st);
+    } else {
+        win ? launch_bf16<D, kMaskWindow, false>(a, st) : launch_bf16<D, kMaskCausal, false>(a, st);
+    }
 }
 
 }  // namespace
 
 void launch_fwd(const FwdArgs& a, hipStream_t st) {
     if (a.dtype == kBF16) {
-        const bool win = a.causal && (a.window < a.N || a.sinks > 0);
-        const int mode = !a.causal ? kMaskNone : win ? kMaskWindow : kMaskCausal;
-        if (a.d == 64) {
-            mode == kMaskNone     ? launch_bf16<64, kMaskNone>(a, st)
-            : mode == kMaskCausal ? launch_bf16<64, kMaskCausal>(a, st)
-                                  : launch_bf16<64, kMaskWindow>(a, st);
-        } else {
-            // d = 128 runs plain causal attention through the window variant
-            // (window = N, no sinks: the same mask).  Its register allocation
-            // has no spills and measured 3% faster on the long causal prefill.
-            mode == kMaskNone ? launch_bf16<128, kMaskNone>(a, st)
-                              : launch_bf16<128, kMaskWindow>(a, st);
-        }
+        a.d == 64 ? launch_bf16_d<64>(a, st) : launch_bf16_d<128>(a, st);
     } else {
         if (a.d == 64) a.causal ? launch_f32<64, true>(a, st) : launch_f32<64, false>(a, st);
         else a.causal ? launch_f32<128, true>(a, st) : launch_f32<128, false>(a, st);

@@ -18,6 +18,9 @@ struct FwdArgs {
     int causal, dtype;
     int window = 0x40000000;   // causal only: key j visible to query i iff j <= i and
     int sinks = 0;             // (i - j < window or j < sinks); the defaults give plain causal
+    int drop_thr = 0;          // dropout: byte threshold round(256 p); 0 = no dropout
+    unsigned long long seed = 0;
+    unsigned int offset = 0;
 };
 void launch_fwd(const FwdArgs& a, hipStream_t st);
 
@@ -67,6 +70,9 @@ struct BwdArgs {
     int causal, dtype;
     int window = 0x40000000;   // as in FwdArgs
     int sinks = 0;
+    int drop_thr = 0;
+    unsigned long long seed = 0;
+    unsigned int offset = 0;
 };
 // stages: bit 0 = D preprocess, bit 1 = dK/dV, bit 2 = dQ (launched in that order)
 void launch_bwd(const BwdArgs& a, int stages, hipStream_t st);

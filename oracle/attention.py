@@ -235,7 +235,7 @@ def attention_bwd_head(q, k, v, do, tau, causal, window=None, sinks=0, d_from_sa
     drop = (keep, p): dropout as in attention_fwd_head.  With Z = keep / (1 - p):
     O = (P o Z) V, dV = (P o Z)^T dO, dS = P o (Z o dP - D) with dP = dO V^T and
     D_i = sum_j P_ij Z_ij dP_ij = dO_i . O_i.
-    Returns dict(dq, dk, dv, o, lse, D, D_from_o, p, ds).
+    Returns dict(dq, dk, dv, o, lse, D, D_from_o, p, pz (= P o Z), ds).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -256,7 +256,7 @@ def attention_bwd_head(q, k, v, do, tau, causal, window=None, sinks=0, d_from_sa
     dq = tau * (ds @ k)
     dk = tau * (ds.T @ q)
     return {"dq": dq, "dk": dk, "dv": dv, "o": o, "lse": m + np.log(l),
-            "D": D, "D_from_o": (do * o).sum(axis=1), "p": p, "ds": ds}
+            "D": D, "D_from_o": (do * o).sum(axis=1), "p": p, "pz": p * z, "ds": ds}
 
 
 def attention_bwd(q, k, v, do, tau, causal, window=None, sinks=0, d_from_saved_bf16=False,

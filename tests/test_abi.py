@@ -84,6 +84,28 @@ def test_fwd_window_rejects_bad_arguments():
     assert call(o=P + 4) == 6
 
 
+def test_dropout_rejects_bad_arguments():
+    fa, lib = _lib()
+    f = [P, P, P, P, P, 1, 1, 16, 64, 0.125, 1, 0.1, 5, 0, 1, None]
+    bad = list(f); bad[11] = -0.1
+    assert lib.fa_fwd_dropout(*bad) == 7
+    bad = list(f); bad[11] = 0.999
+    assert lib.fa_fwd_dropout(*bad) == 7
+    bad = list(f); bad[11] = float("nan")
+    assert lib.fa_fwd_dropout(*bad) == 7
+    bad = list(f); bad[10] = 3
+    assert lib.fa_fwd_dropout(*bad) == 3
+    bad = list(f); bad[0] = None
+    assert lib.fa_fwd_dropout(*bad) == 1
+    b = [P, P, P, P, P, P, P, P, P, 1, 2, 64, 64, 0.125, 1, 0.1, 5, 0, P, 1 << 20, 1, None]
+    bad = list(b); bad[15] = 1.0
+    assert lib.fa_bwd_dropout(*bad) == 7
+    bad = list(b); bad[20] = 0
+    assert lib.fa_bwd_dropout(*bad) == 3
+    bad = list(b); bad[18] = None
+    assert lib.fa_bwd_dropout(*bad) == 4
+
+
 def _dec(lib, **kw):
     a = dict(q=P, k=P, v=P, sl=P, B=2, H=2, N=100, d=128, tau=0.1, o=P, lse=P, ns=0, ws=P,
              wsb=1 << 30, dtype=1)

@@ -5,7 +5,7 @@ import pytest
 
 import fa_inputs
 from oracle import attention as orc
-from tests.util import assert_close, to_device, to_f64
+from tests.util import assert_close, rounding_allowance, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -84,20 +84,6 @@ def _bwd(x, tau, window, sinks):
     o, lse = fa.fwd(q, k, v, tau=tau, causal=True, window=window, sinks=sinks)
     dq, dk, dv = fa.bwd(q, k, v, o, lse, do, tau=tau, causal=True, window=window, sinks=sinks)
     return {"dq": to_f64(dq), "dk": to_f64(dk), "dv": to_f64(dv)}
-
-
-def rounding_allowance(g, q, k, do, tau):
-    """Per-element error allowance of the gradients for the bf16 operands the
-    kernels feed to their MFMA products: P and dS are rounded to bfloat16
-    (relative error <= 2^-9 each, round to nearest) before dV = P^T dO,
-    dK = tau dS^T Q and dQ = tau dS K, so each output can be off by 2^-9 times
-    the sum of the magnitudes of its terms.  The stated absolute bound assumes
-    those sums are of order one; with a window of a few keys plus sinks a sink
-    key's gradient sums hundreds of large terms."""
-    u = 2.0 ** -9
-    return {"dv": u * (np.abs(g["p"]).T @ np.abs(do)),
-            "dk": u * tau * (np.abs(g["ds"]).T @ np.abs(q)),
-            "dq": u * tau * (np.abs(g["ds"]) @ np.abs(k))}
 
 
 @pytest.mark.parametrize("d", [64, 128])

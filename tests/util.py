@@ -60,3 +60,18 @@ def assert_close(got, ref, dtype, what, kind="out", ulp_allow=False, extra=None)
             assert mx <= tol["max"], "%s: max |err| %.3g > %.3g (mean %.3g)" % (what, mx, tol["max"], mean)
         assert mean <= tol["mean"], "%s: mean |err| %.3g > %.3g" % (what, mean, tol["mean"])
     return mx, mean
+
+
+def rounding_allowance(g, q, k, do, tau):
+    """Per-element error allowance of one head's gradients for the bf16
+    operands the kernels feed to their MFMA products: P (dropped, if dropout)
+    and dS are rounded to bfloat16 (relative error <= 2^-9 each, round to
+    nearest) before dV = (P o Z)^T dO, dK = tau dS^T Q and dQ = tau dS K, so an
+    output can be off by 2^-9 times the sum of the magnitudes of its terms.
+    The stated absolute bound assumes those sums are of order one; with a few
+    visible keys per row (small windows, short causal rows under dropout) they
+    are not.  g: the oracle's attention_bwd_head result."""
+    u = 2.0 ** -9
+    return {"dv": u * (np.abs(g["pz"]).T @ np.abs(do)),
+            "dk": u * tau * (np.abs(g["ds"]).T @ np.abs(q)),
+            "dq": u * tau * (np.abs(g["ds"]) @ np.abs(k))}
