@@ -29,6 +29,12 @@ Readings where the pages are silent (each listed in the design notes):
   paradoxo do primeiro token" — StreamingLLM keeps the first few tokens and
   slides the window over the rest): on top of the causal mask, key j is
   visible to query i iff i - j < window or j < sinks.
+* block-sparse attention ("flash-attention" page, "o que isso custou": the
+  paper's answer to long sequences is block-sparse FlashAttention, an
+  approximation): a block mask over (query block, key block) pairs of sizes
+  bq x bk; key j is visible to query i only if block (i // bq, j // bk) is
+  set (and j <= i under the causal mask).  A row with no visible key has the
+  empty sum: O = 0 and LSE = -inf.
 * dropout ("flash-attention" page, "o problema" lists dropout among the
   memory-bound steps of standard attention; "como funciona": the backward keeps
   the pseudo-random generator's state and regenerates the mask): after the
@@ -55,16 +61,17 @@ __all__ = [
     "scores", "probs", "attention_fwd_head", "attention_fwd", "attention_bwd_head",
     "attention_bwd", "decode_fwd", "tiled_fwd_literal", "split_kv_decode",
     "gather_pages", "decode_paged", "visible", "round_to_bf16", "philox4x32_10",
-    "dropout_threshold", "dropout_keep", "head_dropout",
+    "dropout_threshold", "dropout_keep", "head_dropout", "head_block",
 ]
 
 
-def visible(row_idx, key_idx, causal, window=None, sinks=0):
+def visible(row_idx, key_idx, causal, window=None, sinks=0, block=None):
     """Boolean [rows, keys]: which keys each query row may attend to.
 
     causal: key j <= query i.  window (causal only): additionally i - j < window
     or j < sinks (a sliding window of the `window` most recent keys, the query's
-    own included, plus the first `sinks` keys)."""
+    own included, plus the first `sinks` keys).  block = (mask, bq, bk): also
+    mask[i // bq, j // bk] must be set (block-sparse attention)."""
     i = np.asarray(row_idx)[:, None]
     j = np.asarray(key_idx)[None, :]
     vis = np.ones((i.shape[0], j.shape[1]), dtype=bool)
@@ -72,26 +79,40 @@ def visible(row_idx, key_idx, causal, window=None, sinks=0):
         vis &= j <= i
     if window is not None:
         vis &= ((i - j) < window) | (j < sinks)
+    if block is not None:
+        mask, bq, bk = block
+        vis &= np.asarray(mask, dtype=bool)[i // bq, j // bk]
     return vis
 
 
-def scores(q_rows, k, tau, row_idx, causal, window=None, sinks=0):
+def scores(q_rows, k, tau, row_idx, causal, window=None, sinks=0, block=None):
     """S[r, j] = tau * q_rows[r] . k[j], with -inf where key j is not visible to
     query row_idx[r] ("o problema": S = Q K^T; "como funciona": the scale tau)."""
     s = tau * (np.asarray(q_rows, dtype=np.float64) @ np.asarray(k, dtype=np.float64).T)
-    if causal or window is not None:
-        s = np.where(visible(row_idx, np.arange(k.shape[0]), causal, window, sinks), s, -np.inf)
+    if causal or window is not None or block is not None:
+        s = np.where(visible(row_idx, np.arange(k.shape[0]), causal, window, sinks, block), s,
+                     -np.inf)
     return s
 
 
 def probs(s):
     """Row softmax of a full score block: P = exp(S - m) / l, m = rowmax, l = rowsum.
 
-    Returns (P, m, l)."""
+    A row with no visible key (all -inf) has the empty sum: P = 0, m = -inf,
+    l = 0 (so its LSE = m + ln l is -inf).  Returns (P, m, l)."""
     m = s.max(axis=1)
-    e = np.exp(s - m[:, None])
+    live = np.isfinite(m)
+    e = np.zeros_like(s)
+    e[live] = np.exp(s[live] - m[live, None])
     l = e.sum(axis=1)
-    return e / l[:, None], m, l
+    p = np.zeros_like(s)
+    p[live] = e[live] / l[live, None]
+    return p, m, l
+
+
+def _lse(m, l):
+    with np.errstate(divide="ignore"):
+        return m + np.log(l)
 
 
 PHILOX_M = (0xD2511F53, 0xCD9E8D57)   # round multipliers
@@ -154,7 +175,7 @@ def _check_window(causal, window, sinks):
 
 
 def attention_fwd_head(q, k, v, tau, causal, rows=None, chunk=1024, window=None, sinks=0,
-                       drop=None):
+                       drop=None, block=None):
     """Standard attention for one (batch, head): O[r] and LSE[r] for the requested rows.
 
     q: [Nq, d], k/v: [Nk, d].  The score rows are materialised whole, in chunks
@@ -175,13 +196,13 @@ def attention_fwd_head(q, k, v, tau, causal, rows=None, chunk=1024, window=None,
     for a in range(0, len(rows), chunk):
         r = rows[a:a + chunk]
         kmax = (int(r.max()) + 1) if causal else k.shape[0]
-        s = scores(q[r], k[:kmax], tau, r, causal, window, sinks)
+        s = scores(q[r], k[:kmax], tau, r, causal, window, sinks, block)
         p, m, l = probs(s)
         if drop is not None:
             keep, pd = drop
             p = p * keep(r, np.arange(kmax)) / (1.0 - pd)
         o[a:a + len(r)] = p @ v[:kmax]
-        lse[a:a + len(r)] = m + np.log(l)
+        lse[a:a + len(r)] = _lse(m, l)
     return o, lse
 
 
@@ -194,9 +215,20 @@ def head_dropout(dropout, bh):
     return (lambda rows, keys: dropout_keep(rows, keys, bh, seed, offset, p)), pe
 
 
-def attention_fwd(q, k, v, tau, causal, window=None, sinks=0, dropout=None):
+def head_block(block, h):
+    """(mask, bq, bk) of head h for block = (masks [1 or H, nbq, nbk], bq, bk), or None."""
+    if block is None:
+        return None
+    masks, bq, bk = block
+    masks = np.asarray(masks)
+    return masks[h if masks.shape[0] > 1 else 0], bq, bk
+
+
+def attention_fwd(q, k, v, tau, causal, window=None, sinks=0, dropout=None, block=None):
     """Standard attention over [B, H, N, d] tensors: returns O [B,H,N,d], LSE [B,H,N].
-    dropout = (seed, offset, p): the dropout of head b*H + h as in head_dropout."""
+    dropout = (seed, offset, p): the dropout of head b*H + h as in head_dropout.
+    block = (masks [1 or H, nbq, nbk], bq, bk): block-sparse (masks shared by
+    every batch entry; one per head or one for all heads)."""
     B, H, N, d = q.shape
     o = np.empty((B, H, N, v.shape[-1]))
     lse = np.empty((B, H, N))
@@ -204,7 +236,8 @@ def attention_fwd(q, k, v, tau, causal, window=None, sinks=0, dropout=None):
         for h in range(H):
             o[b, h], lse[b, h] = attention_fwd_head(q[b, h], k[b, h], v[b, h], tau, causal,
                                                     window=window, sinks=sinks,
-                                                    drop=head_dropout(dropout, b * H + h))
+                                                    drop=head_dropout(dropout, b * H + h),
+                                                    block=head_block(block, h))
     return o, lse
 
 
@@ -219,7 +252,7 @@ def round_to_bf16(x):
 
 
 def attention_bwd_head(q, k, v, do, tau, causal, window=None, sinks=0, d_from_saved_bf16=False,
-                       drop=None):
+                       drop=None, block=None):
     """Hand-derived gradients of O = softmax(tau Q K^T [+mask]) V for one head.
 
     With the loss's gradient dO:
@@ -243,7 +276,7 @@ def attention_bwd_head(q, k, v, do, tau, causal, window=None, sinks=0, d_from_sa
     do = np.asarray(do, dtype=np.float64)
     _check_window(causal, window, sinks)
     n = q.shape[0]
-    s = scores(q, k, tau, np.arange(n), causal, window, sinks)
+    s = scores(q, k, tau, np.arange(n), causal, window, sinks, block)
     p, m, l = probs(s)
     z = 1.0 if drop is None else drop[0](np.arange(n), np.arange(k.shape[0])) / (1.0 - drop[1])
     o = (p * z) @ v
@@ -255,12 +288,12 @@ def attention_bwd_head(q, k, v, do, tau, causal, window=None, sinks=0, d_from_sa
     ds = p * (dp - D[:, None])
     dq = tau * (ds @ k)
     dk = tau * (ds.T @ q)
-    return {"dq": dq, "dk": dk, "dv": dv, "o": o, "lse": m + np.log(l),
+    return {"dq": dq, "dk": dk, "dv": dv, "o": o, "lse": _lse(m, l),
             "D": D, "D_from_o": (do * o).sum(axis=1), "p": p, "pz": p * z, "ds": ds}
 
 
 def attention_bwd(q, k, v, do, tau, causal, window=None, sinks=0, d_from_saved_bf16=False,
-                  dropout=None):
+                  dropout=None, block=None):
     """attention_bwd_head over [B, H, N, d]; returns dq, dk, dv, D as arrays."""
     B, H, N, d = q.shape
     out = {name: np.empty((B, H, N, d)) for name in ("dq", "dk", "dv")}
@@ -268,7 +301,8 @@ def attention_bwd(q, k, v, do, tau, causal, window=None, sinks=0, d_from_saved_b
     for b in range(B):
         for h in range(H):
             g = attention_bwd_head(q[b, h], k[b, h], v[b, h], do[b, h], tau, causal, window, sinks,
-                                   d_from_saved_bf16, drop=head_dropout(dropout, b * H + h))
+                                   d_from_saved_bf16, drop=head_dropout(dropout, b * H + h),
+                                   block=head_block(block, h))
             for name in ("dq", "dk", "dv", "D"):
                 out[name][b, h] = g[name]
     return out
@@ -295,7 +329,7 @@ def decode_fwd(q, k, v, seqlens, tau, heads=None, batches=None):
     return o, lse
 
 
-def tiled_fwd_literal(q, k, v, tau, causal, Br, Bc, window=None, sinks=0):
+def tiled_fwd_literal(q, k, v, tau, causal, Br, Bc, window=None, sinks=0, block=None):
     """Self-check of the tiled recurrence, in the page's own loop order.
 
     Follows "como funciona" of the "flash-attention" encyclopedia page: the outer
@@ -323,9 +357,9 @@ def tiled_fwd_literal(q, k, v, tau, causal, Br, Bc, window=None, sinks=0):
             rows = np.arange(i0, min(i0 + Br, nq))
             Qi, Oi, li, mi = q[rows], O[rows].copy(), l[rows].copy(), m[rows].copy()
             Sij = tau * (Qi @ Kj.T)
-            if causal or window is not None:
+            if causal or window is not None or block is not None:
                 keys = np.arange(j0, j0 + Kj.shape[0])
-                Sij = np.where(visible(rows, keys, causal, window, sinks), Sij, -np.inf)
+                Sij = np.where(visible(rows, keys, causal, window, sinks, block), Sij, -np.inf)
             m_til = Sij.max(axis=1)
             live = np.isfinite(m_til)
             if not live.any():
@@ -340,7 +374,7 @@ def tiled_fwd_literal(q, k, v, tau, causal, Br, Bc, window=None, sinks=0):
                         + a_new[:, None] * (P_til @ Vj)) / l_new[:, None]
             li[live], mi[live] = l_new, m_new
             O[rows], l[rows], m[rows] = Oi, li, mi
-    return O, m + np.log(l)
+    return O, _lse(m, l)
 
 
 def split_kv_decode(q, k, v, tau, bounds):

@@ -590,3 +590,95 @@ def test_dropout_gradients_finite_differences(causal):
     np.testing.assert_allclose(g["dk"].sum(axis=0), 0, atol=1e-12)
     o_fwd, _ = orc.attention_fwd_head(q, k, v, tau, causal, drop=drop)
     np.testing.assert_allclose(g["o"], o_fwd, atol=1e-14)
+
+
+# --- block-sparse attention -------------------------------------------------
+
+def test_block_mask_all_ones_is_dense():
+    q, k, v = _qkv(50, 8, 801)
+    for causal in (False, True):
+        o1, l1 = orc.attention_fwd_head(q, k, v, 0.3, causal)
+        ones = np.ones((4, 7), dtype=np.uint8)
+        o2, l2 = orc.attention_fwd_head(q, k, v, 0.3, causal, block=(ones, 16, 8))
+        np.testing.assert_array_equal(o1, o2)
+        np.testing.assert_array_equal(l1, l2)
+
+
+def test_block_lower_triangle_with_causal_is_causal():
+    """A lower-triangular block mask (square blocks) under the causal mask
+    drops only blocks the causal mask drops anyway."""
+    q, k, v = _qkv(64, 8, 802)
+    tri = np.tril(np.ones((4, 4), dtype=np.uint8))
+    o1, l1 = orc.attention_fwd_head(q, k, v, 0.3, True)
+    o2, l2 = orc.attention_fwd_head(q, k, v, 0.3, True, block=(tri, 16, 16))
+    np.testing.assert_array_equal(o1, o2)
+    np.testing.assert_array_equal(l1, l2)
+
+
+def test_block_diagonal_is_independent_segments():
+    """A block-diagonal mask makes each block of rows attend to its own block
+    of keys only: standard attention on each segment separately."""
+    n, bs = 48, 16
+    q, k, v = _qkv(n, 6, 803)
+    diag = np.eye(n // bs, dtype=np.uint8)
+    for causal in (False, True):
+        o, l = orc.attention_fwd_head(q, k, v, 0.5, causal, block=(diag, bs, bs))
+        for a in range(0, n, bs):
+            oo, ll = orc.attention_fwd_head(q[a:a + bs], k[a:a + bs], v[a:a + bs], 0.5, causal)
+            np.testing.assert_allclose(o[a:a + bs], oo, atol=1e-14)
+            np.testing.assert_allclose(l[a:a + bs], ll, atol=1e-14)
+
+
+def test_block_uniform_weights_and_empty_rows():
+    """Q = 0: O_i is the mean of V over the visible keys and LSE_i = ln(count);
+    a row whose blocks are all clear has O = 0 and LSE = -inf."""
+    n, d = 40, 4
+    _, k, v = _qkv(n, d, 804)
+    q = np.zeros((n, d))
+    mask = np.array([[1, 0, 1], [0, 0, 0], [1, 1, 0], [0, 1, 1], [1, 0, 0]], dtype=np.uint8)
+    o, l = orc.attention_fwd_head(q, k, v, 0.5, False, block=(mask, 8, 16))
+    for i in range(n):
+        keys = [j for j in range(n) if mask[i // 8, j // 16]]
+        if keys:
+            np.testing.assert_allclose(o[i], v[keys].mean(axis=0), atol=1e-14)
+            np.testing.assert_allclose(l[i], np.log(len(keys)), atol=1e-14)
+        else:
+            assert np.all(o[i] == 0) and np.isneginf(l[i])
+
+
+@pytest.mark.parametrize("Br,Bc", [(16, 16), (7, 13), (64, 5)])
+def test_tiled_recurrence_with_block_mask(Br, Bc):
+    q, k, v = _qkv(64, 8, 805)
+    mask = (np.random.default_rng(806).random((8, 4)) < 0.5).astype(np.uint8)
+    mask[0, 0] = 1
+    for causal in (False, True):
+        o1, l1 = orc.attention_fwd_head(q, k, v, 0.4, causal, block=(mask, 8, 16))
+        o2, l2 = orc.tiled_fwd_literal(q, k, v, 0.4, causal, Br, Bc, block=(mask, 8, 16))
+        live = np.isfinite(l1)
+        np.testing.assert_allclose(o2, o1, atol=1e-12)
+        np.testing.assert_allclose(l2[live], l1[live], atol=1e-12)
+        assert np.array_equal(np.isneginf(l2), ~live)
+
+
+def test_block_gradients_finite_differences():
+    n, d, tau = 12, 4, 0.7
+    q, k, v = _qkv(n, d, 807)
+    do = np.random.default_rng(808).standard_normal((n, d))
+    mask = np.array([[1, 0, 1], [0, 1, 1], [0, 0, 0]], dtype=np.uint8)
+    blk = (mask, 4, 4)
+    for causal in (False, True):
+        g = orc.attention_bwd_head(q, k, v, do, tau, causal, block=blk)
+        f = lambda qq, kk, vv: float((orc.attention_fwd_head(qq, kk, vv, tau, causal, block=blk)[0]
+                                      * do).sum())
+        h = 1e-6
+        for name, x in (("dq", q), ("dk", k), ("dv", v)):
+            num = np.zeros_like(x)
+            for idx in np.ndindex(*x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += h
+                xm[idx] -= h
+                num[idx] = (f(*[xp if x is a else a for a in (q, k, v)])
+                            - f(*[xm if x is a else a for a in (q, k, v)])) / (2 * h)
+            np.testing.assert_allclose(g[name], num, rtol=1e-6, atol=1e-8)
+        # rows 8..11 see nothing: no gradient flows through them
+        assert np.all(g["dq"][8:] == 0) and np.all(g["D"][8:] == 0)
