@@ -16,7 +16,8 @@ The line also carries, measured in the same run:
     peak (MFMA bf16 2.5 PFLOP/s; HBM 8 TB/s), with the HBM traffic read from
     the committed rocprofv3 counter summary when it matches the sources;
   * "also_measured": the long causal prefill (1x32x16384x128), the same
-    prefill as a sliding-window (local) layer with a 4096-key window, the split-KV
+    prefill as a sliding-window (local) layer with a 4096-key window and as a
+    block-sparse layer (band plus global blocks), the split-KV
     decode (64x32, L_b ~ U[1024, 8192], d=128), the paged decode with grouped
     KV heads (64 sequences, 32 query / 8 KV heads, 16-token pages, the same
     key lengths), the causal backward (4x16x4096x64) and the same shape with
@@ -235,6 +236,29 @@ def bench_extra(fa, reps=20):
     out["window_prefill"] = {"shape": [B, H, N, d], "window": wnd, "sinks": 0, "ms": round(ms, 4),
                              "TFLOP/s": round(fl / ms / 1e9, 2),
                              "frac_mfma_bf16": round(fl / ms / 1e-3 / PEAK_MFMA_BF16, 4)}
+    del q, k, v, o, lse
+
+    # the same prefill block-sparse: 128 x 128 blocks, a band of 3 blocks
+    # around the diagonal plus the first key block (global tokens), causal
+    B, H, N, d, bs = 1, 32, 16384, 128, 128
+    nb = N // bs
+    bi, bj = np.meshgrid(np.arange(nb), np.arange(nb), indexing="ij")
+    mask_np = ((np.abs(bi - bj) <= 1) | (bj == 0)).astype(np.uint8)
+    # visible pairs: whole blocks below the diagonal, half (with it) on it
+    pairs = float(((mask_np == 1) & (bi > bj)).sum()) * bs * bs + nb * bs * (bs + 1) / 2
+    g.manual_seed(1003)
+    q, k, v = (torch.randn(B, H, N, d, device=dev, generator=g).to(torch.bfloat16) for _ in range(3))
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, N, device=dev)
+    bm = torch.from_numpy(mask_np[None]).to(dev)
+    ms = time_it(lambda: fa.fwd(q, k, v, 1 / math.sqrt(d), True, o, lse, block_mask=bm,
+                                block_size=(bs, bs)), reps)
+    fl = 4.0 * B * H * d * pairs
+    out["block_sparse_prefill"] = {"shape": [B, H, N, d], "block": [bs, bs],
+                                   "pattern": "band +-1 block and global first key block, causal",
+                                   "density": round(pairs / (N * (N + 1) / 2), 4),
+                                   "ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 2),
+                                   "frac_mfma_bf16": round(fl / ms / 1e-3 / PEAK_MFMA_BF16, 4)}
     del q, k, v, o, lse
 
     # decode: 64 x 32 x 8192 x 128, L_b ~ U[1024, 8192]

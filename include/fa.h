@@ -54,7 +54,7 @@ typedef enum {
     FA_ERR_HIP = 5,          /* the HIP runtime reported a launch error        */
     FA_ERR_ALIGN = 6,        /* a pointer is not 16-byte aligned               */
     FA_ERR_ARG = 7           /* a value out of range: tau, split count, window,
-                                sinks, stage or dropout probability             */
+                                sinks, stage, dropout probability, block size   */
 } fa_status;
 
 typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
@@ -121,6 +121,28 @@ int fa_fwd_window(const void* q, const void* k, const void* v, void* o, float* l
 int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* lse,
                    int B, int H, int N, int d, float tau, int causal, float p_drop,
                    unsigned long long seed, unsigned int offset, int dtype, void* stream);
+
+/*
+ * fa_fwd_block_sparse - block-sparse attention forward.
+ *
+ * The pages' answer to sequences too long for exact attention is the
+ * block-sparse variant of the fused kernel, an approximation ("flash-attention"
+ * page, "o que isso custou"): a mask over (query block, key block) pairs
+ * switches whole blocks of the score matrix off, and tiles that hold no set
+ * block are never loaded.  Key j is visible to query i only if
+ * block_mask[head][i / block_q][j / block_k] != 0 (and j <= i when causal).
+ * A row with no visible key gets the empty sum: O = 0, LSE = -inf.
+ *
+ * block_mask : device uint8 [mask_heads, ceil(N/block_q), ceil(N/block_k)],
+ *              shared by all batch entries; mask_heads = 1 (one mask for all
+ *              heads) or H (head h uses block_mask[h]).
+ * block_q, block_k : powers of two in [32, 1024] (FA_ERR_ARG otherwise).
+ * N <= 262144 (FA_ERR_SHAPE otherwise); bf16 only.  Other arguments as fa_fwd.
+ */
+int fa_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                        int B, int H, int N, int d, float tau, int causal,
+                        const unsigned char* block_mask, int mask_heads, int block_q,
+                        int block_k, int dtype, void* stream);
 
 /*
  * fa_decode_workspace_bytes - workspace that fa_decode needs.
@@ -266,6 +288,19 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
                    int B, int H, int N, int d, float tau, int causal, float p_drop,
                    unsigned long long seed, unsigned int offset,
                    void* workspace, size_t workspace_bytes, int dtype, void* stream);
+
+/*
+ * fa_bwd_block_sparse - backward of fa_fwd_block_sparse (same mask and block
+ * sizes; o and lse from that forward).  Query and key tiles holding no set
+ * block are skipped; rows with no visible key receive zero gradient.
+ * Arguments as fa_bwd plus the block mask.
+ */
+int fa_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                        int B, int H, int N, int d, float tau, int causal,
+                        const unsigned char* block_mask, int mask_heads, int block_q,
+                        int block_k, void* workspace, size_t workspace_bytes, int dtype,
+                        void* stream);
 
 /*
  * fa_bwd_stage - enqueue one of fa_bwd's three kernels.

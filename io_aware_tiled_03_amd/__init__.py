@@ -34,6 +34,8 @@ SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _P]),
     "fa_fwd_window": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _I, _I, _P]),
     "fa_fwd_dropout": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _F, _U64, _U32, _I, _P]),
+    "fa_fwd_block_sparse": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P, _I, _I, _I, _I,
+                                 _P]),
     "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "fa_decode_num_splits": (_I, [_I, _I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _I, _P, _Z, _I, _P]),
@@ -49,6 +51,8 @@ SIGNATURES = {
                            _I, _P]),
     "fa_bwd_dropout": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _F, _U64,
                             _U32, _P, _Z, _I, _P]),
+    "fa_bwd_block_sparse": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P,
+                                 _I, _I, _I, _P, _Z, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
 }
 
@@ -102,12 +106,24 @@ def _need(t, name):
         raise ValueError("%s must be contiguous" % name)
 
 
-def fwd(q, k, v, tau=None, causal=False, o=None, lse=None, window=None, sinks=0, dropout=None):
+def _block_args(block_mask, block_size, H):
+    import torch
+    _need(block_mask, "block_mask")
+    if block_mask.dtype != torch.uint8 or block_mask.dim() != 3:
+        raise TypeError("block_mask must be a uint8 tensor [mask_heads, nbq, nbk]")
+    bq, bk = block_size
+    return block_mask.data_ptr(), int(block_mask.shape[0]), int(bq), int(bk)
+
+
+def fwd(q, k, v, tau=None, causal=False, o=None, lse=None, window=None, sinks=0, dropout=None,
+        block_mask=None, block_size=(128, 128)):
     """O = softmax(tau Q K^T [+causal mask]) V and LSE, via fa_fwd.
 
     With window (causal only): the causal mask restricted to the `window` most
     recent keys plus the first `sinks` keys, via fa_fwd_window.
-    With dropout = (p, seed, offset): dropout on P, via fa_fwd_dropout."""
+    With dropout = (p, seed, offset): dropout on P, via fa_fwd_dropout.
+    With block_mask (uint8 [1 or H, ceil(N/bq), ceil(N/bk)], block_size = (bq, bk)):
+    block-sparse attention, via fa_fwd_block_sparse."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         _need(t, n)
@@ -115,6 +131,15 @@ def fwd(q, k, v, tau=None, causal=False, o=None, lse=None, window=None, sinks=0,
     tau = 1.0 / math.sqrt(d) if tau is None else float(tau)
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    if block_mask is not None:
+        if window is not None or dropout is not None:
+            raise ValueError("block-sparse attention takes no window and no dropout")
+        st = lib().fa_fwd_block_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                       lse.data_ptr(), B, H, N, d, tau, int(bool(causal)),
+                                       *_block_args(block_mask, block_size, H), _dtype_code(q),
+                                       _stream(q))
+        check("fa_fwd_block_sparse", st)
+        return o, lse
     if dropout is not None:
         if window is not None:
             raise ValueError("dropout is supported with no mask or the causal mask")
@@ -213,12 +238,13 @@ def bwd_workspace_bytes(B, H, N):
 
 
 def bwd(q, k, v, o, lse, do, tau=None, causal=False, dq=None, dk=None, dv=None, workspace=None,
-        stage=None, window=None, sinks=0, dropout=None):
+        stage=None, window=None, sinks=0, dropout=None, block_mask=None, block_size=(128, 128)):
     """dQ, dK, dV of fa_fwd's output given dO, via fa_bwd (workspace holds D on return).
 
     With stage in (0, 1, 2) only that kernel is enqueued, via fa_bwd_stage.  With
     window (causal only): the backward of the sliding-window forward, via fa_bwd_window.
-    With dropout = (p, seed, offset): the backward of fa_fwd_dropout, via fa_bwd_dropout."""
+    With dropout = (p, seed, offset): the backward of fa_fwd_dropout, via fa_bwd_dropout.
+    With block_mask: the backward of fa_fwd_block_sparse, via fa_bwd_block_sparse."""
     import torch
     for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (do, "do")):
         _need(t, n)
@@ -234,7 +260,12 @@ def bwd(q, k, v, o, lse, do, tau=None, causal=False, dq=None, dk=None, dv=None, 
             do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, tau,
             int(bool(causal)), workspace.data_ptr(),
             workspace.numel() * workspace.element_size(), _dtype_code(q), _stream(q))
-    if dropout is not None:
+    if block_mask is not None:
+        if window is not None or dropout is not None or stage is not None:
+            raise ValueError("block-sparse backward: no window, no dropout, whole backward only")
+        bargs = args[:15] + _block_args(block_mask, block_size, H) + args[15:]
+        check("fa_bwd_block_sparse", lib().fa_bwd_block_sparse(*bargs))
+    elif dropout is not None:
         if window is not None or stage is not None:
             raise ValueError("dropout backward: no window, whole backward only")
         p, seed, offset = dropout

@@ -99,6 +99,46 @@ int fa_fwd_dropout(const void* q, const void* k, const void* v, void* o, float* 
     return after_launch();
 }
 
+// Block-sparse arguments: fills bs or returns the status to report.
+static int block_sparse_args(const unsigned char* mask, int mask_heads, int block_q, int block_k,
+                             int H, int N, fa::BlockSparse* bs) {
+    if (!mask) return FA_ERR_NULL;
+    auto pow2 = [](int x) { return x >= 32 && x <= 1024 && (x & (x - 1)) == 0; };
+    if (!pow2(block_q) || !pow2(block_k)) return FA_ERR_ARG;
+    if (mask_heads != 1 && mask_heads != H) return FA_ERR_SHAPE;
+    if (N > 64 * fa::kMaxSparseTiles) return FA_ERR_SHAPE;   // tile lists live in LDS
+    bs->mask = mask;
+    bs->nbq = (N + block_q - 1) / block_q;
+    bs->nbk = (N + block_k - 1) / block_k;
+    bs->lgbq = __builtin_ctz((unsigned)block_q);
+    bs->lgbk = __builtin_ctz((unsigned)block_k);
+    bs->heads = mask_heads;
+    bs->H = H;
+    return FA_OK;
+}
+
+int fa_fwd_block_sparse(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                        int H, int N, int d, float tau, int causal, const unsigned char* block_mask,
+                        int mask_heads, int block_q, int block_k, int dtype, void* stream) {
+    if (!q || !k || !v || !o || !lse) return FA_ERR_NULL;
+    int st = check_common(B, H, N, d, tau, dtype);
+    if (st != FA_OK) return st;
+    if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
+    if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    fa::BlockSparse bs;
+    st = block_sparse_args(block_mask, mask_heads, block_q, block_k, H, N, &bs);
+    if (st != FA_OK) return st;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse))
+        return FA_ERR_ALIGN;
+    const long long bh = (long long)B * H;
+    if (!grid_ok(bh * ((N + 63) / 64), 256)) return FA_ERR_SHAPE;
+    fa::FwdArgs a{q, k, v, o, lse, B, H, N, d, tau, causal, dtype};
+    a.blk = bs;
+    (void)hipGetLastError();
+    fa::launch_fwd(a, (hipStream_t)stream);
+    return after_launch();
+}
+
 int fa_decode_num_splits(int B, int H, int N_max, int d, int num_splits) {
     if (B < 1 || H < 1 || N_max < 1 || N_max > (1 << 20) || (d != 64 && d != 128)) return 0;
     if (num_splits < 0 || num_splits > 1024) return 0;
@@ -203,7 +243,8 @@ int bwd_common(int stages, const void* q, const void* k, const void* v, const vo
                const float* lse, const void* dout, void* dq, void* dk, void* dv, int B, int H,
                int N, int d, float tau, int causal, void* workspace, size_t workspace_bytes,
                int dtype, void* stream, int window = 0, int sinks = 0, int drop_thr = 0,
-               unsigned long long seed = 0, unsigned int offset = 0) {
+               unsigned long long seed = 0, unsigned int offset = 0,
+               const fa::BlockSparse* bs = nullptr) {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
     int st = check_common(B, H, N, d, tau, dtype);
     if (st != FA_OK) return st;
@@ -224,6 +265,7 @@ int bwd_common(int stages, const void* q, const void* k, const void* v, const vo
     a.drop_thr = drop_thr;
     a.seed = seed;
     a.offset = offset;
+    if (bs) a.blk = *bs;
     (void)hipGetLastError();
     fa::launch_bwd(a, stages, (hipStream_t)stream);
     return after_launch();
@@ -258,6 +300,18 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
                       workspace_bytes, dtype, stream, 0, 0, thr, seed, offset);
 }
 
+int fa_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o,
+                        const float* lse, const void* dout, void* dq, void* dk, void* dv, int B,
+                        int H, int N, int d, float tau, int causal,
+                        const unsigned char* block_mask, int mask_heads, int block_q, int block_k,
+                        void* workspace, size_t workspace_bytes, int dtype, void* stream) {
+    fa::BlockSparse bs;
+    const int st = block_sparse_args(block_mask, mask_heads, block_q, block_k, H, N, &bs);
+    if (st != FA_OK) return st;
+    return bwd_common(7, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, tau, causal, workspace,
+                      workspace_bytes, dtype, stream, 0, 0, 0, 0, 0, &bs);
+}
+
 int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
                  const float* lse, const void* dout, void* dq, void* dk, void* dv, int B, int H,
                  int N, int d, float tau, int causal, void* workspace, size_t workspace_bytes,
@@ -278,7 +332,8 @@ const char* fa_status_string(int status) {
         case FA_ERR_ALIGN: return "a pointer is not aligned (16 bytes for tensors)";
         case FA_ERR_ARG:
             return "bad argument value (tau finite and > 0, num_splits 0..1024, window >= 1, "
-                   "sinks >= 0, stage 0..2, dropout probability in [0, 255/256])";
+                   "sinks >= 0, stage 0..2, dropout probability in [0, 255/256], block sizes "
+                   "powers of two in [32, 1024])";
         default: return "unknown status";
     }
 }

@@ -89,7 +89,7 @@ struct TileCopy {
 
 // Mask modes: none, causal, causal with a sliding window and sink tokens
 // (key j visible to query i iff j <= i and (i - j < window or j < sinks)).
-enum : int { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2 };
+enum : int { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2, kMaskBlock = 3, kMaskBlockCausal = 4 };
 
 // DROP: the forward dropped P with the mask of Dropout::block; with
 // Z = keep / (1 - p): dV = (P o Z)^T dO and dS = P o (Z o dP - D).
@@ -98,8 +98,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int N, float scale_log2,
-    float tau, int window, int sinks, Dropout drop) {
-    constexpr bool CAUSAL = MODE != kMaskNone, WIN = MODE == kMaskWindow;
+    float tau, int window, int sinks, Dropout drop, BlockSparse bs) {
+    constexpr bool CAUSAL = MODE == kMaskCausal || MODE == kMaskWindow || MODE == kMaskBlockCausal;
+    constexpr bool WIN = MODE == kMaskWindow, BLK = MODE >= kMaskBlock;
     constexpr int BC = 128, BR = 64;
     constexpr int STR = D + 8;                 // padded row (16 * odd bytes)
     // Double buffers as distinct LDS variables picked at compile time, so that
@@ -109,6 +110,10 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     __shared__ __attribute__((aligned(16))) uint16_t sdO0[BR * STR], sdO1[BR * STR];
     __shared__ __attribute__((aligned(16))) float sL0[BR], sL1[BR];
     __shared__ __attribute__((aligned(16))) float sD0[BR], sD1[BR];
+    // block-sparse: the workgroup's active query tiles, in order
+    __shared__ uint16_t s_list[BLK ? kMaxSparseTiles : 1];
+    __shared__ uint64_t s_bal[BLK ? kMaxSparseTiles / 64 : 1];
+    __shared__ int s_off[BLK ? kMaxSparseTiles / 64 + 1 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
@@ -162,6 +167,15 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         else if (tid < 2 * BR) (B1 ? sD1 : sD0)[tid - BR] = ld_d;
     };
 
+    // Block-sparse: this wave's key block (waves hold 32 keys, blocks >= 32)
+    // and the bit of the query block holding row q.
+    const unsigned char* bmcol = nullptr;
+    if constexpr (BLK) {
+        const int head = bs.heads > 1 ? bh % bs.H : 0;
+        bmcol = bs.mask + (size_t)head * bs.nbq * bs.nbk + (min(kw, N - 1) >> bs.lgbk);
+    }
+    auto block_bit = [&](int q) { return bmcol[(size_t)min(q >> bs.lgbq, bs.nbq - 1) * bs.nbk] != 0; };
+
     auto compute = [&](auto bufc, int q0, auto maskc) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(maskc)::value != 0;
         constexpr bool B1 = decltype(bufc)::value != 0;
@@ -174,6 +188,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
             const int qs = q0 + qb * 32;
             if (MASK && CAUSAL && qs + 31 < kw) continue;   // all these queries precede the keys
             if (MASK && WIN && qs - (kw + 31) >= window && kw >= sinks) continue;   // all past the window
+            if (BLK && !block_bit(qs)) continue;   // the 32 x 32 block is clear
             u32x4 qa[D / 16], oa[D / 16];
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks) {
@@ -242,12 +257,6 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         }
     };
 
-    if (qt0 < n_qt) {
-        stage(qt0, ic<0>{});
-        stage_ld(ic<0>{});
-        wait_vmem();
-        __syncthreads();
-    }
     // query tiles that reach into this workgroup's keys need the causal mask
     const int qmask_end = CAUSAL ? min(n_qt, (k0 + BC + BR - 1) / BR) : qt0;
     // Under a window: no query past the last key's window sees the tile
@@ -259,30 +268,59 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         qwin = max(0, (k0 + window - BR + 1 + BR - 1) / BR);
     }
     const int qu_end = max(qmask_end, min(qwin, qt_end));   // end of the unmasked query tiles
-    auto tile_b = [&](int qt, auto bufc, auto maskc) __attribute__((always_inline)) {   // query tile qt lives in buffer bufc
+    // Query tiles are visited as positions p = 0, 1, ...: tile qt0 + p, or
+    // under a block mask the p-th listed active tile; position p lives in
+    // buffer p % 2.
+    int npos = qt_end - qt0, pm1 = qmask_end - qt0, pu = max(pm1, qu_end - qt0);
+    if constexpr (BLK) {
+        const int head = bs.heads > 1 ? bh % bs.H : 0;
+        const unsigned char* mh = bs.mask + (size_t)head * bs.nbq * bs.nbk;
+        const int kb0 = k0 >> bs.lgbk, kb1 = (min(k0 + BC, N) - 1) >> bs.lgbk;
+        auto active = [&](int t) {
+            if (CAUSAL && t < qt0) return false;
+            const int rb0 = (t * BR) >> bs.lgbq, rb1 = min((t * BR + BR - 1) >> bs.lgbq, bs.nbq - 1);
+            bool act = false;
+            for (int rb = rb0; rb <= rb1; ++rb)
+                for (int kb = kb0; kb <= kb1; ++kb) act |= mh[(size_t)rb * bs.nbk + kb] != 0;
+            return act;
+        };
+        npos = build_tile_list<4>(active, n_qt, s_list, s_bal, s_off, wave, lane, tid);
+        pm1 = pu = 0;   // every listed tile runs the masked body
+    }
+    auto qt_at = [&](int p) {
+        if constexpr (BLK) return (int)s_list[min(p, max(npos - 1, 0))];
+        return qt0 + p;
+    };
+    if (npos > 0) {
+        stage(qt_at(0), ic<0>{});
+        stage_ld(ic<0>{});
+        wait_vmem();
+        __syncthreads();
+    }
+    auto tile_b = [&](int p, auto bufc, auto maskc) __attribute__((always_inline)) {   // position p lives in buffer bufc
         constexpr ic<1 - decltype(bufc)::value> other{};
-        if (qt + 1 < qt_end) stage(qt + 1, other);
-        const int q0 = qt * BR;
+        if (p + 1 < npos) stage(qt_at(p + 1), other);
+        const int q0 = qt_at(p) * BR;
         if (!(CAUSAL && q0 + BR - 1 < kw) && !(WIN && q0 - (kw + 31) >= window && kw >= sinks))
             compute(bufc, q0, maskc);
-        if (qt + 1 < qt_end) stage_ld(other);
+        if (p + 1 < npos) stage_ld(other);
         wait_vmem();
         __syncthreads();
     };
-    // Query tiles [tb, te), tile qt in buffer (qt - qt0) % 2: an odd first
-    // tile alone, then pairs, then an even last tile (buffers fixed at compile time).
-    auto phase = [&](int tb, int te, auto maskc) __attribute__((always_inline)) {
-        int qt = tb;
-        if (qt < te && ((qt - qt0) & 1)) { tile_b(qt, ic<1>{}, maskc); ++qt; }
-        for (; qt + 1 < te; qt += 2) {
-            tile_b(qt, ic<0>{}, maskc);
-            tile_b(qt + 1, ic<1>{}, maskc);
+    // Positions [pb, pe), position p in buffer p % 2: an odd first position
+    // alone, then pairs, then an even last one (buffers fixed at compile time).
+    auto phase = [&](int pb, int pe, auto maskc) __attribute__((always_inline)) {
+        int p = pb;
+        if (p < pe && (p & 1)) { tile_b(p, ic<1>{}, maskc); ++p; }
+        for (; p + 1 < pe; p += 2) {
+            tile_b(p, ic<0>{}, maskc);
+            tile_b(p + 1, ic<1>{}, maskc);
         }
-        if (qt < te) tile_b(qt, ic<0>{}, maskc);
+        if (p < pe) tile_b(p, ic<0>{}, maskc);
     };
-    phase(qt0, qmask_end, ic<1>{});
-    phase(max(qt0, qmask_end), qu_end, ic<0>{});
-    phase(max(qt0, qu_end), qt_end, ic<1>{});
+    phase(0, pm1, ic<1>{});
+    phase(max(0, pm1), pu, ic<0>{});
+    phase(max(0, pu), npos, ic<1>{});
 
     if (key < N) {
         uint16_t* dkr = dK + base + (size_t)key * D;
@@ -309,12 +347,17 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
     uint16_t* __restrict__ dQ, int BH, int N, float scale_log2, float tau, int n_qtiles, int window,
-    int sinks, Dropout drop) {
-    constexpr bool CAUSAL = MODE != kMaskNone, WIN = MODE == kMaskWindow;
+    int sinks, Dropout drop, BlockSparse bs) {
+    constexpr bool CAUSAL = MODE == kMaskCausal || MODE == kMaskWindow || MODE == kMaskBlockCausal;
+    constexpr bool WIN = MODE == kMaskWindow, BLK = MODE >= kMaskBlock;
     constexpr int BR = 128, BC = 64;
     constexpr int STR = D + 8;
     __shared__ __attribute__((aligned(16))) uint16_t sK0[BC * STR], sK1[BC * STR];
     __shared__ __attribute__((aligned(16))) uint16_t sV0[BC * STR], sV1[BC * STR];
+    // block-sparse: the workgroup's active key tiles, in order
+    __shared__ uint16_t s_list[BLK ? kMaxSparseTiles : 1];
+    __shared__ uint64_t s_bal[BLK ? kMaxSparseTiles / 64 : 1];
+    __shared__ int s_off[BLK ? kMaxSparseTiles / 64 + 1 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
@@ -352,12 +395,22 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
     // Keys past N are zero rows (buffer descriptor), so their dS meets K = 0
     // in dQ += dS K and needs no mask; only the causal diagonal is masked.
+    // Block-sparse: the mask row of this wave's query block (waves hold 32
+    // rows, blocks >= 32) and the bit of the key block holding key j.
+    const unsigned char* bmrow = nullptr;
+    if constexpr (BLK) {
+        const int head = bs.heads > 1 ? bh % bs.H : 0;
+        bmrow = bs.mask + ((size_t)head * bs.nbq + (min(qw, N - 1) >> bs.lgbq)) * bs.nbk;
+    }
+    auto block_bit = [&](int j) { return bmrow[min(j >> bs.lgbk, bs.nbk - 1)] != 0; };
+
     auto compute = [&](auto bufc, int k0, auto maskc) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(maskc)::value != 0;
         const uint16_t* k_lds = decltype(bufc)::value ? sK1 : sK0;
         const uint16_t* v_lds = decltype(bufc)::value ? sV1 : sV0;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
+            if (BLK && !block_bit(k0 + 32 * kb)) continue;   // the 32 x 32 block is clear
             u32x4 ka[D / 16], va[D / 16];
 #pragma unroll
             for (int ks = 0; ks < D / 16; ++ks) {
@@ -423,14 +476,35 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         tfull = max(tlo, (max(lo_max, 0) + BC - 1) / BC);
         nsk = min((sinks + BC - 1) / BC, tlo);
     }
-    auto tile_at = [&](int p) { return p < nsk ? p : tlo + (p - nsk); };
+    // Block-sparse: the workgroup's active key tiles in LDS.
+    int nact = 0;
+    if constexpr (BLK) {
+        const int head = bs.heads > 1 ? bh % bs.H : 0;
+        const unsigned char* mh = bs.mask + (size_t)head * bs.nbq * bs.nbk;
+        const int rb0 = q0 >> bs.lgbq, rb1 = (min(q0 + BR, N) - 1) >> bs.lgbq;
+        auto active = [&](int t) {
+            const int kb0 = (t * BC) >> bs.lgbk, kb1 = min((t * BC + BC - 1) >> bs.lgbk, bs.nbk - 1);
+            bool act = false;
+            for (int rb = rb0; rb <= rb1; ++rb)
+                for (int kb = kb0; kb <= kb1; ++kb) act |= mh[(size_t)rb * bs.nbk + kb] != 0;
+            return act;
+        };
+        nact = build_tile_list<4>(active, ntiles, s_list, s_bal, s_off, wave, lane, tid);
+    }
+    auto tile_at = [&](int p) {
+        if constexpr (BLK) return (int)s_list[min(p, max(nact - 1, 0))];
+        return p < nsk ? p : tlo + (p - nsk);
+    };
     // tiles in [tfull, tdiag) precede every query of the workgroup and lie
     // inside every row's window: no mask
     const int jsplit = CAUSAL ? min(ntiles, q0 / BC) : ntiles;
     const int tdiag = max(tfull, jsplit);
-    const int p1 = nsk + (tfull - tlo), p2 = nsk + (tdiag - tlo), p3 = nsk + (ntiles - tlo);
-    cp.issue(krs, tile_at(0) * BC, sK0, wave);
-    cp.issue(vrs, tile_at(0) * BC, sV0, wave);
+    int p1 = nsk + (tfull - tlo), p2 = nsk + (tdiag - tlo), p3 = nsk + (ntiles - tlo);
+    if constexpr (BLK) p1 = p2 = 0, p3 = nact;   // every listed tile masked
+    if (p3 > 0) {
+        cp.issue(krs, tile_at(0) * BC, sK0, wave);
+        cp.issue(vrs, tile_at(0) * BC, sV0, wave);
+    }
     wait_vmem();
     __syncthreads();
     auto tile_b = [&](int p, auto bufc, auto maskc) __attribute__((always_inline)) {   // position p lives in buffer bufc
@@ -443,7 +517,8 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         const int k0 = tile_at(p) * BC;
         if constexpr (decltype(maskc)::value != 0) {
             const bool sees = !(CAUSAL && k0 > qw + 31) &&
-                              !(WIN && k0 + BC - 1 < qw - window + 1 && k0 >= sinks);
+                              !(WIN && k0 + BC - 1 < qw - window + 1 && k0 >= sinks) &&
+                              !(BLK && !block_bit(k0) && !block_bit(k0 + 32));
             if (sees) compute(bufc, k0, maskc);
         } else {
             compute(bufc, k0, maskc);
@@ -500,20 +575,23 @@ void launch(const BwdArgs& a, int stages, hipStream_t st) {
         hipLaunchKernelGGL((bwd_dkdv_kernel<D, MODE, DROP>), dim3(nk * bh), dim3(256), 0, st,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                            (const uint16_t*)a.dout, a.lse, a.D, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                           bh, a.N, a.tau * kLog2e, a.tau, a.window, a.sinks, drop);
+                           bh, a.N, a.tau * kLog2e, a.tau, a.window, a.sinks, drop, a.blk);
     }
     if (stages & 4) {
         const int nq = (a.N + 127) / 128;
         hipLaunchKernelGGL((bwd_dq_kernel<D, MODE, DROP>), dim3(nq * bh), dim3(256), 0, st,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                            (const uint16_t*)a.dout, a.lse, a.D, (uint16_t*)a.dq, bh, a.N,
-                           a.tau * kLog2e, a.tau, nq, a.window, a.sinks, drop);
+                           a.tau * kLog2e, a.tau, nq, a.window, a.sinks, drop, a.blk);
     }
 }
 
 template <int D>
 void launch_d(const BwdArgs& a, int stages, hipStream_t st) {
-    if (a.drop_thr > 0) {   // dropout: with no mask or the plain causal mask
+    if (a.blk.mask) {       // block-sparse (no window, no dropout)
+        a.causal ? launch<D, kMaskBlockCausal, false>(a, stages, st)
+                 : launch<D, kMaskBlock, false>(a, stages, st);
+    } else if (a.drop_thr > 0) {   // dropout: with no mask or the plain causal mask
         a.causal ? launch<D, kMaskCausal, true>(a, stages, st)
                  : launch<D, kMaskNone, true>(a, stages, st);
     } else if (!a.causal) {

@@ -206,6 +206,44 @@ struct Dropout {
     }
 };
 
+// Block-sparse tile lists: writes to list[] (LDS), in increasing order, the
+// tiles t < ntiles for which active(t) holds, and returns how many there are.
+// Waves ballot chunks of 64 tiles, one thread places the chunks by a prefix
+// sum, then every wave writes its tiles.  bal and off are LDS scratch of
+// ceil(ntiles / 64) and ceil(ntiles / 64) + 1 entries.  Every thread of the
+// workgroup must call it (it synchronises the workgroup).
+template <int NW, typename F>
+__device__ __forceinline__ int build_tile_list(F active, int ntiles, uint16_t* list, uint64_t* bal,
+                                               int* off, int wave, int lane, int tid) {
+    const int nchunks = (ntiles + 63) / 64;
+    for (int c = wave; c < nchunks; c += NW) {
+        const int t = 64 * c + lane;
+        const bool act = t < ntiles && active(t);
+        const uint64_t b = __builtin_amdgcn_ballot_w64(act);
+        if (lane == 0) bal[c] = b;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        int acc = 0;
+        for (int c = 0; c < nchunks; ++c) {
+            off[c] = acc;
+            acc += __builtin_popcountll(bal[c]);
+        }
+        off[nchunks] = acc;
+    }
+    __syncthreads();
+    for (int c = wave; c < nchunks; c += NW) {
+        const uint64_t b = bal[c];
+        if ((b >> lane) & 1)
+            list[off[c] + __builtin_amdgcn_mbcnt_hi((uint32_t)(b >> 32),
+                                                    __builtin_amdgcn_mbcnt_lo((uint32_t)b, 0u))] =
+                (uint16_t)(64 * c + lane);
+    }
+    const int n = off[nchunks];
+    __syncthreads();
+    return n;
+}
+
 // Direct global -> LDS copy of 16 bytes per lane: lane i's bytes land at
 // lds_base + 16*i (lds_base must be the same for the whole wave).  Completion
 // is tracked by vmcnt, not by any register: wait with wait_vmem() before a

@@ -80,8 +80,9 @@ __device__ __forceinline__ void prio_lo() {
 
 template <int N_> using ic = std::integral_constant<int, N_>;
 
-// Mask modes of the bf16 forward.
-enum : int { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2 };
+// Mask modes of the bf16 forward (kMaskBlock*: block-sparse, without or with
+// the causal mask).
+enum : int { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2, kMaskBlock = 3, kMaskBlockCausal = 4 };
 
 // BC keys per tile, NW waves per workgroup (32 query rows each); MODE is one
 // of the mask modes (kMaskWindow: causal with a sliding window and sinks).
@@ -91,8 +92,11 @@ template <int D, int MODE, int BC, int NW, bool DROP>
 __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, float* __restrict__ LSE, int BH, int N, float scale_log2, float tau,
-    int n_qtiles, int window, int sinks, Dropout drop) {
-    constexpr bool CAUSAL = MODE != kMaskNone, WIN = MODE == kMaskWindow;
+    int n_qtiles, int window, int sinks, Dropout drop, BlockSparse bs) {
+    constexpr bool CAUSAL = MODE == kMaskCausal || MODE == kMaskWindow || MODE == kMaskBlockCausal;
+    constexpr bool WIN = MODE == kMaskWindow, BLK = MODE >= kMaskBlock;
+    // rows that may meet tiles before their first visible key (-inf guards)
+    constexpr bool SPARSE_ROWS = WIN || BLK;
     constexpr int BR = 32 * NW, NKB = BC / 32;
     constexpr int KCH = D / 8;             // 16-byte chunks per row
     constexpr int KSTR = D + FA_FWD_KPAD;  // K row stride (elements), padded against bank conflicts
@@ -105,6 +109,10 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
     // tile's load with this tile's compute.)
     __shared__ __attribute__((aligned(16))) uint16_t sK0[BC * KSTR], sK1[BC * KSTR];
     __shared__ __attribute__((aligned(16))) uint16_t sV0[BC * VSTR], sV1[BC * VSTR];
+    // block-sparse: the workgroup's active key tiles, in order
+    __shared__ uint16_t s_list[BLK ? kMaxSparseTiles : 1];
+    __shared__ uint64_t s_bal[BLK ? kMaxSparseTiles / 64 : 1];
+    __shared__ int s_off[BLK ? kMaxSparseTiles / 64 + 1 : 1];
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
@@ -169,6 +177,15 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
         for (int t = 0; t < VPW; ++t)
             if (wave + NW * t < VNI) buf_ld16_lds(vrs, vgo[t] + t0, &sv[(wave + NW * t) * 512]);
     };
+    // Block-sparse: the mask row of this wave's query block (waves hold 32
+    // rows and blocks are at least 32 rows, so one row per wave).
+    const unsigned char* bmrow = nullptr;
+    if constexpr (BLK) {
+        const int head = bs.heads > 1 ? bh % bs.H : 0;
+        bmrow = bs.mask + ((size_t)head * bs.nbq + (min(qw, N - 1) >> bs.lgbq)) * bs.nbk;
+    }
+    auto block_bit = [&](int key) { return bmrow[min(key >> bs.lgbk, bs.nbk - 1)] != 0; };
+
     // Per-lane offsets of the operand reads.  K: physical row kb*32 + ln.
     // V (transposing read): lane s of 16-lane group G reads key 8*(G/2) + s/4
     // (+4 for slots 4..7), columns 16*(G%2) + 4*(s%4).
@@ -182,6 +199,11 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
         constexpr bool MASK = decltype(maskc)::value != 0;
         const uint16_t* const sk = decltype(bufc)::value ? sK1 : sK0;
         const uint16_t* const sv = decltype(bufc)::value ? sV1 : sV0;
+        bool bbit[NKB];   // block-sparse: the wave's bit for each 32-key block
+        if constexpr (BLK) {
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) bbit[kb] = block_bit(k0 + 32 * kb);
+        }
         f32x16 s[NKB];
         prio_hi();
 #pragma unroll
@@ -201,7 +223,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
                 for (int r = 0; r < 16; ++r) {
                     const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7);
                     if (key >= N ||
-                        (CAUSAL && (key > qrow || (WIN && qrow - key >= window && key >= sinks))))
+                        (CAUSAL && (key > qrow || (WIN && qrow - key >= window && key >= sinks))) ||
+                        (BLK && !bbit[kb]))
                         s[kb][r] = neg_inf();
                 }
         }
@@ -216,9 +239,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
         const bool grow = (mx - m) * scale_log2 > FA_FWD_RESCALE_LOG2;
         if (__builtin_amdgcn_ballot_w64(grow) != 0) {
             const float mnew = fmaxf(m, mx);
-            // under a window a row may have seen no visible key yet (m = mnew
-            // = -inf, l and O still zero): keep it as it is
-            const float alpha = (WIN && m == mnew) ? 1.f : fast_exp2((m - mnew) * scale_log2);
+            // under a window or a block mask a row may have seen no visible key
+            // yet (m = mnew = -inf, l and O still zero): keep it as it is
+            const float alpha = (SPARSE_ROWS && m == mnew) ? 1.f : fast_exp2((m - mnew) * scale_log2);
             l *= alpha;
 #pragma unroll
             for (int db = 0; db < D / 32; ++db)
@@ -228,7 +251,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
         }
         // a row with no visible key so far keeps m = -inf; its scores are all
         // -inf as well, so any finite reference gives p = 0
-        const float mc = (WIN && MASK && m == neg_inf()) ? 0.f : m * scale_log2;
+        const float mc = (SPARSE_ROWS && MASK && m == neg_inf()) ? 0.f : m * scale_log2;
         u32x4 pf[NKB][2];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -285,9 +308,36 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
         tfull = max(tlo, (max(lo_max, 0) + BC - 1) / BC);   // first tile inside every row's window
         nsk = min((sinks + BC - 1) / BC, tlo);              // sink tiles below the window
     }
-    auto tile_at = [&](int p) { return p < nsk ? p : tlo + (p - nsk); };
+    // Block-sparse: list the workgroup's active key tiles (those holding a
+    // set block for one of its query blocks) in LDS, in order.  Pass 1 ballots
+    // tiles in chunks of 64 per wave, a prefix sum places the chunks, pass 2
+    // writes the tile numbers.
+    int nact = 0;
+    if constexpr (BLK) {
+        const int head = bs.heads > 1 ? bh % bs.H : 0;
+        const unsigned char* mh = bs.mask + (size_t)head * bs.nbq * bs.nbk;
+        const int rb0 = q0 >> bs.lgbq, rb1 = (min(q0 + BR, N) - 1) >> bs.lgbq;
+        auto active = [&](int t) {
+            const int kb0 = (t * BC) >> bs.lgbk, kb1 = min((t * BC + BC - 1) >> bs.lgbk, bs.nbk - 1);
+            bool act = false;
+            for (int rb = rb0; rb <= rb1; ++rb)
+                for (int kb = kb0; kb <= kb1; ++kb) act |= mh[(size_t)rb * bs.nbk + kb] != 0;
+            return act;
+        };
+        nact = build_tile_list<NW>(active, ntiles, s_list, s_bal, s_off, wave, lane, tid);
+    }
+    auto tile_at = [&](int p) {
+        if constexpr (BLK) return (int)s_list[min(p, max(nact - 1, 0))];
+        return p < nsk ? p : tlo + (p - nsk);
+    };
     // Whether any row of this wave sees a key of the tile at k0.
     auto wave_sees = [&](int k0) {
+        if constexpr (BLK) {
+            bool any = false;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) any |= block_bit(k0 + 32 * kb);
+            if (!any) return false;
+        }
         if constexpr (!CAUSAL) return true;
         if constexpr (!WIN) return k0 <= qw + 31;
         return k0 <= qw + 31 && (k0 + BC - 1 >= qw - window + 1 || k0 < sinks);
@@ -320,8 +370,9 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
     // window.  The others (sinks, window edge, diagonal, sequence end) are masked.
     const int jsplit = min(CAUSAL ? q0 / BC : ntiles, nfull);
     const int tdiag = max(tfull, jsplit);
-    const int p1 = nsk + (tfull - tlo), p2 = nsk + (tdiag - tlo), p3 = nsk + (ntiles - tlo);
-    stage(tile_at(0), ic<0>{});
+    int p1 = nsk + (tfull - tlo), p2 = nsk + (tdiag - tlo), p3 = nsk + (ntiles - tlo);
+    if constexpr (BLK) p1 = p2 = 0, p3 = nact;   // block-sparse: every listed tile masked
+    if (p3 > 0) stage(tile_at(0), ic<0>{});
     wait_vmem();
     __syncthreads();
     phase(0, p1, ic<1>{});
@@ -329,7 +380,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
     phase(p2, p3, ic<1>{});
 
     l += xor32(l);
-    const float inv = (DROP ? drop.scale : 1.f) / l;
+    // a row that saw no key (block-sparse) keeps the empty sum: O = 0, LSE = -inf
+    const float inv = (BLK && l == 0.f) ? 0.f : (DROP ? drop.scale : 1.f) / l;
     if (qrow < N) {
         uint16_t* orow = O + base + (size_t)qrow * D;
 #pragma unroll
@@ -342,7 +394,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
                 w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
                 *reinterpret_cast<u32x2*>(orow + d) = w;
             }
-        if (hf == 0) LSE[(size_t)bh * N + qrow] = m * tau + __logf(l);
+        if (hf == 0)
+            LSE[(size_t)bh * N + qrow] = (BLK && l == 0.f) ? neg_inf() : m * tau + __logf(l);
     }
 }
 
@@ -440,7 +493,7 @@ void launch_bf16(const FwdArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((fwd_bf16_kernel<D, MODE, BC, NW, DROP>), dim3(nq * bh), dim3(64 * NW), 0,
                        st, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.o, a.lse, bh, a.N, a.tau * kLog2e, a.tau, nq, a.window,
-                       a.sinks, make_dropout(a.drop_thr, a.seed, a.offset));
+                       a.sinks, make_dropout(a.drop_thr, a.seed, a.offset), a.blk);
 }
 
 template <int D, bool C>
@@ -456,7 +509,10 @@ void launch_f32(const FwdArgs& a, hipStream_t st) {
 template <int D>
 void launch_bf16_d(const FwdArgs& a, hipStream_t st) {
     const bool win = a.causal && (a.window < a.N || a.sinks > 0);
-    if (a.drop_thr > 0) {   // dropout: with no mask or the plain causal mask
+    if (a.blk.mask) {       // block-sparse (no window, no dropout)
+        a.causal ? launch_bf16<D, kMaskBlockCausal, false>(a, st)
+                 : launch_bf16<D, kMaskBlock, false>(a, st);
+    } else if (a.drop_thr > 0) {   // dropout: with no mask or the plain causal mask
         a.causal ? launch_bf16<D, kMaskCausal, true>(a, st) : launch_bf16<D, kMaskNone, true>(a, st);
     } else if (!a.causal) {
         launch_bf16<D, kMaskNone, false>(a, st);

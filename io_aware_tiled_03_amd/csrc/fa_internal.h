@@ -9,6 +9,16 @@ namespace fa {
 
 enum { kF32 = 0, kBF16 = 1 };
 
+// Largest number of key (or query) tiles a block-sparse workgroup lists in LDS.
+constexpr int kMaxSparseTiles = 4096;
+
+// Block-sparse attention: key j is visible to query i only if
+// mask[head][i >> lgbq][j >> lgbk] != 0 (head = h when heads == H, else 0).
+struct BlockSparse {
+    const unsigned char* mask = nullptr;   // [heads, nbq, nbk] uint8
+    int nbq = 0, nbk = 0, lgbq = 0, lgbk = 0, heads = 0, H = 1;
+};
+
 struct FwdArgs {
     const void *q, *k, *v;
     void* o;
@@ -21,6 +31,7 @@ struct FwdArgs {
     int drop_thr = 0;          // dropout: byte threshold round(256 p); 0 = no dropout
     unsigned long long seed = 0;
     unsigned int offset = 0;
+    BlockSparse blk;           // block-sparse when blk.mask != nullptr
 };
 void launch_fwd(const FwdArgs& a, hipStream_t st);
 
@@ -73,6 +84,7 @@ struct BwdArgs {
     int drop_thr = 0;
     unsigned long long seed = 0;
     unsigned int offset = 0;
+    BlockSparse blk;
 };
 // stages: bit 0 = D preprocess, bit 1 = dK/dV, bit 2 = dQ (launched in that order)
 void launch_bwd(const BwdArgs& a, int stages, hipStream_t st);

@@ -106,6 +106,28 @@ def test_dropout_rejects_bad_arguments():
     assert lib.fa_bwd_dropout(*bad) == 4
 
 
+def test_block_sparse_rejects_bad_arguments():
+    fa, lib = _lib()
+    f = [P, P, P, P, P, 1, 2, 256, 64, 0.125, 1, P, 1, 64, 64, 1, None]
+    bad = list(f); bad[11] = None
+    assert lib.fa_fwd_block_sparse(*bad) == 1
+    bad = list(f); bad[13] = 48
+    assert lib.fa_fwd_block_sparse(*bad) == 7     # not a power of two
+    bad = list(f); bad[14] = 16
+    assert lib.fa_fwd_block_sparse(*bad) == 7     # below 32
+    bad = list(f); bad[12] = 3
+    assert lib.fa_fwd_block_sparse(*bad) == 2     # mask heads neither 1 nor H
+    bad = list(f); bad[7] = 262145
+    assert lib.fa_fwd_block_sparse(*bad) == 2     # tile lists would overflow LDS
+    bad = list(f); bad[15] = 0
+    assert lib.fa_fwd_block_sparse(*bad) == 3     # bf16 only
+    b = [P, P, P, P, P, P, P, P, P, 1, 2, 256, 64, 0.125, 1, P, 1, 64, 64, P, 1 << 20, 1, None]
+    bad = list(b); bad[17] = 2048
+    assert lib.fa_bwd_block_sparse(*bad) == 7
+    bad = list(b); bad[19] = None
+    assert lib.fa_bwd_block_sparse(*bad) == 4
+
+
 def _dec(lib, **kw):
     a = dict(q=P, k=P, v=P, sl=P, B=2, H=2, N=100, d=128, tau=0.1, o=P, lse=P, ns=0, ws=P,
              wsb=1 << 30, dtype=1)

@@ -1,0 +1,158 @@
+"""GPU parity of block-sparse attention (fa_fwd_block_sparse,
+fa_bwd_block_sparse) against the float64 oracle."""
+import numpy as np
+import pytest
+
+import fa_inputs
+from oracle import attention as orc
+from tests.util import assert_close, rounding_allowance, to_device, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+def _mask(heads, N, bq, bk, density, seed, causal):
+    rng = np.random.default_rng(seed)
+    nbq, nbk = -(-N // bq), -(-N // bk)
+    m = (rng.random((heads, nbq, nbk)) < density).astype(np.uint8)
+    m[:, 0, 0] = 1
+    return m
+
+
+def _lse_close(got, ref, what):
+    """Equal -inf pattern (rows with no visible key), finite parts within the LSE bound."""
+    assert np.array_equal(np.isneginf(got), np.isneginf(ref)), what
+    live = np.isfinite(ref)
+    assert_close(got[live], ref[live], "bf16", what, kind="lse")
+
+
+def _run_fwd(x, tau, causal, mask, bq, bk):
+    import io_aware_tiled_03_amd as fa
+    import torch
+    q, k, v = (to_device(x[n]) for n in ("q", "k", "v"))
+    o, lse = fa.fwd(q, k, v, tau=tau, causal=causal, block_mask=torch.from_numpy(mask).cuda(),
+                    block_size=(bq, bk))
+    return to_f64(o), to_f64(lse)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("bq,bk", [(32, 32), (64, 128), (128, 64), (256, 32)])
+@pytest.mark.parametrize("N,density", [(100, 0.5), (257, 0.3), (1000, 0.6)])
+def test_block_sparse_fwd_small(N, density, bq, bk, causal, d):
+    B, H = 2, 2
+    x = fa_inputs.dense_inputs(B, H, N, d, "bf16", 20000 + N + bq + bk)
+    tau = 1.0 / np.sqrt(d)
+    mask = _mask(H if bq == bk else 1, N, bq, bk, density, N + bq, causal)
+    o, lse = _run_fwd(x, tau, causal, mask, bq, bk)
+    ro, rl = orc.attention_fwd(*(x[n].f64() for n in ("q", "k", "v")), tau, causal,
+                               block=(mask, bq, bk))
+    assert_close(o, ro, "bf16", "O")
+    _lse_close(lse, rl, "LSE")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("d", [64, 128])
+def test_block_sparse_visibility_exact(d, causal):
+    """Q = 0 gives uniform weights over the visible keys; V one-hot for keys
+    J0 .. J0+d-1 makes O_i[c] > 0 exactly when key J0+c is visible to row i
+    (and 0 otherwise), so the pattern of zeros is the visibility, bit for bit."""
+    import io_aware_tiled_03_amd as fa
+    import torch
+    N, bq, bk, J0 = 768, 64, 32, 256
+    mask = _mask(2, N, bq, bk, 0.4, 7, causal)
+    q = torch.zeros(1, 2, N, d, dtype=torch.bfloat16, device="cuda")
+    k = torch.randn(1, 2, N, d, generator=torch.Generator().manual_seed(3)).to("cuda", torch.bfloat16)
+    v = torch.zeros(1, 2, N, d)
+    v[:, :, J0 + torch.arange(d), torch.arange(d)] = 1.0
+    o, _ = fa.fwd(q, k, v.to("cuda", torch.bfloat16), causal=causal,
+                  block_mask=torch.from_numpy(mask).cuda(), block_size=(bq, bk))
+    got = to_f64(o)[0] > 0
+    for h in range(2):
+        vis = orc.visible(np.arange(N), J0 + np.arange(d), causal, block=(mask[h], bq, bk))
+        assert np.array_equal(got[h], vis), (h, int((got[h] != vis).sum()))
+
+
+def test_block_sparse_all_ones_is_dense():
+    import io_aware_tiled_03_amd as fa
+    import torch
+    x = fa_inputs.dense_inputs(2, 2, 640, 128, "bf16", 21000)
+    q, k, v = (to_device(x[n]) for n in ("q", "k", "v"))
+    ones = torch.ones(1, 5, 5, dtype=torch.uint8, device="cuda")
+    for causal in (False, True):
+        o1, l1 = fa.fwd(q, k, v, causal=causal)
+        o2, l2 = fa.fwd(q, k, v, causal=causal, block_mask=ones, block_size=(128, 128))
+        assert (o1.float() - o2.float()).abs().max() <= 2e-2
+        assert (l1 - l2).abs().max() <= 1e-3
+
+
+def test_block_sparse_long_prefill_bigbird_pattern():
+    """The long prefill shape (1x32x16384x128, causal) with a band of 3 key
+    blocks around the diagonal plus the first key block (global tokens),
+    128 x 128 blocks: sampled rows of 4 heads against the oracle."""
+    w = fa_inputs.WORKLOADS[3]
+    x = fa_inputs.workload_inputs(w)
+    nb = w.N // 128
+    i, j = np.meshgrid(np.arange(nb), np.arange(nb), indexing="ij")
+    mask = ((np.abs(i - j) <= 1) | (j == 0)).astype(np.uint8)[None]
+    o, lse = _run_fwd(x, w.tau, True, mask, 128, 128)
+    qf, kf, vf = (x[n].f64() for n in ("q", "k", "v"))
+    rng = np.random.Generator(np.random.PCG64(35))
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 255, 256, 8191, 8192, 16383],
+                                     rng.integers(0, w.N, 100)]))
+    for h in (0, 11, 25, 31):
+        ro, rl = orc.attention_fwd_head(qf[0, h], kf[0, h], vf[0, h], w.tau, True, rows=rows,
+                                        block=(mask[0], 128, 128))
+        assert_close(o[0, h, rows], ro, "bf16", "O[h=%d]" % h)
+        _lse_close(lse[0, h, rows], rl, "LSE[h=%d]" % h)
+
+
+def _run_bwd(x, tau, causal, mask, bq, bk):
+    import io_aware_tiled_03_amd as fa
+    import torch
+    q, k, v, do = (to_device(x[n]) for n in ("q", "k", "v", "do"))
+    m = torch.from_numpy(mask).cuda()
+    o, lse = fa.fwd(q, k, v, tau=tau, causal=causal, block_mask=m, block_size=(bq, bk))
+    dq, dk, dv = fa.bwd(q, k, v, o, lse, do, tau=tau, causal=causal, block_mask=m,
+                        block_size=(bq, bk))
+    return {"dq": to_f64(dq), "dk": to_f64(dk), "dv": to_f64(dv)}
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("bq,bk", [(32, 32), (64, 128), (128, 64)])
+@pytest.mark.parametrize("N,density", [(100, 0.5), (300, 0.3), (700, 0.6)])
+def test_block_sparse_bwd_small(N, density, bq, bk, causal, d):
+    B, H = 2, 2
+    x = fa_inputs.dense_inputs(B, H, N, d, "bf16", 22000 + N + bq + bk, with_do=True)
+    tau = 1.0 / np.sqrt(d)
+    mask = _mask(H, N, bq, bk, density, 2 * N + bk, causal)
+    g = _run_bwd(x, tau, causal, mask, bq, bk)
+    qf, kf, vf, dof = (x[n].f64() for n in ("q", "k", "v", "do"))
+    for b in range(B):
+        for h in range(H):
+            # D from the saved bf16 output and the bf16-operand allowance:
+            # sparse rows can have few visible keys (P close to one)
+            ref = orc.attention_bwd_head(qf[b, h], kf[b, h], vf[b, h], dof[b, h], tau, causal,
+                                         d_from_saved_bf16=True, block=(mask[h], bq, bk))
+            extra = rounding_allowance(ref, qf[b, h], kf[b, h], dof[b, h], tau)
+            for name in ("dq", "dk", "dv"):
+                assert_close(g[name][b, h], ref[name], "bf16", "%s[%d,%d]" % (name, b, h),
+                             ulp_allow=True, extra=extra[name])
+
+
+def test_block_sparse_bwd_workload_shape():
+    """The backward workload's shape (4x16x4096x64 bf16, causal) with a
+    random 50% mask of 128 x 128 blocks (diagonal kept), one mask per head:
+    2 sampled heads element by element at the stated bounds."""
+    w = fa_inputs.WORKLOADS[5]
+    x = fa_inputs.workload_inputs(w)
+    nb = w.N // 128
+    mask = (np.random.default_rng(36).random((w.H, nb, nb)) < 0.5).astype(np.uint8)
+    mask[:, np.arange(nb), np.arange(nb)] = 1
+    g = _run_bwd(x, w.tau, True, mask, 128, 128)
+    qf, kf, vf, dof = (x[n].f64() for n in ("q", "k", "v", "do"))
+    for b, h in ((1, 2), (3, 9)):
+        ref = orc.attention_bwd_head(qf[b, h], kf[b, h], vf[b, h], dof[b, h], w.tau, True,
+                                     d_from_saved_bf16=True, block=(mask[h], 128, 128))
+        for name in ("dq", "dk", "dv"):
+            assert_close(g[name][b, h], ref[name], "bf16", "%s[%d,%d]" % (name, b, h))
