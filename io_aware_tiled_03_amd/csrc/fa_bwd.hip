@@ -209,13 +209,18 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                 lq[i] = *reinterpret_cast<const f32x4*>(&l_lds[qb * 32 + 16 * (i >> 1) + 8 * hf + 4 * (i & 1)]);
                 dq4[i] = *reinterpret_cast<const f32x4*>(&d_lds[qb * 32 + 16 * (i >> 1) + 8 * hf + 4 * (i & 1)]);
             }
-            // dropout words: 4-query group g = r/4 holds queries
-            // qs + 16 (g/2) + 8 hf + 4 (g%2) + 0..3; word r%4, byte key%4
-            u32x4 dblk[4];
+            // dropout bits: 4-query group g = r/4 holds queries
+            // qs + 16 (g/2) + 8 hf + 4 (g%2) + 0..3.  The four lanes of a quad
+            // hold keys of one 4-key block, so lane e computes the block of
+            // query group e, byte-transposes it (byte w of word e' = byte e'
+            // of word w) and a quad transpose hands lane key%4 its byte of
+            // every word of all four groups: byte w of kb4[g] = bit (query
+            // 4-group g + w, this key).
+            u32x4 kb4;
             if constexpr (DROP) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    dblk[g] = drop.block(key, qs + 16 * (g >> 1) + 8 * hf + 4 * (g & 1), bh);
+                const int e = key & 3;
+                kb4 = quad_transpose(byte_transpose(
+                          drop.block(key, qs + 16 * (e >> 1) + 8 * hf + 4 * (e & 1), bh)), e);
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -225,7 +230,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                     if (CAUSAL && (key > q || (WIN && q - key >= window && key >= sinks))) p = 0.f;
                 }
                 if constexpr (DROP) {
-                    const bool kept = drop.keep(dblk[r >> 2][r & 3], key & 3);
+                    const bool kept = drop.keep(kb4[r >> 2], r & 3);
                     sacc[r] = kept ? p : 0.f;
                     dp[r] = p * ((kept ? dp[r] * drop.scale : 0.f) - dq4[r >> 2][r & 3]);
                 } else {
@@ -426,13 +431,13 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
             }
             // dropout words of this lane's row for the 4-key groups g = r/4:
             // keys k0 + 32 kb + 16 (g/2) + 8 hf + 4 (g%2) + 0..3, byte r%4
-            uint32_t dw[4] = {0u, 0u, 0u, 0u};
+            // (one generator call per lane: lane r of the quad computes key
+            // group r, a quad transpose hands out the rows' words)
+            u32x4 dw = {0u, 0u, 0u, 0u};
             if constexpr (DROP) {
-#pragma unroll
-                for (int g = 0; g < 4; ++g)
-                    dw[g] = Dropout::row_word(
-                        drop.block(k0 + kb * 32 + 16 * (g >> 1) + 8 * hf + 4 * (g & 1), qrow, bh),
-                        qrow & 3);
+                const int r4 = qrow & 3;
+                dw = quad_transpose(
+                    drop.block(k0 + kb * 32 + 16 * (r4 >> 1) + 8 * hf + 4 * (r4 & 1), qrow, bh), r4);
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) {

@@ -206,6 +206,40 @@ struct Dropout {
     }
 };
 
+// 4 x 4 transpose across each group of four lanes: lane r (0..3 within its
+// quad) holds row r, a[0..3]; afterwards it holds column r, b[g] = lane g's
+// a[r].  Two butterfly stages (partner lane r^1, then r^2) exchange one
+// element per pair of indices through DPP quad permutes.
+__device__ __forceinline__ u32x4 quad_transpose(u32x4 a, int r) {
+#pragma unroll
+    for (int k = 1; k <= 2; k <<= 1) {
+        const bool hi = (r & k) != 0;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            if (w & k) continue;   // pair (w, w + k)
+            const uint32_t send = hi ? a[w] : a[w + k];
+            const uint32_t recv = (uint32_t)(k == 1
+                ? __builtin_amdgcn_mov_dpp((int)send, kDppXor1, 0xF, 0xF, false)
+                : __builtin_amdgcn_mov_dpp((int)send, kDppXor2, 0xF, 0xF, false));
+            if (hi) a[w] = recv;
+            else a[w + k] = recv;
+        }
+    }
+    return a;
+}
+
+// 4 x 4 byte transpose inside one lane: out[e] holds byte e of in[0..3]
+// (byte w of out[e] = byte e of in[w]).  v_perm_b32 picks bytes of {hi, lo}
+// (selectors 0..3 address lo, 4..7 hi).
+__device__ __forceinline__ u32x4 byte_transpose(const u32x4& a) {
+    const uint32_t t01 = __builtin_amdgcn_perm(a[1], a[0], 0x05010400u);   // a0b0 a1b0 a0b1 a1b1
+    const uint32_t t23 = __builtin_amdgcn_perm(a[3], a[2], 0x05010400u);
+    const uint32_t u01 = __builtin_amdgcn_perm(a[1], a[0], 0x07030602u);   // a0b2 a1b2 a0b3 a1b3
+    const uint32_t u23 = __builtin_amdgcn_perm(a[3], a[2], 0x07030602u);
+    return u32x4{__builtin_amdgcn_perm(t23, t01, 0x05040100u), __builtin_amdgcn_perm(t23, t01, 0x07060302u),
+                 __builtin_amdgcn_perm(u23, u01, 0x05040100u), __builtin_amdgcn_perm(u23, u01, 0x07060302u)};
+}
+
 // Block-sparse tile lists: writes to list[] (LDS), in increasing order, the
 // tiles t < ntiles for which active(t) holds, and returns how many there are.
 // Waves ballot chunks of 64 tiles, one thread places the chunks by a prefix

@@ -252,6 +252,18 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
         // a row with no visible key so far keeps m = -inf; its scores are all
         // -inf as well, so any finite reference gives p = 0
         const float mc = (SPARSE_ROWS && MASK && m == neg_inf()) ? 0.f : m * scale_log2;
+        // Dropout words, one generator call per lane per 32-key block: the four
+        // lanes of a quad hold rows of one 4-row block, so lane r computes the
+        // block of key group r (keys 16(r/2) + 8hf + 4(r%2) + 0..3) and a quad
+        // transpose hands every lane its own row's word of all four groups.
+        u32x4 dwq[NKB];
+        if constexpr (DROP) {
+            const int r4 = qrow & 3;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+                dwq[kb] = quad_transpose(
+                    drop.block(k0 + kb * 32 + 16 * (r4 >> 1) + 8 * hf + 4 * (r4 & 1), qrow, bh), r4);
+        }
         u32x4 pf[NKB][2];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
@@ -260,10 +272,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
                 // dropout words of this lane's row for keys k0+32kb+16t+8hf+0..3 and +4..7
                 uint32_t dw[2] = {0u, 0u};
                 if constexpr (DROP) {
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh)
-                        dw[hh] = Dropout::row_word(
-                            drop.block(k0 + kb * 32 + 16 * t + 8 * hf + 4 * hh, qrow, bh), qrow & 3);
+                    dw[0] = dwq[kb][2 * t];
+                    dw[1] = dwq[kb][2 * t + 1];
                 }
 #pragma unroll
                 for (int w = 0; w < 4; ++w) {
