@@ -153,7 +153,15 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
 
     const int n_qt = (N + BR - 1) / BR;
     const int qt0 = CAUSAL ? k0 / BR : 0;
-    float ld_l = 0.f, ld_d = 0.f;   // this thread's LSE/D value of the next tile (threads < 128)
+    // The next tile's LSE (threads < BR) or D (threads BR .. 2BR-1) value of
+    // this thread, raw: one register whose load is only waited for when it is
+    // written to LDS after the current tile's math.  (Two variables assigned
+    // under the thread test became a private array in scratch, and the store
+    // into it waited for every outstanding load, the next tile's Q and dO
+    // copies included, before the current tile could start.)
+    const bool ld_is_l = tid < BR;
+    const float* const ld_src = (ld_is_l ? LSE : Dv) + (size_t)bh * N;
+    float ld_v = 0.f;
     auto stage = [&](int qt, auto bufc) __attribute__((always_inline)) {
         constexpr bool B1 = decltype(bufc)::value != 0;
         const int q0 = qt * BR;
@@ -161,14 +169,13 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         cp.issue(ors, q0, B1 ? sdO1 : sdO0, wave);
         if (tid < 2 * BR) {
             const int q = q0 + (tid & (BR - 1));
-            if (tid < BR) ld_l = q < N ? LSE[(size_t)bh * N + q] * kLog2e : __builtin_inff();
-            else ld_d = q < N ? Dv[(size_t)bh * N + q] : 0.f;
+            ld_v = q < N ? ld_src[q] : (ld_is_l ? __builtin_inff() : 0.f);
         }
     };
     auto stage_ld = [&](auto bufc) __attribute__((always_inline)) {
         constexpr bool B1 = decltype(bufc)::value != 0;
-        if (tid < BR) (B1 ? sL1 : sL0)[tid] = ld_l;
-        else if (tid < 2 * BR) (B1 ? sD1 : sD0)[tid - BR] = ld_d;
+        if (ld_is_l) (B1 ? sL1 : sL0)[tid] = ld_v * kLog2e;
+        else if (tid < 2 * BR) (B1 ? sD1 : sD0)[tid - BR] = ld_v;
     };
 
     // Block-sparse: this wave's key block (waves hold 32 keys, blocks >= 32)
