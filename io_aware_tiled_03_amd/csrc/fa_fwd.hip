@@ -63,6 +63,15 @@ __device__ __forceinline__ int kperm_inv(int r) {
 #ifndef FA_FWD_VPAD
 #define FA_FWD_VPAD 16       // V row padding (bf16 elements)
 #endif
+// d=128: the score products' K operand reads are issued this many ahead of
+// the products that use them (the compiler's own order kept two in flight,
+// exposing the LDS latency before every other product; four measured 2%
+// faster on the long causal prefill, more gave nothing further; at d=64,
+// with more waves per SIMD to hide the latency, it gave nothing).  0 leaves
+// the order to the compiler.
+#ifndef FA_FWD_SCHED
+#define FA_FWD_SCHED 4
+#endif
 #ifndef FA_FWD_PRIO
 #define FA_FWD_PRIO 0        // raise wave priority while issuing MFMA chains
 #endif
@@ -215,6 +224,21 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
 #pragma unroll
             for (int ks = 1; ks < D / 16; ++ks) s[kb] = mfma32x32x16(ka[ks], qf[ks], s[kb]);
         }
+#if FA_FWD_SCHED
+        if constexpr (D == 128 && !DROP && !BLK) {
+            // the score products as a scheduling region of their own: AH K
+            // operand reads first, then two products per two further reads
+            constexpr int NR = NKB * D / 16, AH = FA_FWD_SCHED;
+            __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);
+#pragma unroll
+            for (int i = 0; i < (NR - AH) / 2; ++i) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, AH, 0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+#endif
         prio_lo();
         if constexpr (MASK) {
 #pragma unroll
