@@ -2,7 +2,7 @@
 
 One step = one pass of the whole path over the GPT-2-medium-shaped batch
 (B=8, H=16, N=1024, d=64, bf16, tau=1/8):
-    fa_fwd non-causal, fa_fwd causal, fa_bwd causal (its three kernels enqueued
+    fa_fwd non-causal, fa_fwd causal, fa_bwd causal (its two kernels enqueued
     one by one through fa_bwd_stage), and fa_decode with one query per sequence
     against the same K/V as the cache (L_b = N for every b).
 value = algorithmic TFLOP/s of the step (forward 4*B*H*N^2*d, halved when
@@ -97,9 +97,8 @@ def make_step(fa, x, B, H, N, d, tau, timer=None):
     calls = [
         ("fwd_noncausal", lambda: fa.fwd(q, k, v, tau, False, o_nc, lse_nc)),
         ("fwd_causal", lambda: fa.fwd(q, k, v, tau, True, o_c, lse_c)),
-        ("bwd_pre", lambda: fa.bwd(q, k, v, o_c, lse_c, do, tau, True, dq, dk, dv, ws, stage=0)),
+        ("bwd_dq", lambda: fa.bwd(q, k, v, o_c, lse_c, do, tau, True, dq, dk, dv, ws, stage=0)),
         ("bwd_dkdv", lambda: fa.bwd(q, k, v, o_c, lse_c, do, tau, True, dq, dk, dv, ws, stage=1)),
-        ("bwd_dq", lambda: fa.bwd(q, k, v, o_c, lse_c, do, tau, True, dq, dk, dv, ws, stage=2)),
         ("decode", lambda: fa.decode(qd, k, v, seq, tau, 0, od, lsed, wsd)),
     ]
 
@@ -128,11 +127,12 @@ def step_work(B, H, N, d):
     return {
         "fwd_noncausal": (4.0 * n2, 3 * t + t + lse),
         "fwd_causal": (2.0 * n2, 3 * t + t + lse),
-        "bwd_pre": (2.0 * B * H * N * d, 2 * t + lse),
+        # dQ kernel: D = rowsum(dO o O) for its rows, then the dQ product (1 of
+        # the 5 backward GEMMs; its own S and dP recompute is not counted);
+        # reads Q, K, V, dO, O, LSE, writes dQ and D
+        "bwd_dq": (1.0 * n2 + 2.0 * B * H * N * d, 5 * t + 2 * lse + t),
         # dK/dV kernel: S, dP, dV, dK products (4 of the 5 backward GEMMs), causal half
         "bwd_dkdv": (4.0 * n2, 4 * t + 2 * lse + 2 * t),
-        # dQ kernel: the dQ product (1 of 5) plus its own S and dP recompute
-        "bwd_dq": (1.0 * n2, 4 * t + 2 * lse + t),
         "decode": (4.0 * B * H * N * d, 2 * t + 2 * B * H * d * e + B * H * 4),
     }
 

@@ -245,12 +245,13 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N);
  * fa_bwd - recomputing backward of fa_fwd.
  *
  * Uses only O and LSE saved by the forward ("flash-attention" page, "como
- * funciona", backward paragraph): first D_i = dO_i . O_i (the page's identity
- * D_i = P_i . dP_i = dO_i . O_i, an inner product of length d), then one kernel
- * per key tile that recomputes S = tau Q K^T and P = exp(S - LSE) on chip and
- * accumulates dV = P^T dO and dK = tau dS^T Q with dS = P o (dO V^T - D), and
- * one kernel per query tile that accumulates dQ = tau dS K.  No atomics: the
- * result is deterministic.
+ * funciona", backward paragraph).  Two kernels: one per query tile that first
+ * forms D_i = dO_i . O_i for its rows (the page's identity D_i = P_i . dP_i =
+ * dO_i . O_i, an inner product of length d), writes it to the workspace and
+ * accumulates dQ = tau dS K with dS = P o (dO V^T - D); then one per key tile
+ * that recomputes S = tau Q K^T and P = exp(S - LSE) on chip and accumulates
+ * dV = P^T dO and dK = tau dS^T Q, reading D.  No atomics: the result is
+ * deterministic.
  *
  * q, k, v, o, dout : [B, H, N, d], dtype `dtype`; o is fa_fwd's output.
  * lse              : [B, H, N] float, fa_fwd's output.
@@ -303,13 +304,13 @@ int fa_bwd_block_sparse(const void* q, const void* k, const void* v, const void*
                         void* stream);
 
 /*
- * fa_bwd_stage - enqueue one of fa_bwd's three kernels.
+ * fa_bwd_stage - enqueue one of fa_bwd's two kernels.
  *
- * stage 0 computes D into the workspace, stage 1 dK and dV, stage 2 dQ (stages
- * 1 and 2 read D, so stage 0 must have run on the same inputs).  Enqueuing
- * stages 0, 1, 2 in order on one stream is exactly fa_bwd.  Same arguments and
- * checks as fa_bwd, plus FA_ERR_ARG for a stage outside 0..2.  Meant for
- * per-kernel timing and for callers that only need D.
+ * stage 0 computes dQ and writes D into the workspace, stage 1 dK and dV
+ * (it reads D, so stage 0 must have run on the same inputs).  Enqueuing
+ * stages 0, 1 in order on one stream is exactly fa_bwd.  Same arguments and
+ * checks as fa_bwd, plus FA_ERR_ARG for a stage outside 0..1.  Meant for
+ * per-kernel timing.
  */
 int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,
                  const float* lse, const void* dout, void* dq, void* dk, void* dv,

@@ -241,7 +241,8 @@ def bwd(q, k, v, o, lse, do, tau=None, causal=False, dq=None, dk=None, dv=None, 
         stage=None, window=None, sinks=0, dropout=None, block_mask=None, block_size=(128, 128)):
     """dQ, dK, dV of fa_fwd's output given dO, via fa_bwd (workspace holds D on return).
 
-    With stage in (0, 1, 2) only that kernel is enqueued, via fa_bwd_stage.  With
+    With stage in (0, 1) only that kernel is enqueued, via fa_bwd_stage (0: dQ
+    and D, 1: dK and dV, which reads D).  With
     window (causal only): the backward of the sliding-window forward, via fa_bwd_window.
     With dropout = (p, seed, offset): the backward of fa_fwd_dropout, via fa_bwd_dropout.
     With block_mask: the backward of fa_fwd_block_sparse, via fa_bwd_block_sparse."""

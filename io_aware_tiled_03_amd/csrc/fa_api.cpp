@@ -276,7 +276,7 @@ int bwd_common(int stages, const void* q, const void* k, const void* v, const vo
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dout, void* dq, void* dk, void* dv, int B, int H, int N, int d, float tau,
            int causal, void* workspace, size_t workspace_bytes, int dtype, void* stream) {
-    return bwd_common(7, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, tau, causal, workspace,
+    return bwd_common(3, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, tau, causal, workspace,
                       workspace_bytes, dtype, stream);
 }
 
@@ -285,7 +285,7 @@ int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, co
                   float tau, int window, int sinks, void* workspace, size_t workspace_bytes,
                   int dtype, void* stream) {
     if (window < 1 || sinks < 0) return FA_ERR_ARG;
-    return bwd_common(7, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, tau, 1, workspace,
+    return bwd_common(3, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, tau, 1, workspace,
                       workspace_bytes, dtype, stream, window, sinks);
 }
 
@@ -296,7 +296,7 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
                    void* stream) {
     const int thr = drop_threshold(p_drop);
     if (thr < 0) return FA_ERR_ARG;
-    return bwd_common(7, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, tau, causal, workspace,
+    return bwd_common(3, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, tau, causal, workspace,
                       workspace_bytes, dtype, stream, 0, 0, thr, seed, offset);
 }
 
@@ -308,7 +308,7 @@ int fa_bwd_block_sparse(const void* q, const void* k, const void* v, const void*
     fa::BlockSparse bs;
     const int st = block_sparse_args(block_mask, mask_heads, block_q, block_k, H, N, &bs);
     if (st != FA_OK) return st;
-    return bwd_common(7, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, tau, causal, workspace,
+    return bwd_common(3, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, tau, causal, workspace,
                       workspace_bytes, dtype, stream, 0, 0, 0, 0, 0, &bs);
 }
 
@@ -316,7 +316,7 @@ int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const v
                  const float* lse, const void* dout, void* dq, void* dk, void* dv, int B, int H,
                  int N, int d, float tau, int causal, void* workspace, size_t workspace_bytes,
                  int dtype, void* stream) {
-    if (stage < 0 || stage > 2) return FA_ERR_ARG;
+    if (stage < 0 || stage > 1) return FA_ERR_ARG;
     return bwd_common(1 << stage, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, tau, causal,
                       workspace, workspace_bytes, dtype, stream);
 }
@@ -332,7 +332,7 @@ const char* fa_status_string(int status) {
         case FA_ERR_ALIGN: return "a pointer is not aligned (16 bytes for tensors)";
         case FA_ERR_ARG:
             return "bad argument value (tau finite and > 0, num_splits 0..1024, window >= 1, "
-                   "sinks >= 0, stage 0..2, dropout probability in [0, 255/256], block sizes "
+                   "sinks >= 0, stage 0..1, dropout probability in [0, 255/256], block sizes "
                    "powers of two in [32, 1024])";
         default: return "unknown status";
     }

@@ -7,8 +7,15 @@
 //   dV   = P^T dO,   dP = dO V^T,   dS = P o (dP - D),
 //   dK   = tau dS^T Q,               dQ = tau dS K.
 //
-// Kernels (bf16 in, fp32 accumulation on MFMA, bf16 out; no atomics):
-//  bwd_pre_kernel  : D for every row, an inner product of length d.
+// Kernels (bf16 in, fp32 accumulation on MFMA, bf16 out; no atomics), run in
+// this order:
+//  bwd_dq_kernel   : one workgroup per 128-query tile (32 queries per wave, Q
+//                    and dO rows in registers); first forms D for its rows
+//                    from O and dO (an inner product of length d) and writes
+//                    it out, then loops over 64-key tiles of K and V up to the
+//                    diagonal, recomputing S^T = K Q^T and dP^T = V dO^T (one
+//                    query per lane) and accumulating dQ^T += K^T dS^T with
+//                    K^T from the transposing read.
 //  bwd_dkdv_kernel : one workgroup per 128-key tile (32 keys per wave, K and V
 //                    of those keys held in registers); loops over query tiles
 //                    (128 rows at d = 64, 64 at d = 128 and under a block
@@ -17,12 +24,8 @@
 //                    read their A operands row-wise (one key per result lane);
 //                    dV^T += dO^T P and dK^T += Q^T dS read dO^T and Q^T with
 //                    the transposing LDS read and take P and dS straight from
-//                    registers as B operands.
-//  bwd_dq_kernel   : one workgroup per 128-query tile (32 queries per wave, Q
-//                    and dO rows in registers); loops over 64-key tiles of K
-//                    and V up to the diagonal, recomputing S^T = K Q^T and
-//                    dP^T = V dO^T (one query per lane) and accumulating
-//                    dQ^T += K^T dS^T with K^T from the transposing read.
+//                    registers as B operands; it reads the D that the dQ
+//                    kernel wrote.
 // A-operand rows are read in the kperm order so that the C registers of each
 // lane half hold 8 consecutive rows, ready to be packed as a B operand.  Only
 // tiles that cross the causal diagonal run the masked variant.
@@ -38,27 +41,6 @@ namespace {
 __device__ __forceinline__ int kperm(int m) {
     const int j = 4 * (m >> 3) + (m & 3);
     return 16 * (j >> 3) + 8 * ((m >> 2) & 1) + (j & 7);
-}
-
-// D_i = sum_d dO_id O_id in fp32; D/8 lanes per row.
-template <int D>
-__global__ __launch_bounds__(256) void bwd_pre_kernel(const uint16_t* __restrict__ O,
-                                                      const uint16_t* __restrict__ dO,
-                                                      float* __restrict__ Dv, size_t rows) {
-    constexpr int LPR = D / 8;
-    const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
-    const size_t row = gid / LPR;
-    const int c = (int)(gid % LPR);
-    float acc = 0.f;
-    if (row < rows) {
-        const u32x4 a = ld16(O + row * D + c * 8), b = ld16(dO + row * D + c * 8);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            acc += bf16lo(a[i]) * bf16lo(b[i]) + bf16hi(a[i]) * bf16hi(b[i]);
-    }
-#pragma unroll
-    for (int off = 1; off < LPR; off <<= 1) acc += __shfl_xor(acc, off, 64);
-    if (row < rows && c == 0) Dv[row] = acc;
 }
 
 template <int N_> using ic = std::integral_constant<int, N_>;
@@ -361,8 +343,9 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
 template <int D, int MODE, bool DROP>
 __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
-    uint16_t* __restrict__ dQ, int BH, int N, float scale_log2, float tau, int n_qtiles, int window,
+    const uint16_t* __restrict__ dO, const uint16_t* __restrict__ O, const float* __restrict__ LSE,
+    float* __restrict__ Dv, uint16_t* __restrict__ dQ, int BH, int N, float scale_log2, float tau,
+    int n_qtiles, int window,
     int sinks, Dropout drop, BlockSparse bs) {
     constexpr bool CAUSAL = MODE == kMaskCausal || MODE == kMaskWindow || MODE == kMaskBlockCausal;
     constexpr bool WIN = MODE == kMaskWindow, BLK = MODE >= kMaskBlock;
@@ -383,15 +366,26 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const size_t base = (size_t)bh * N * D;
     const int q0 = qt * BR, qw = q0 + 32 * wave, qrow = qw + ln;
 
+    // D_i = dO_i . O_i (the page's identity D_i = P_i . dP_i = dO_i . O_i),
+    // formed here from the rows this wave owns: each lane holds half of its
+    // row's d entries (the same slices as its dO operands), the two wave
+    // halves are added, and the value is written to the workspace for the
+    // dK/dV kernel, which runs after this one.
     u32x4 qf[D / 16], df[D / 16];
+    float dpart = 0.f;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
         const size_t off = base + (size_t)qrow * D + ks * 16 + hf * 8;
         qf[ks] = qrow < N ? ld16(Q + off) : u32x4{0, 0, 0, 0};
         df[ks] = qrow < N ? ld16(dO + off) : u32x4{0, 0, 0, 0};
+        const u32x4 of = qrow < N ? ld16(O + off) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            dpart += bf16lo(of[i]) * bf16lo(df[ks][i]) + bf16hi(of[i]) * bf16hi(df[ks][i]);
     }
     const float lse2 = qrow < N ? LSE[(size_t)bh * N + qrow] * kLog2e : __builtin_inff();
-    const float Dq = qrow < N ? Dv[(size_t)bh * N + qrow] : 0.f;
+    const float Dq = dpart + xor32(dpart);
+    if (hf == 0 && qrow < N) Dv[(size_t)bh * N + qrow] = Dq;
     f32x16 dqacc[D / 32];
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -580,11 +574,14 @@ void launch(const BwdArgs& a, int stages, hipStream_t st) {
     drop.offset = a.offset;
     drop.thr = a.drop_thr;
     drop.scale = a.drop_thr > 0 ? 256.f / (256.f - (float)a.drop_thr) : 1.f;
+    // stage bit 0: dQ, which also writes D; bit 1: dK and dV, which read D
     if (stages & 1) {
-        const size_t rows = (size_t)bh * a.N;
-        const size_t pre_blocks = (rows * (D / 8) + 255) / 256;
-        hipLaunchKernelGGL((bwd_pre_kernel<D>), dim3((unsigned)pre_blocks), dim3(256), 0, st,
-                           (const uint16_t*)a.o, (const uint16_t*)a.dout, a.D, rows);
+        const int nq = (a.N + 127) / 128;
+        hipLaunchKernelGGL((bwd_dq_kernel<D, MODE, DROP>), dim3(nq * bh), dim3(256), 0, st,
+                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
+                           (const uint16_t*)a.dout, (const uint16_t*)a.o, a.lse, a.D,
+                           (uint16_t*)a.dq, bh, a.N, a.tau * kLog2e, a.tau, nq, a.window, a.sinks,
+                           drop, a.blk);
     }
     if (stages & 2) {
         const int nk = (a.N + 127) / 128;
@@ -592,13 +589,6 @@ void launch(const BwdArgs& a, int stages, hipStream_t st) {
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                            (const uint16_t*)a.dout, a.lse, a.D, (uint16_t*)a.dk, (uint16_t*)a.dv,
                            bh, a.N, a.tau * kLog2e, a.tau, a.window, a.sinks, drop, a.blk);
-    }
-    if (stages & 4) {
-        const int nq = (a.N + 127) / 128;
-        hipLaunchKernelGGL((bwd_dq_kernel<D, MODE, DROP>), dim3(nq * bh), dim3(256), 0, st,
-                           (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
-                           (const uint16_t*)a.dout, a.lse, a.D, (uint16_t*)a.dq, bh, a.N,
-                           a.tau * kLog2e, a.tau, nq, a.window, a.sinks, drop, a.blk);
     }
 }
 

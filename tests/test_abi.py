@@ -248,6 +248,7 @@ def test_bwd_window_rejects_bad_arguments():
 def test_bwd_stage_rejects_bad_arguments():
     fa, lib = _lib()
     args = (P, P, P, P, P, P, P, P, P, 1, 2, 64, 64, 0.125, 1, P, 1 << 20, 1, None)
+    assert lib.fa_bwd_stage(2, *args) == 7
     assert lib.fa_bwd_stage(3, *args) == 7
     assert lib.fa_bwd_stage(-1, *args) == 7
     bad = list(args); bad[10] = 0
