@@ -155,6 +155,74 @@ def load_traffic(kernel):
     return e.get("bytes_per_launch")
 
 
+# The step's kernels as rocprofv3 names them (the decode call launches two).
+STEP_KERNELS = {
+    "fwd_noncausal": ["fwd_bf16_kernel<64, 0, 64, 4, false>"],
+    "fwd_causal": ["fwd_bf16_kernel<64, 1, 64, 4, false>"],
+    "bwd_dq": ["bwd_dq_kernel<64, 1, false>"],
+    "bwd_dkdv": ["bwd_dkdv_kernel<64, 1, false>"],
+    "decode": ["decode_split_kernel<unsigned short, 64>", "decode_merge_kernel<unsigned short, 64>"],
+}
+
+
+def _counter_means(run_dir, counter):
+    """Mean value of `counter` per dispatch, by kernel name, over the
+    *counter_collection.csv files rocprofv3 wrote under run_dir."""
+    import csv
+    import glob
+    per = {}
+    files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no counter_collection.csv under %s" % run_dir)
+    for fn in files:
+        with open(fn) as f:
+            for row in csv.DictReader(f):
+                if row.get("Counter_Name") != counter:
+                    continue
+                key = (fn, row["Dispatch_Id"])
+                name = row["Kernel_Name"]
+                per.setdefault(name, {}).setdefault(key, 0.0)
+                per[name][key] += float(row["Counter_Value"])
+    return {name: sum(d.values()) / len(d) for name, d in per.items()}
+
+
+def summarize_counters(fetch_step, fetch_copy, write_step, write_copy, copy_mib, commands):
+    """Writes profiles/traffic.json: HBM bytes per launch of the step's kernels
+    from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by what the
+    same counter reads per byte of the plain device copy (--calibrate-copy)."""
+    copy_bytes = float(copy_mib << 20)
+    out = {"about": "HBM bytes per launch of the step's kernels (8x16x1024x64 bf16) from two "
+                    "rocprofv3 counter runs, FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each "
+                    "divided by what the same counter reads per byte of a plain %d MiB device "
+                    "copy (bench.py --calibrate-copy %d) run the same way." % (copy_mib, copy_mib),
+           "commands": commands, "copy_counter_per_byte": {}, "src_digest": src_digest(),
+           "kernels": {}}
+    vals = {}
+    for counter, step_dir, copy_dir in (("FETCH_SIZE", fetch_step, fetch_copy),
+                                        ("WRITE_SIZE", write_step, write_copy)):
+        cm = _counter_means(copy_dir, counter)
+        copy_kib = max(cm.values())   # the copy is the largest dispatch of that run
+        out["copy_counter_per_byte"][counter] = copy_kib * 1024.0 / copy_bytes
+        vals[counter] = _counter_means(step_dir, counter)
+    for bench_name, names in STEP_KERNELS.items():
+        e = {}
+        for counter, key in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
+            kib = 0.0
+            for n in names:
+                hits = [v for k, v in vals[counter].items() if n in k]
+                if not hits:
+                    raise SystemExit("kernel %s not in the %s run" % (n, counter))
+                kib += hits[0]
+            e[counter + "_KiB"] = round(kib, 1)
+            e[key + "_bytes"] = round(kib * 1024.0 / out["copy_counter_per_byte"][counter], 1)
+        e["bytes_per_launch"] = int(round(e["fetch_bytes"] + e["write_bytes"]))
+        out["kernels"][bench_name] = e
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out["kernels"]))
+
+
 def cpu_baseline(xh, B, H, N, d, tau, budget_s=10.0):
     """The float64 oracle over whole heads of the same step until ~budget_s seconds."""
     import numpy as np
@@ -364,7 +432,22 @@ def main(argv=None):
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times "
                          "(scales the HBM byte counters of a profiler run) and exit")
+    ap.add_argument("--summarize-counters", nargs=4, default=None,
+                    metavar=("FETCH_STEP", "FETCH_COPY", "WRITE_STEP", "WRITE_COPY"),
+                    help="write profiles/traffic.json from four rocprofv3 --pmc output "
+                         "directories (FETCH_SIZE and WRITE_SIZE, each over a step run and a "
+                         "--calibrate-copy 1024 run) and exit; runs on the host, no GPU")
     args = ap.parse_args(argv)
+    if args.summarize_counters:
+        d = args.summarize_counters
+        cmds = ["rocprofv3 --pmc %s --output-format csv -d %s -o %s -- python -u bench.py %s"
+                % (c, r, o, a) for c, r, o, a in (
+                    ("FETCH_SIZE", d[0], "step", "--steps 3 --warmup 1 --no-extra --no-cpu"),
+                    ("FETCH_SIZE", d[1], "copy", "--calibrate-copy 1024"),
+                    ("WRITE_SIZE", d[2], "step", "--steps 3 --warmup 1 --no-extra --no-cpu"),
+                    ("WRITE_SIZE", d[3], "copy", "--calibrate-copy 1024"))]
+        summarize_counters(d[0], d[1], d[2], d[3], 1024, cmds)
+        return 0
     if args.gpus != 1:
         print("bench.py: this attention path runs on one GPU; --gpus %d is not supported "
               "(sharding over (batch, head) is described in the design notes, not built)"
