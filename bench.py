@@ -155,7 +155,8 @@ def load_traffic(kernel):
     return e.get("bytes_per_launch")
 
 
-# The step's kernels as rocprofv3 names them (the decode call launches two).
+# The step's kernels as rocprofv3 names them (a decode with more than one
+# split also launches the merge; the step's decode has one split).
 STEP_KERNELS = {
     "fwd_noncausal": ["fwd_bf16_kernel<64, 0, 64, 4, false>"],
     "fwd_causal": ["fwd_bf16_kernel<64, 1, 64, 4, false>"],
@@ -208,11 +209,11 @@ def summarize_counters(fetch_step, fetch_copy, write_step, write_copy, copy_mib,
         e = {}
         for counter, key in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
             kib = 0.0
-            for n in names:
+            for i, n in enumerate(names):
                 hits = [v for k, v in vals[counter].items() if n in k]
-                if not hits:
+                if not hits and i == 0:
                     raise SystemExit("kernel %s not in the %s run" % (n, counter))
-                kib += hits[0]
+                kib += hits[0] if hits else 0.0
             e[counter + "_KiB"] = round(kib, 1)
             e[key + "_bytes"] = round(kib * 1024.0 / out["copy_counter_per_byte"][counter], 1)
         e["bytes_per_launch"] = int(round(e["fetch_bytes"] + e["write_bytes"]))

@@ -170,6 +170,9 @@ int fa_decode_num_splits(int B, int H, int N_max, int d, int num_splits);
  * lse_s in the workspace, and a merge kernel combines them with the block-merge
  * rule of the running (m, l) statistics ("flash-attention" page, "como
  * funciona"): LSE = ln sum_s exp(lse_s), O = sum_s exp(lse_s - LSE) o_s.
+ * With a single split that partial is the result: the split kernel stores O
+ * and LSE itself (the same values the merge would store) and no merge runs.
+ * The automatic count is one split when N_max <= 1024.
  *
  * q         : [B, H, 1, d] queries (the newest token of each sequence).
  * k, v      : [B, H, N_max, d] caches; rows at and beyond L_b are never read.

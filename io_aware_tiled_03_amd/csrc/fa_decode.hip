@@ -22,6 +22,12 @@ namespace {
 
 template <int N_> using ic = std::integral_constant<int, N_>;
 
+// One output element in the output dtype (bf16: round to nearest even).
+__device__ __forceinline__ void store_out(uint16_t* p, float v) {
+    *reinterpret_cast<__bf16*>(p) = (__bf16)v;
+}
+__device__ __forceinline__ void store_out(float* p, float v) { *p = v; }
+
 template <typename T> struct Elem;
 template <> struct Elem<uint16_t> {   // bf16: 8 elements per 16-byte piece
     static constexpr int PER16 = 8;
@@ -77,7 +83,12 @@ template <typename T, int D>
 __global__ __launch_bounds__(256) void decode_split_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int* __restrict__ seqlens, int B, int H, int N_max, int chunk, float scale_log2,
-    float tau, float* __restrict__ ws_o, float* __restrict__ ws_lse) {
+    float tau, float* __restrict__ ws_o, float* __restrict__ ws_lse, T* __restrict__ O,
+    float* __restrict__ LSE) {
+    // O and LSE non-null: there is a single split, whose normalised partial
+    // is already the result, so it is stored as the merge would store it
+    // (the merge of one split multiplies by exp(0) = 1 and adds ln 1 = 0) and
+    // the merge is not launched.
     constexpr int PER = Elem<T>::PER16;
     constexpr int CPR = D / PER;          // lanes per key row
     constexpr int KPL = 64 / CPR;         // keys per wave load instruction
@@ -99,6 +110,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     const int L = min(max(seqlens[b], 0), N_max);
     const int kb = s * chunk, ke = min(L, kb + chunk);
     if (kb >= ke) {   // empty split: contributes nothing to the merge
+        if (O) {          // an empty sequence: O = 0, LSE = -inf (the empty sum)
+            if (tid < D) store_out(O + bh * D + tid, 0.f);
+            if (tid == 0) LSE[bh] = neg_inf();
+            return;
+        }
         if (tid < D) ws_o[wsi * D + tid] = 0.f;
         if (tid == 0) ws_lse[wsi] = neg_inf();
         return;
@@ -219,8 +235,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
             lt += sl[w] * a;
             ot += so[w][tid] * a;
         }
-        ws_o[wsi * D + tid] = ot / lt;
-        if (tid == 0) ws_lse[wsi] = M * tau + __logf(lt);
+        if (O) {
+            store_out(O + bh * D + tid, ot / lt);
+            if (tid == 0) LSE[bh] = M * tau + __logf(lt);
+        } else {
+            ws_o[wsi * D + tid] = ot / lt;
+            if (tid == 0) ws_lse[wsi] = M * tau + __logf(lt);
+        }
     }
 }
 
@@ -262,13 +283,7 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(
     const float inv = sum > 0.f ? 1.f / sum : 0.f;
 #pragma unroll
     for (int i = 0; i < PL; ++i) {
-        const float v = acc[i] * inv;
-        if constexpr (sizeof(T) == 2) {
-            typedef __bf16 bf;
-            reinterpret_cast<bf*>(O)[(size_t)bh * D + t + 64 * i] = (bf)v;
-        } else {
-            O[(size_t)bh * D + t + 64 * i] = v;
-        }
+        store_out(O + (size_t)bh * D + t + 64 * i, acc[i] * inv);
     }
     if (t == 0) LSE[bh] = (M == neg_inf()) ? neg_inf() : M + __logf(sum);
 }
@@ -509,9 +524,11 @@ template <typename T, int D>
 void launch(const DecodeArgs& a, hipStream_t st) {
     hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(a.num_splits * a.B * a.H), dim3(256), 0, st,
                        (const T*)a.q, (const T*)a.k, (const T*)a.v, a.seqlens, a.B, a.H, a.N_max,
-                       a.chunk, a.tau * kLog2e, a.tau, a.ws_o, a.ws_lse);
-    hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.B * a.H), dim3(64), 0, st, a.ws_o,
-                       a.ws_lse, a.num_splits, a.B * a.H, (T*)a.o, a.lse);
+                       a.chunk, a.tau * kLog2e, a.tau, a.ws_o, a.ws_lse,
+                       a.num_splits == 1 ? (T*)a.o : nullptr, a.num_splits == 1 ? a.lse : nullptr);
+    if (a.num_splits > 1)
+        hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.B * a.H), dim3(64), 0, st, a.ws_o,
+                           a.ws_lse, a.num_splits, a.B * a.H, (T*)a.o, a.lse);
 }
 
 }  // namespace
@@ -527,8 +544,12 @@ int decode_splits(int B, int H, int N_max, int d, int requested) {
         const int c = decode_chunk(N_max, requested);
         return (N_max + c - 1) / c;
     }
-    // Automatic: the shortest chunk (>= 256 keys) that keeps the grid at or
-    // below 16384 workgroups.
+    // Automatic: one split when no sequence can hold more than 1024 keys
+    // (such a decode is bound by launch and memory latency: the split kernel
+    // then stores the result itself and the merge launch is saved, 9 us
+    // instead of 11-12 us at 8x16x1024x64); otherwise the shortest chunk
+    // (>= 256 keys) that keeps the grid at or below 16384 workgroups.
+    if (N_max <= 1024) return 1;
     const long bh = (long)B * H;
     int c = 256;
     while (c < N_max && bh * ((N_max + c - 1) / c) > 16384) c *= 2;

@@ -152,7 +152,10 @@ def test_decode_rejects_bad_arguments():
 
 def test_decode_split_rule():
     fa, lib = _lib()
-    # automatic splits: >= 256 keys per split unless that would exceed 16384 workgroups
+    # automatic splits: one when N_max <= 1024, else >= 256 keys per split
+    # unless that would exceed 16384 workgroups
+    assert lib.fa_decode_num_splits(8, 16, 1024, 64, 0) == 1
+    assert lib.fa_decode_num_splits(8, 16, 2048, 64, 0) == 8
     assert lib.fa_decode_num_splits(1, 1, 8192, 128, 0) == 32
     assert lib.fa_decode_num_splits(64, 32, 8192, 128, 0) == 8
     assert lib.fa_decode_num_splits(1, 1, 100, 128, 0) == 1

@@ -32,11 +32,13 @@ def test_decode_small(num_splits, d, dtype):
     assert_close(lse, rl, dtype, "LSE", kind="lse")
 
 
-def test_decode_empty_sequence():
+@pytest.mark.parametrize("num_splits", [1, 2])
+def test_decode_empty_sequence(num_splits):
     """L_b = 0 (clamped length): no visible key, O = 0 and LSE = -inf by definition
-    of an empty sum; the other sequences are unaffected."""
+    of an empty sum; the other sequences are unaffected.  One split stores the
+    result from the split kernel itself, two go through the merge."""
     x = fa_inputs.decode_inputs(2, 2, 128, 128, "bf16", 9100, seqlens=[0, 100])
-    o, lse = _run(x, 128, 0.1, 0)
+    o, lse = _run(x, 128, 0.1, num_splits)
     assert np.all(o[0] == 0) and np.all(np.isneginf(lse[0]))
     ro, rl = orc.decode_fwd(x["q"].f64(), x["k"].f64(), x["v"].f64(), x["seqlens"], 0.1,
                             batches=[1])
@@ -60,6 +62,16 @@ def test_decode_workload_full():
         ro[b], rl[b] = ob[0], lb[0]
     assert_close(o, ro, "bf16", "O")
     assert_close(lse, rl, "bf16", "LSE", kind="lse")
+
+
+def test_decode_one_split_matches_merge_bits():
+    """One split written by the split kernel directly equals, bit for bit, the
+    merge of that one split (weight exp(0) = 1, ln 1 = 0), which is what two
+    splits of which the second is empty (L_b <= chunk) reduce to."""
+    x = fa_inputs.decode_inputs(3, 2, 256, 64, "bf16", 9300, seqlens=[64, 100, 128])
+    o1, l1 = _run(x, 64, 0.125, 1)   # chunk 256: one split, no merge
+    o2, l2 = _run(x, 64, 0.125, 2)   # chunk 128: the second split is empty, merged
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
 
 
 def test_decode_splits_agree():
