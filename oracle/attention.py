@@ -308,6 +308,54 @@ def attention_bwd(q, k, v, do, tau, causal, window=None, sinks=0, d_from_saved_b
     return out
 
 
+def attention_dq_rows(q, k, v, do, tau, causal, rows, chunk=64):
+    """dQ and D of the requested rows of one head, without the full N x N matrices.
+
+    The same hand-derived gradient as attention_bwd_head, restricted to rows:
+    for each row i, P_i over its visible keys, dP_i = dO_i V^T,
+    D_i = sum_j P_ij dP_ij, dS_i = P_i o (dP_i - D_i), dQ_i = tau dS_i K.
+    Score rows are formed in chunks of ``chunk`` rows (under the causal mask
+    only against keys up to the chunk's last row).  Returns (dq, D)."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    rows = np.asarray(rows, dtype=np.int64)
+    dq = np.empty((len(rows), k.shape[1]))
+    D = np.empty(len(rows))
+    for a in range(0, len(rows), chunk):
+        r = rows[a:a + chunk]
+        kmax = (int(r.max()) + 1) if causal else k.shape[0]
+        p = probs(scores(q[r], k[:kmax], tau, r, causal))[0]
+        dp = do[r] @ v[:kmax].T
+        Dr = (p * dp).sum(axis=1)
+        dq[a:a + len(r)] = tau * ((p * (dp - Dr[:, None])) @ k[:kmax])
+        D[a:a + len(r)] = Dr
+    return dq, D
+
+
+def attention_dkdv_last_keys(q, k, v, do, tau, nk):
+    """dK and dV of the last nk keys of one head under the causal mask.
+
+    Key j is visible only to queries i >= j, so the last nk keys receive
+    gradient only from the last nk query rows: their full score rows give P,
+    dP = dO V^T, D and dS = P o (dP - D) (as attention_bwd_head), and then
+    dV_j = sum_i P_ij dO_i and dK_j = tau sum_i dS_ij Q_i over those rows.
+    Returns (dk, dv) of shape [nk, d]."""
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    v = np.asarray(v, dtype=np.float64)
+    do = np.asarray(do, dtype=np.float64)
+    n = q.shape[0]
+    r = np.arange(n - nk, n)
+    p = probs(scores(q[r], k, tau, r, True))[0]
+    dp = do[r] @ v.T
+    ds = p * (dp - (p * dp).sum(axis=1)[:, None])
+    dv = p[:, n - nk:].T @ do[r]
+    dk = tau * (ds[:, n - nk:].T @ q[r])
+    return dk, dv
+
+
 def decode_fwd(q, k, v, seqlens, tau, heads=None, batches=None):
     """One query per (b, h) against keys [0, L_b) of the cache; no mask inside.
 

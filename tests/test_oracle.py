@@ -251,6 +251,63 @@ def test_backward_column_sum_invariants(causal):
 
 
 @pytest.mark.parametrize("causal", [False, True])
+def test_dq_rows_match_finite_differences_and_full_backward(causal):
+    """attention_dq_rows (the row-sampled dQ for heads too long for the full
+    matrices): central differences of L = sum(O o dO) with respect to the
+    sampled rows of Q (rel <= 1e-6), and the full-head backward's rows, with
+    chunks that split the sampled rows unevenly."""
+    n, d, tau, h = 11, 4, 0.7, 1e-6
+    rng = np.random.Generator(np.random.PCG64(140 + causal))
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    rows = np.array([0, 3, 4, 10])
+    dq, D = orc.attention_dq_rows(q, k, v, do, tau, causal, rows, chunk=3)
+
+    def loss(qq):
+        o, _ = orc.attention_fwd_head(qq, k, v, tau, causal)
+        return float((o * do).sum())
+
+    num = np.empty((len(rows), d))
+    for a, i in enumerate(rows):
+        for j in range(d):
+            qp, qm = q.copy(), q.copy()
+            qp[i, j] += h
+            qm[i, j] -= h
+            num[a, j] = (loss(qp) - loss(qm)) / (2 * h)
+    np.testing.assert_allclose(dq, num, rtol=1e-6, atol=1e-8)
+    g = orc.attention_bwd_head(q, k, v, do, tau, causal)
+    np.testing.assert_allclose(dq, g["dq"][rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(D, g["D"][rows], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("nk", [1, 3, 7])
+def test_dkdv_last_keys_match_finite_differences_and_full_backward(nk):
+    """attention_dkdv_last_keys: central differences of L = sum(O o dO) with
+    respect to the last keys and values (rel <= 1e-6), and the full-head causal
+    backward's last rows."""
+    n, d, tau, h = 10, 3, 0.8, 1e-6
+    rng = np.random.Generator(np.random.PCG64(150 + nk))
+    q, k, v, do = (rng.standard_normal((n, d)) for _ in range(4))
+    dk, dv = orc.attention_dkdv_last_keys(q, k, v, do, tau, nk)
+
+    def loss(kk, vv):
+        o, _ = orc.attention_fwd_head(q, kk, vv, tau, True)
+        return float((o * do).sum())
+
+    for got, idx in ((dk, 0), (dv, 1)):
+        num = np.empty((nk, d))
+        for a, i in enumerate(range(n - nk, n)):
+            for j in range(d):
+                plus, minus = [k.copy(), v.copy()], [k.copy(), v.copy()]
+                plus[idx][i, j] += h
+                minus[idx][i, j] -= h
+                num[a, j] = (loss(*plus) - loss(*minus)) / (2 * h)
+        np.testing.assert_allclose(got, num, rtol=1e-6, atol=1e-8)
+    g = orc.attention_bwd_head(q, k, v, do, tau, True)
+    np.testing.assert_allclose(dk, g["dk"][n - nk:], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(dv, g["dv"][n - nk:], rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("n,d", [(5, 3), (9, 4), (16, 8)])
 def test_backward_matches_finite_differences(causal, n, d):
     """Central differences of L = sum(O o dO) match dQ, dK and dV (rel <= 1e-6)."""
