@@ -258,7 +258,7 @@ def cpu_baseline(xh, B, H, N, d, tau, budget_s=10.0):
                       % (heads, B * H, dt)}
 
 
-def bench_extra(fa, reps=20):
+def bench_extra(fa, reps=50):
     """Full-size long-prefill, decode and backward workloads, each vs its roofline."""
     import torch
     out = {}
@@ -267,7 +267,8 @@ def bench_extra(fa, reps=20):
     stream = torch.cuda.current_stream()
 
     def time_it(fn, reps):
-        for _ in range(3):
+        """Median of reps HIP-event pairs on the stream, after 10 warm-up calls."""
+        for _ in range(10):
             fn()
         torch.cuda.synchronize()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
