@@ -19,9 +19,7 @@ import ctypes
 import math
 import os
 
-# FA_LIB may name another build of the same library (for example a tuning build).
-LIB_PATH = os.environ.get("FA_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
-                                                    "libfa.so")
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_F32, FA_BF16 = 0, 1
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED",
@@ -91,7 +89,7 @@ def _dtype_code(t):
         return FA_BF16
     if t.dtype == torch.float32:
         return FA_F32
-    raise TypeError("unsupported dtype %s" % t.dtype)
+    raise TypeError("unsupported dtype %s (bfloat16 or float32)" % t.dtype)
 
 
 def _stream(t):
@@ -99,20 +97,52 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def _need(t, name):
-    if not t.is_cuda:
-        raise ValueError("%s must be a GPU tensor" % name)
+def _expect(t, name, shape, dtype):
+    """t has exactly this shape and dtype and is contiguous (ValueError otherwise).
+
+    The library receives bare device pointers: a tensor smaller than the
+    kernels assume, or of another element size, would be read or written out
+    of bounds on the device, so every tensor is checked before any call."""
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
 
 
-def _block_args(block_mask, block_size, H):
+def _same_gpu(tensors):
+    """Every tensor lives on one and the same GPU (ValueError otherwise)."""
+    dev = None
+    for name, t in tensors:
+        if not t.is_cuda:
+            raise ValueError("%s must be a GPU tensor" % name)
+        if dev is None:
+            dev = t.device
+        elif t.device != dev:
+            raise ValueError("%s is on %s, the other tensors on %s" % (name, t.device, dev))
+
+
+def _block_args(block_mask, block_size, H, N):
     import torch
-    _need(block_mask, "block_mask")
+    bq, bk = (int(x) for x in block_size)
+    if bq < 1 or bk < 1:
+        raise ValueError("block sizes must be positive")
     if block_mask.dtype != torch.uint8 or block_mask.dim() != 3:
-        raise TypeError("block_mask must be a uint8 tensor [mask_heads, nbq, nbk]")
-    bq, bk = block_size
-    return block_mask.data_ptr(), int(block_mask.shape[0]), int(bq), int(bk)
+        raise ValueError("block_mask must be a uint8 tensor [mask_heads, nbq, nbk]")
+    heads = int(block_mask.shape[0])
+    if heads not in (1, H):
+        raise ValueError("block_mask has %d heads, expected 1 or %d" % (heads, H))
+    _expect(block_mask, "block_mask", (heads, -(-N // bq), -(-N // bk)), torch.uint8)
+    return block_mask.data_ptr(), heads, bq, bk
+
+
+def _check_dense(named, lse, B, H, N, d, dt):
+    """named: (name, tensor) pairs that must all be [B, H, N, d] of dtype dt."""
+    import torch
+    for n, t in named:
+        _expect(t, n, (B, H, N, d), dt)
+    _expect(lse, "lse", (B, H, N), torch.float32)
 
 
 def fwd(q, k, v, tau=None, causal=False, o=None, lse=None, window=None, sinks=0, dropout=None,
@@ -125,21 +155,26 @@ def fwd(q, k, v, tau=None, causal=False, o=None, lse=None, window=None, sinks=0,
     With block_mask (uint8 [1 or H, ceil(N/bq), ceil(N/bk)], block_size = (bq, bk)):
     block-sparse attention, via fa_fwd_block_sparse."""
     import torch
-    for t, n in ((q, "q"), (k, "k"), (v, "v")):
-        _need(t, n)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
     B, H, N, d = q.shape
+    _dtype_code(q)
     tau = 1.0 / math.sqrt(d) if tau is None else float(tau)
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None else lse
+    _check_dense((("q", q), ("k", k), ("v", v), ("o", o)), lse, B, H, N, d, q.dtype)
+    devs = [("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse)]
     if block_mask is not None:
         if window is not None or dropout is not None:
             raise ValueError("block-sparse attention takes no window and no dropout")
+        bargs = _block_args(block_mask, block_size, H, N)
+        _same_gpu(devs + [("block_mask", block_mask)])
         st = lib().fa_fwd_block_sparse(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
                                        lse.data_ptr(), B, H, N, d, tau, int(bool(causal)),
-                                       *_block_args(block_mask, block_size, H), _dtype_code(q),
-                                       _stream(q))
+                                       *bargs, _dtype_code(q), _stream(q))
         check("fa_fwd_block_sparse", st)
         return o, lse
+    _same_gpu(devs)
     if dropout is not None:
         if window is not None:
             raise ValueError("dropout is supported with no mask or the causal mask")
@@ -171,20 +206,42 @@ def decode_num_splits(B, H, N_max, d, num_splits=0):
     return int(lib().fa_decode_num_splits(B, H, N_max, d, num_splits))
 
 
-def decode(q, k, v, seqlens_k, tau=None, num_splits=0, o=None, lse=None, workspace=None):
-    """One query per (b, h) against the KV cache rows [0, seqlens_k[b]), via fa_decode."""
+def _workspace(ws, need, device, name="workspace"):
+    """A caller's workspace (any dtype, contiguous, at least `need` bytes, which
+    the library checks again) or a new one of `need` bytes."""
     import torch
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (seqlens_k, "seqlens_k")):
-        _need(t, n)
-    if seqlens_k.dtype != torch.int32:
-        raise TypeError("seqlens_k must be int32")
+    if ws is None:
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=device)
+    if not ws.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    if ws.numel() * ws.element_size() < need:
+        raise ValueError("%s holds %d bytes, the call needs %d"
+                         % (name, ws.numel() * ws.element_size(), need))
+    return ws
+
+
+def decode(q, k, v, seqlens_k, tau=None, num_splits=0, o=None, lse=None, workspace=None):
+    """One query per (b, h) against the KV cache rows [0, seqlens_k[b]), via fa_decode.
+
+    q [B, H, 1, d]; k, v [B, H, N_max, d] of q's dtype; seqlens_k int32 [B]."""
+    import torch
+    if k.dim() != 4:
+        raise ValueError("k must be [B, H, N_max, d]")
     B, H, N_max, d = k.shape
+    _dtype_code(q)
     tau = 1.0 / math.sqrt(d) if tau is None else float(tau)
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    _expect(q, "q", (B, H, 1, d), q.dtype)
+    _expect(k, "k", (B, H, N_max, d), q.dtype)
+    _expect(v, "v", (B, H, N_max, d), q.dtype)
+    _expect(o, "o", (B, H, 1, d), q.dtype)
+    _expect(lse, "lse", (B, H), torch.float32)
+    _expect(seqlens_k, "seqlens_k", (B,), torch.int32)
     need = decode_workspace_bytes(B, H, N_max, d, num_splits)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q.device)
+    _same_gpu([("q", q), ("k", k), ("v", v), ("seqlens_k", seqlens_k), ("o", o), ("lse", lse),
+               ("workspace", workspace)])
     st = lib().fa_decode(q.data_ptr(), k.data_ptr(), v.data_ptr(), seqlens_k.data_ptr(), B, H,
                          N_max, d, tau, o.data_ptr(), lse.data_ptr(), int(num_splits),
                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
@@ -209,20 +266,27 @@ def decode_paged(q, k_pages, v_pages, block_table, seqlens_k, tau=None, num_spli
     q [B, Hq, 1, d]; k_pages, v_pages [num_pages, Hkv, page_size, d];
     block_table int32 [B, max_pages]; seqlens_k int32 [B]."""
     import torch
-    for t, n in ((q, "q"), (k_pages, "k_pages"), (v_pages, "v_pages"),
-                 (block_table, "block_table"), (seqlens_k, "seqlens_k")):
-        _need(t, n)
-    if block_table.dtype != torch.int32 or seqlens_k.dtype != torch.int32:
-        raise TypeError("block_table and seqlens_k must be int32")
+    if q.dim() != 4 or k_pages.dim() != 4 or block_table.dim() != 2:
+        raise ValueError("q [B, Hq, 1, d], pages [num_pages, Hkv, page_size, d], "
+                         "block_table [B, max_pages]")
     B, Hq, _, d = q.shape
     num_pages, Hkv, page_size, _ = k_pages.shape
     max_pages = block_table.shape[1]
+    _dtype_code(q)
     tau = 1.0 / math.sqrt(d) if tau is None else float(tau)
     o = torch.empty_like(q) if o is None else o
     lse = torch.empty((B, Hq), dtype=torch.float32, device=q.device) if lse is None else lse
+    _expect(q, "q", (B, Hq, 1, d), q.dtype)
+    _expect(k_pages, "k_pages", (num_pages, Hkv, page_size, d), q.dtype)
+    _expect(v_pages, "v_pages", (num_pages, Hkv, page_size, d), q.dtype)
+    _expect(block_table, "block_table", (B, max_pages), torch.int32)
+    _expect(seqlens_k, "seqlens_k", (B,), torch.int32)
+    _expect(o, "o", (B, Hq, 1, d), q.dtype)
+    _expect(lse, "lse", (B, Hq), torch.float32)
     need = decode_paged_workspace_bytes(B, Hq, Hkv, page_size, max_pages, d, num_splits)
-    if workspace is None:
-        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q.device)
+    workspace = _workspace(workspace, need, q.device)
+    _same_gpu([("q", q), ("k_pages", k_pages), ("v_pages", v_pages), ("block_table", block_table),
+               ("seqlens_k", seqlens_k), ("o", o), ("lse", lse), ("workspace", workspace)])
     st = lib().fa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
                                block_table.data_ptr(), seqlens_k.data_ptr(), B, Hq, Hkv,
                                num_pages, page_size, max_pages, d, tau, o.data_ptr(),
@@ -247,16 +311,23 @@ def bwd(q, k, v, o, lse, do, tau=None, causal=False, dq=None, dk=None, dv=None, 
     With dropout = (p, seed, offset): the backward of fa_fwd_dropout, via fa_bwd_dropout.
     With block_mask: the backward of fa_fwd_block_sparse, via fa_bwd_block_sparse."""
     import torch
-    for t, n in ((q, "q"), (k, "k"), (v, "v"), (o, "o"), (lse, "lse"), (do, "do")):
-        _need(t, n)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
     B, H, N, d = q.shape
+    _dtype_code(q)
     tau = 1.0 / math.sqrt(d) if tau is None else float(tau)
     dq = torch.empty_like(q) if dq is None else dq
     dk = torch.empty_like(k) if dk is None else dk
     dv = torch.empty_like(v) if dv is None else dv
-    if workspace is None:
-        workspace = torch.empty(bwd_workspace_bytes(B, H, N) // 4, dtype=torch.float32,
-                                device=q.device)
+    _check_dense((("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk),
+                  ("dv", dv)), lse, B, H, N, d, q.dtype)
+    workspace = _workspace(workspace, bwd_workspace_bytes(B, H, N), q.device)
+    bargs = None
+    if block_mask is not None:
+        bargs = _block_args(block_mask, block_size, H, N)
+    _same_gpu([("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("do", do), ("dq", dq),
+               ("dk", dk), ("dv", dv), ("workspace", workspace)]
+              + ([("block_mask", block_mask)] if block_mask is not None else []))
     args = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), lse.data_ptr(),
             do.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, H, N, d, tau,
             int(bool(causal)), workspace.data_ptr(),
@@ -264,8 +335,7 @@ def bwd(q, k, v, o, lse, do, tau=None, causal=False, dq=None, dk=None, dv=None, 
     if block_mask is not None:
         if window is not None or dropout is not None or stage is not None:
             raise ValueError("block-sparse backward: no window, no dropout, whole backward only")
-        bargs = args[:15] + _block_args(block_mask, block_size, H) + args[15:]
-        check("fa_bwd_block_sparse", lib().fa_bwd_block_sparse(*bargs))
+        check("fa_bwd_block_sparse", lib().fa_bwd_block_sparse(*(args[:15] + bargs + args[15:])))
     elif dropout is not None:
         if window is not None or stage is not None:
             raise ValueError("dropout backward: no window, whole backward only")

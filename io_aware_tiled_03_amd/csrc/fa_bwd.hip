@@ -403,8 +403,11 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const int kend = CAUSAL ? min(N, q0 + BR) : N;
     const int ntiles = (kend + BC - 1) / BC;
 
-    // Keys past N are zero rows (buffer descriptor), so their dS meets K = 0
-    // in dQ += dS K and needs no mask; only the causal diagonal is masked.
+    // Keys past N are zero rows (buffer descriptor) but still get a
+    // probability exp2(-LSE) from their zero score, which overflows to inf
+    // for a row whose LSE is below about -88; inf times their K = 0 would
+    // make the row's dQ NaN, so the tile holding them runs the masked body,
+    // which gives them p = 0 (as the forward does).
     // Block-sparse: the mask row of this wave's query block (waves hold 32
     // rows, blocks >= 32) and the bit of the key block holding key j.
     const unsigned char* bmrow = nullptr;
@@ -449,7 +452,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
                 float p = fast_exp2(__builtin_fmaf(sacc[r], scale_log2, -lse2));
                 if constexpr (MASK) {
                     const int kk = k0 + kb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7);
-                    if (CAUSAL && (kk > qrow || (WIN && qrow - kk >= window && kk >= sinks))) p = 0.f;
+                    if (kk >= N ||
+                        (CAUSAL && (kk > qrow || (WIN && qrow - kk >= window && kk >= sinks))))
+                        p = 0.f;
                 }
                 if constexpr (DROP) {
                     const bool kept = drop.keep(dw[r >> 2], r & 3);
@@ -505,9 +510,9 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
         if constexpr (BLK) return (int)s_list[min(p, max(nact - 1, 0))];
         return p < nsk ? p : tlo + (p - nsk);
     };
-    // tiles in [tfull, tdiag) precede every query of the workgroup and lie
-    // inside every row's window: no mask
-    const int jsplit = CAUSAL ? min(ntiles, q0 / BC) : ntiles;
+    // tiles in [tfull, tdiag) precede every query of the workgroup, lie
+    // inside every row's window and hold no key past N: no mask
+    const int jsplit = min(ntiles, CAUSAL ? q0 / BC : N / BC);
     const int tdiag = max(tfull, jsplit);
     int p1 = nsk + (tfull - tlo), p2 = nsk + (tdiag - tlo), p3 = nsk + (ntiles - tlo);
     if constexpr (BLK) p1 = p2 = 0, p3 = nact;   // every listed tile masked

@@ -63,20 +63,10 @@ __device__ __forceinline__ float row_sum(float x) {
 #ifndef FA_DECODE_U
 #define FA_DECODE_U 4
 #endif
-#ifndef FA_DECODE_ROTATE
-#define FA_DECODE_ROTATE 0
-#endif
-#ifndef FA_DECODE_NT
-#define FA_DECODE_NT 1
-#endif
-
-// Streaming 16-byte load of the KV cache (read once: optionally non-temporal).
+// Streaming 16-byte load of the KV cache (read once: non-temporal, so it does
+// not displace reused lines in the caches).
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
-#if FA_DECODE_NT
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-#else
-    return ld16(p);
-#endif
 }
 
 template <typename T, int D>
@@ -174,18 +164,10 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     };
 
     // The chunk is walked in stages of KPI keys; wave w takes stages w, w+4, ...
-    // Each workgroup starts at a rotated stage so that concurrently running
-    // workgroups, whose chunks begin at large power-of-two offsets, do not all
-    // hit the same HBM channels in lock step (the softmax merge does not depend
-    // on the order of the keys).  Two register stages: the loads of the next
-    // keys are in flight while the current ones are consumed.
+    // Two register stages: the loads of the next keys are in flight while the
+    // current ones are consumed.
     const int nst = (ke - kb + KPI - 1) / KPI;
-    const int rot = (int)(blockIdx.x % (unsigned)nst) * FA_DECODE_ROTATE;
-    auto stage_key = [&](int t) {
-        int p = t + rot;
-        p = p >= nst ? p - nst : p;
-        return kb + p * KPI;
-    };
+    auto stage_key = [&](int t) { return kb + t * KPI; };
     int t = wave;
     if (t < nst) {
         u32x4 ka[U], va[U], kn[U], vn[U];
@@ -532,52 +514,6 @@ void launch(const DecodeArgs& a, hipStream_t st) {
 }
 
 }  // namespace
-
-int decode_chunk(int N_max, int splits) {
-    int c = (N_max + splits - 1) / splits;
-    return (c + 63) / 64 * 64;
-}
-
-int decode_splits(int B, int H, int N_max, int d, int requested) {
-    (void)d;
-    if (requested > 0) {
-        const int c = decode_chunk(N_max, requested);
-        return (N_max + c - 1) / c;
-    }
-    // Automatic: one split when no sequence can hold more than 1024 keys
-    // (such a decode is bound by launch and memory latency: the split kernel
-    // then stores the result itself and the merge launch is saved, 9 us
-    // instead of 11-12 us at 8x16x1024x64); otherwise the shortest chunk
-    // (>= 256 keys) that keeps the grid at or below 16384 workgroups.
-    if (N_max <= 1024) return 1;
-    const long bh = (long)B * H;
-    int c = 256;
-    while (c < N_max && bh * ((N_max + c - 1) / c) > 16384) c *= 2;
-    return (N_max + c - 1) / c;
-}
-
-size_t decode_ws_bytes(int B, int H, int d, int splits) {
-    return (size_t)splits * B * H * (size_t)(d + 1) * sizeof(float);
-}
-
-int decode_paged_chunk(int max_keys, int splits) {
-    const int c = (max_keys + splits - 1) / splits;
-    return (c + 127) / 128 * 128;
-}
-
-int decode_paged_splits(int B, int Hq, int Hkv, int max_keys, int requested) {
-    if (requested > 0) {
-        const int c = decode_paged_chunk(max_keys, requested);
-        return (max_keys + c - 1) / c;
-    }
-    // Automatic: the shortest chunk (>= 512 keys) that keeps the grid at or
-    // below 4096 workgroups (each workgroup holds a whole CU's worth of LDS).
-    const long units = (long)B * Hkv * ((Hq / Hkv + 15) / 16);
-    int c = 512;
-    while (c < max_keys && units * ((max_keys + c - 1) / c) > 4096) c *= 2;
-    c = decode_paged_chunk(max_keys, (max_keys + c - 1) / c);
-    return (max_keys + c - 1) / c;
-}
 
 void launch_decode_paged(const PagedDecodeArgs& a, hipStream_t st) {
     a.d == 64 ? launch_paged<64>(a, st) : launch_paged<128>(a, st);

@@ -7,8 +7,6 @@
 //                             i%32, the same eight k-slots; C (32 x 32) fp32:
 //                             lane i, register r holds
 //                             row 8*(r/4) + 4*(i/32) + r%4, column i%32.
-//   v_mfma_f32_32x32x2_f32    A: lane i holds row i%32, k = i/32; B: column
-//                             i%32, k = i/32; C as above.
 // A and B always receive the same logical k in the same (half, slot), so the
 // hardware's internal k order never matters; only the row/column/C mapping
 // above does.
@@ -59,10 +57,6 @@ __device__ __forceinline__ f32x4 mfma16x16x16(const u32x2& a, const u32x2& b, co
                                                       __builtin_bit_cast(v4i16, b), c, 0, 0, 0);
 }
 
-__device__ __forceinline__ f32x16 mfma32x32x2f32(float a, float b, const f32x16& c) {
-    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
-}
-
 // exp2 on the transcendental unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -74,9 +68,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
-    return __builtin_bit_cast(float, (uint32_t)h << 16);
-}
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
 
@@ -134,13 +125,6 @@ __device__ __forceinline__ u32x4 lds_read_tr16_x2(const void* lds_lo, const void
     return r;
 }
 
-// a.lo*b.lo + a.hi*b.hi + c for packed bf16 pairs, fp32 accumulation.
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a),
-                                           __builtin_bit_cast(bf16x2, b), c, false);
-}
-
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
 
 // Raw buffer resource over `bytes` bytes at `base` (gfx9 descriptor word 3 =
@@ -150,9 +134,6 @@ typedef __amdgpu_buffer_rsrc_t rsrc_t;
 __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                              0x00020000);
-}
-__device__ __forceinline__ u32x4 buf_ld16(rsrc_t r, uint32_t byte_off) {
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0));
 }
 // The same load marked non-temporal (data read once: keep it from displacing
 // reused lines in the caches).
@@ -286,26 +267,7 @@ __device__ __forceinline__ void buf_ld16_lds(rsrc_t r, uint32_t byte_off, void* 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds_base, 16,
                                              byte_off, 0, 0, 0);
 }
-// Direct global -> LDS copy of 16 bytes per lane from a per-lane 64-bit
-// address (no 4 GiB descriptor limit); lane i's bytes land at lds_base + 16*i
-// (lds_base wave-uniform, passed in M0).  Issued as inline assembly so that
-// the compiler keeps no bookkeeping of it: where such bookkeeping meets a
-// branch it is merged conservatively into a wait for every outstanding copy
-// before the next LDS read.  The caller orders the copy itself: wait_vmem_le
-// before reading the data, wait_lgkm before refilling a buffer whose reads
-// may still be in flight.
-__device__ __forceinline__ void glb_ld16_lds_async(const void* src, void* lds_base) {
-    const uint32_t m0 = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) void*)lds_base;
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
-}
-__device__ __forceinline__ void wait_lgkm() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-// Wait until at most N vector-memory operations of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmem_le() {
-    static_assert(N >= 0 && N < 64, "vmcnt field");
-    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 
 }  // namespace fa

@@ -13,8 +13,8 @@
 //    operand of S^T = K Q^T, so in the result every lane holds one query
 //    (column) and 16 keys per 32-key block (rows): the row max/sum of the
 //    softmax is a register loop plus one exchange between wave halves;
-//  * K rows are stored in LDS in the order pi^-1 (see kperm/kperm_inv) so that
-//    lane m reading physical row m gets key pi(m), chosen such that the
+//  * K rows are stored in LDS permuted (see kperm) so that lane m reading
+//    physical row m gets key kperm(m), chosen such that the
 //    registers of S^T already hold, per lane half, 8 consecutive keys: the
 //    bf16-rounded P^T feeds the P V product as the B operand directly;
 //  * V stays row-major in LDS; the A operand of O^T = V^T P^T comes from the
@@ -49,10 +49,6 @@ __device__ __forceinline__ int kperm(int m) {
     const int j = 4 * (m >> 3) + (m & 3);
     return 16 * (j >> 3) + 8 * ((m >> 2) & 1) + (j & 7);
 }
-// Inverse of kperm: the LDS row that key r of a 32-key block is stored in.
-__device__ __forceinline__ int kperm_inv(int r) {
-    return 8 * (2 * (r >> 4) + ((r >> 2) & 1)) + 4 * ((r >> 3) & 1) + (r & 3);
-}
 
 #ifndef FA_FWD_RESCALE_LOG2
 #define FA_FWD_RESCALE_LOG2 8.0f
@@ -72,20 +68,6 @@ __device__ __forceinline__ int kperm_inv(int r) {
 #ifndef FA_FWD_SCHED
 #define FA_FWD_SCHED 4
 #endif
-#ifndef FA_FWD_PRIO
-#define FA_FWD_PRIO 0        // raise wave priority while issuing MFMA chains
-#endif
-
-__device__ __forceinline__ void prio_hi() {
-#if FA_FWD_PRIO
-    __builtin_amdgcn_s_setprio(1);
-#endif
-}
-__device__ __forceinline__ void prio_lo() {
-#if FA_FWD_PRIO
-    __builtin_amdgcn_s_setprio(0);
-#endif
-}
 
 template <int N_> using ic = std::integral_constant<int, N_>;
 
@@ -214,7 +196,6 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
             for (int kb = 0; kb < NKB; ++kb) bbit[kb] = block_bit(k0 + 32 * kb);
         }
         f32x16 s[NKB];
-        prio_hi();
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
             u32x4 ka[D / 16];   // all operands of the block first, then the MFMA chain
@@ -239,7 +220,6 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
             __builtin_amdgcn_sched_barrier(0);
         }
 #endif
-        prio_lo();
         if constexpr (MASK) {
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb)
@@ -312,7 +292,6 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
                     pf[kb][t][w] = pack_bf16x2(p0, p1);
                 }
             }
-        prio_hi();
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
@@ -326,7 +305,6 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) oacc[db] = mfma32x32x16(va[db], pf[kb][t], oacc[db]);
             }
-        prio_lo();
     };
 
     // Key tiles are visited in a sequence of positions p: under a window with

@@ -59,8 +59,8 @@ import numpy as np
 
 __all__ = [
     "scores", "probs", "attention_fwd_head", "attention_fwd", "attention_bwd_head",
-    "attention_bwd", "decode_fwd", "tiled_fwd_literal", "split_kv_decode",
-    "gather_pages", "decode_paged", "visible", "round_to_bf16", "philox4x32_10",
+    "attention_bwd", "decode_fwd", "tiled_fwd_partials", "merge_partials", "split_kv_decode",
+    "gather_pages", "decode_paged", "visible", "philox4x32_10",
     "dropout_threshold", "dropout_keep", "head_dropout", "head_block",
 ]
 
@@ -241,18 +241,7 @@ def attention_fwd(q, k, v, tau, causal, window=None, sinks=0, dropout=None, bloc
     return o, lse
 
 
-def round_to_bf16(x):
-    """Nearest bfloat16 value of each entry, as float64: round to float32
-    first (the kernels hold O in fp32), then to 8 significant bits, ties to even."""
-    f = np.ascontiguousarray(np.asarray(x, dtype=np.float64).astype(np.float32))
-    u = f.view(np.uint32)
-    r = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1)))
-         & np.uint32(0xFFFF0000)).astype(np.uint32)
-    return r.view(np.float32).astype(np.float64)
-
-
-def attention_bwd_head(q, k, v, do, tau, causal, window=None, sinks=0, d_from_saved_bf16=False,
-                       drop=None, block=None):
+def attention_bwd_head(q, k, v, do, tau, causal, window=None, sinks=0, drop=None, block=None):
     """Hand-derived gradients of O = softmax(tau Q K^T [+mask]) V for one head.
 
     With the loss's gradient dO:
@@ -261,10 +250,6 @@ def attention_bwd_head(q, k, v, do, tau, causal, window=None, sinks=0, d_from_sa
       dQ = tau dS K;  dK = tau dS^T Q.
     The identity D_i = dO_i . O_i ("como funciona", backward paragraph) is
     returned as a second form of D for the tests to compare.
-    d_from_saved_bf16: take D_i = dO_i . bf16(O_i) in dS instead, i.e. the
-    identity applied to the output the forward saved when O is stored in
-    bfloat16 (the page's backward keeps only the saved O).  The returned "D"
-    is then that value.
     drop = (keep, p): dropout as in attention_fwd_head.  With Z = keep / (1 - p):
     O = (P o Z) V, dV = (P o Z)^T dO, dS = P o (Z o dP - D) with dP = dO V^T and
     D_i = sum_j P_ij Z_ij dP_ij = dO_i . O_i.
@@ -283,8 +268,6 @@ def attention_bwd_head(q, k, v, do, tau, causal, window=None, sinks=0, d_from_sa
     dv = (p * z).T @ do
     dp = z * (do @ v.T)
     D = (p * dp).sum(axis=1)
-    if d_from_saved_bf16:
-        D = (do * round_to_bf16(o)).sum(axis=1)
     ds = p * (dp - D[:, None])
     dq = tau * (ds @ k)
     dk = tau * (ds.T @ q)
@@ -292,8 +275,7 @@ def attention_bwd_head(q, k, v, do, tau, causal, window=None, sinks=0, d_from_sa
             "D": D, "D_from_o": (do * o).sum(axis=1), "p": p, "pz": p * z, "ds": ds}
 
 
-def attention_bwd(q, k, v, do, tau, causal, window=None, sinks=0, d_from_saved_bf16=False,
-                  dropout=None, block=None):
+def attention_bwd(q, k, v, do, tau, causal, window=None, sinks=0, dropout=None, block=None):
     """attention_bwd_head over [B, H, N, d]; returns dq, dk, dv, D as arrays."""
     B, H, N, d = q.shape
     out = {name: np.empty((B, H, N, d)) for name in ("dq", "dk", "dv")}
@@ -301,8 +283,7 @@ def attention_bwd(q, k, v, do, tau, causal, window=None, sinks=0, d_from_saved_b
     for b in range(B):
         for h in range(H):
             g = attention_bwd_head(q[b, h], k[b, h], v[b, h], do[b, h], tau, causal, window, sinks,
-                                   d_from_saved_bf16, drop=head_dropout(dropout, b * H + h),
-                                   block=head_block(block, h))
+                                   drop=head_dropout(dropout, b * H + h), block=head_block(block, h))
             for name in ("dq", "dk", "dv", "D"):
                 out[name][b, h] = g[name]
     return out
@@ -377,52 +358,69 @@ def decode_fwd(q, k, v, seqlens, tau, heads=None, batches=None):
     return o, lse
 
 
-def tiled_fwd_literal(q, k, v, tau, causal, Br, Bc, window=None, sinks=0, block=None):
-    """Self-check of the tiled recurrence, in the page's own loop order.
+def merge_partials(a, b):
+    """Combine the softmax partials of two disjoint key sets.
 
-    Follows "como funciona" of the "flash-attention" encyclopedia page: the outer
-    loop walks KV blocks of Bc rows, the inner loop walks Q blocks of Br rows;
-    O_i, l_i and m_i live in "HBM" arrays that are loaded and stored around each
-    block step; per block, m~ = rowmax(S_ij), P~ = exp(S_ij - m~),
-    m_new = max(m_i, m~), l_new = e^(m_i - m_new) l_i + e^(m~ - m_new) rowsum(P~),
-    and O_i = (l_i e^(m_i - m_new) O_i + e^(m~ - m_new) P~ V_j) / l_new.
+    A partial over a key set J is (m, l, u): m = max_{j in J} S_j, l =
+    sum_{j in J} exp(S_j - m) and u = sum_{j in J} exp(S_j - m) V_j (not
+    normalised), per query row.  For the union of the two sets the reference
+    becomes the larger maximum and each side is rescaled to it by exp(m_side -
+    m) ("como funciona": the running maximum and sum are rescaled whenever a
+    block is merged).  A side with no visible key (m = -inf) contributes
+    nothing.  Arrays: m, l [rows], u [rows, d]."""
+    (ma, la, ua), (mb, lb, ub) = a, b
+    m = np.maximum(ma, mb)
+    fa = np.zeros_like(m)
+    fb = np.zeros_like(m)
+    live = np.isfinite(m)
+    fa[live] = np.exp(ma[live] - m[live])
+    fb[live] = np.exp(mb[live] - m[live])
+    return m, la * fa + lb * fb, ua * fa[:, None] + ub * fb[:, None]
 
-    Under the causal mask (and a sliding window) a block row can be fully masked
-    (m~ = -inf); it then contributes no term and that row's statistics are left
-    as they were.
-    Returns O [N,d] and LSE = m + ln(l) [N] for one head.
-    """
+
+def tiled_fwd_partials(q, k, v, tau, causal, Br, Bc, window=None, sinks=0, block=None):
+    """Self-check of the block decomposition of the softmax, for one head.
+
+    For each block of Br query rows and each block of Bc keys this forms the
+    block's own partial (m, l, u) from its scores alone (the key block's
+    maximum as reference), then combines the partials of a query block with
+    merge_partials as a balanced binary tree (pairs of neighbouring key
+    blocks, then pairs of pairs, ...), so the blocks are merged in a different
+    order from any left-to-right sweep.  The pages claim the blocked result is
+    the exact softmax, not an approximation ("flash-attention" page, "a
+    ideia"): O = u / l and LSE = m + ln l must equal standard attention.
+    A row that sees no key keeps m = -inf, l = 0: O = 0, LSE = -inf.
+    Returns O [N, d] and LSE [N]."""
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     nq, nk = q.shape[0], k.shape[0]
-    O = np.zeros((nq, v.shape[1]))
-    l = np.zeros(nq)
-    m = np.full(nq, -np.inf)
-    for j0 in range(0, nk, Bc):
-        Kj, Vj = k[j0:j0 + Bc], v[j0:j0 + Bc]
-        for i0 in range(0, nq, Br):
-            rows = np.arange(i0, min(i0 + Br, nq))
-            Qi, Oi, li, mi = q[rows], O[rows].copy(), l[rows].copy(), m[rows].copy()
-            Sij = tau * (Qi @ Kj.T)
-            if causal or window is not None or block is not None:
-                keys = np.arange(j0, j0 + Kj.shape[0])
-                Sij = np.where(visible(rows, keys, causal, window, sinks, block), Sij, -np.inf)
-            m_til = Sij.max(axis=1)
-            live = np.isfinite(m_til)
-            if not live.any():
-                continue
-            Sl, ml = Sij[live], m_til[live]
-            P_til = np.exp(Sl - ml[:, None])
-            m_new = np.maximum(mi[live], ml)
-            a_old = np.exp(mi[live] - m_new)
-            a_new = np.exp(ml - m_new)
-            l_new = a_old * li[live] + a_new * P_til.sum(axis=1)
-            Oi[live] = ((li[live] * a_old)[:, None] * Oi[live]
-                        + a_new[:, None] * (P_til @ Vj)) / l_new[:, None]
-            li[live], mi[live] = l_new, m_new
-            O[rows], l[rows], m[rows] = Oi, li, mi
-    return O, _lse(m, l)
+    o = np.zeros((nq, v.shape[1]))
+    lse = np.full(nq, -np.inf)
+    masked = causal or window is not None or block is not None
+    for i0 in range(0, nq, Br):
+        rows = np.arange(i0, min(i0 + Br, nq))
+        parts = []
+        for j0 in range(0, nk, Bc):
+            keys = np.arange(j0, min(j0 + Bc, nk))
+            s = tau * (q[rows] @ k[keys].T)
+            if masked:
+                s = np.where(visible(rows, keys, causal, window, sinks, block), s, -np.inf)
+            m = s.max(axis=1)
+            e = np.zeros_like(s)
+            live = np.isfinite(m)
+            e[live] = np.exp(s[live] - m[live, None])
+            parts.append((m, e.sum(axis=1), e @ v[keys]))
+        while len(parts) > 1:
+            nxt = [merge_partials(parts[t], parts[t + 1]) for t in range(0, len(parts) - 1, 2)]
+            if len(parts) % 2:
+                nxt.append(parts[-1])
+            parts = nxt
+        m, l, u = parts[0]
+        live = l > 0
+        o[rows[live]] = u[live] / l[live, None]
+        lse[rows[live]] = m[live] + np.log(l[live])
+    return o, lse
 
 
 def split_kv_decode(q, k, v, tau, bounds):
@@ -430,9 +428,10 @@ def split_kv_decode(q, k, v, tau, bounds):
 
     Each split s covers keys [bounds[s], bounds[s+1]) and yields its own
     normalised output o_s and lse_s = m_s + ln l_s (standard attention on the
-    split).  The splits are merged with the same rule the tiled recurrence uses
-    to merge blocks ("como funciona"): LSE = ln sum_s exp(lse_s), taken after
-    subtracting max_s lse_s, and O = sum_s exp(lse_s - LSE) o_s.
+    split).  The splits are merged by their log-sum-exp ("como funciona": the
+    partial results of key blocks are combined through their row statistics):
+    LSE = ln sum_s exp(lse_s), taken after subtracting max_s lse_s, and
+    O = sum_s exp(lse_s - LSE) o_s.
     Returns O [1,d], LSE scalar.
     """
     parts = []

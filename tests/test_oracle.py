@@ -178,31 +178,50 @@ def test_row_subset_and_chunking_agree_with_full():
 @pytest.mark.parametrize("causal", [False, True])
 @pytest.mark.parametrize("br,bc", [(16, 16), (7, 13), (13, 7), (1, 64), (64, 5), (100, 100)])
 def test_tiled_recurrence_equals_standard(causal, br, bc):
-    """The block recurrence with running (m, l) ("como funciona") gives exactly
-    standard attention; its result is identical, not approximate."""
+    """Key-block partials (m, l, u) merged through their row statistics ("como
+    funciona") give exactly standard attention ("a ideia": exact, not an
+    approximation), whatever the block shapes and the merge order."""
     n, d = 61, 8
     q, k, v = _rand((n, d), 19) * 2, _rand((n, d), 20) * 2, _rand((n, d), 21)
     o, lse = orc.attention_fwd_head(q, k, v, 0.5, causal)
-    ot, lt = orc.tiled_fwd_literal(q, k, v, 0.5, causal, br, bc)
+    ot, lt = orc.tiled_fwd_partials(q, k, v, 0.5, causal, br, bc)
     np.testing.assert_allclose(ot, o, rtol=0, atol=1e-12)
     np.testing.assert_allclose(lt, lse, rtol=0, atol=1e-12)
 
 
 def test_tiled_recurrence_catches_a_dropped_rescale():
-    """The tiled check is sensitive: leaving out the e^(m_i - m_new) rescale of
-    the running output (a plausible kernel bug) moves the result far."""
+    """The tiled check is sensitive: a merge that adds the partials of two key
+    blocks without bringing them to a common reference maximum (a plausible
+    kernel bug) moves the result far from standard attention, while the
+    oracle's merge of the same two partials reproduces it."""
     n, d = 40, 8
     q, k, v = _rand((n, d), 22) * 3, _rand((n, d), 23) * 3, _rand((n, d), 24)
     o, _ = orc.attention_fwd_head(q, k, v, 0.5, False)
-    O = np.zeros((n, d)); l = np.zeros(n); m = np.full(n, -np.inf)
-    for j0 in range(0, n, 8):
-        s = 0.5 * q @ k[j0:j0 + 8].T
-        mt = s.max(1); p = np.exp(s - mt[:, None])
-        mn = np.maximum(m, mt)
-        ln_ = np.exp(m - mn) * l + np.exp(mt - mn) * p.sum(1)
-        O = (l[:, None] * O + np.exp(mt - mn)[:, None] * (p @ v[j0:j0 + 8])) / ln_[:, None]
-        l, m = ln_, mn
-    assert np.abs(O - o).max() > 1e-3
+
+    def partial(keys):
+        s = 0.5 * q @ k[keys].T
+        m = s.max(axis=1)
+        e = np.exp(s - m[:, None])
+        return m, e.sum(axis=1), e @ v[keys]
+
+    a, b = partial(np.arange(0, 17)), partial(np.arange(17, n))
+    m, l, u = orc.merge_partials(a, b)
+    np.testing.assert_allclose(u / l[:, None], o, atol=1e-12)
+    bad = (a[2] + b[2]) / (a[1] + b[1])[:, None]
+    assert np.abs(bad - o).max() > 1e-3
+
+
+def test_merge_with_an_empty_side_keeps_the_other():
+    """A key block with no visible key (m = -inf, l = 0, u = 0) leaves the
+    other partial unchanged, in either order."""
+    rng = np.random.default_rng(25)
+    a = (rng.standard_normal(5), rng.random(5) + 0.5, rng.standard_normal((5, 3)))
+    empty = (np.full(5, -np.inf), np.zeros(5), np.zeros((5, 3)))
+    for x, y in ((a, empty), (empty, a)):
+        m, l, u = orc.merge_partials(x, y)
+        np.testing.assert_array_equal(m, a[0])
+        np.testing.assert_array_equal(l, a[1])
+        np.testing.assert_array_equal(u, a[2])
 
 
 def test_split_kv_merge_equals_unsplit():
@@ -478,7 +497,7 @@ def test_tiled_recurrence_with_window(Br, Bc, w, s):
     before and after the window) equals the direct computation."""
     q, k, v = _qkv(70, 8, 504)
     o1, l1 = orc.attention_fwd_head(q, k, v, 0.4, True, window=w, sinks=s)
-    o2, l2 = orc.tiled_fwd_literal(q, k, v, 0.4, True, Br, Bc, window=w, sinks=s)
+    o2, l2 = orc.tiled_fwd_partials(q, k, v, 0.4, True, Br, Bc, window=w, sinks=s)
     np.testing.assert_allclose(o2, o1, atol=1e-12)
     np.testing.assert_allclose(l2, l1, atol=1e-12)
 
@@ -516,41 +535,6 @@ def test_window_needs_causal():
         orc.attention_fwd_head(q, k, v, 1.0, True, window=0)
 
 
-# --- D from the saved bfloat16 output ---------------------------------------
-
-def test_round_to_bf16_matches_torch():
-    """The oracle's rounding equals torch's float32 -> bfloat16 conversion
-    (round to nearest even), ties and subnormal-free range included."""
-    import torch
-    rng = np.random.default_rng(601)
-    x = np.concatenate([rng.standard_normal(5000) * 10.0 ** rng.integers(-6, 6, 5000),
-                        # exact ties between two bf16 neighbours, both parities
-                        np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, -(1 + 2 ** -8), 2 ** 20 * (1 + 2 ** -8)])])
-    want = torch.from_numpy(x.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
-    np.testing.assert_array_equal(orc.round_to_bf16(x), want)
-
-
-def test_d_from_saved_bf16_output():
-    """With window 1 every O row is a V row; with V exactly representable in
-    bf16 the saved output is exact and D equals its exact value, so the
-    gradients agree; with general V the difference obeys the rounding bound."""
-    n, d = 12, 8
-    q, k, _ = _qkv(n, d, 602)
-    v = orc.round_to_bf16(np.random.default_rng(603).standard_normal((n, d)))
-    do = np.random.default_rng(604).standard_normal((n, d))
-    g1 = orc.attention_bwd_head(q, k, v, do, 0.5, True, window=1)
-    g2 = orc.attention_bwd_head(q, k, v, do, 0.5, True, window=1, d_from_saved_bf16=True)
-    for name in ("dq", "dk", "dv", "D"):
-        np.testing.assert_allclose(g2[name], g1[name], atol=1e-12)
-    q, k, v = _qkv(40, d, 605)
-    do = np.random.default_rng(606).standard_normal((40, d))
-    g1 = orc.attention_bwd_head(q, k, v, do, 0.5, True)
-    g2 = orc.attention_bwd_head(q, k, v, do, 0.5, True, d_from_saved_bf16=True)
-    bound = (np.abs(do) * 2.0 ** -8 * np.abs(g1["o"])).sum(axis=1) + 1e-12
-    assert np.all(np.abs(g2["D"] - g1["D"]) <= bound)
-    assert np.abs(g2["D"] - g1["D"]).max() > 0
-
-
 # --- dropout: Philox4x32-10 and the dropped attention -------------------------
 
 GOLDEN_DIR = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -564,6 +548,43 @@ def test_philox_known_answers():
         key = [int(x, 16) for x in v["key"]]
         out = orc.philox4x32_10(ctr[None, :], key)[0]
         assert [int(x) for x in out] == [int(x, 16) for x in v["out"]]
+
+
+# Keep patterns of one 4 x 4 block of (query, key) pairs, written out by hand
+# from the published Philox4x32-10 known-answer vectors (the golden file
+# above) under the layout the design notes fix: counter (j/4, i/4, b*H + h,
+# offset), key (seed low word, seed high word), pair (i, j) kept iff byte j%4
+# (byte 0 = least significant) of output word i%4 is >= round(256 p).
+#   ctr 0, key 0 -> 6627e8d5 e169c58d bc57ac4c 9b00dbd8, bytes by row:
+#     d5 e8 27 66 | 8d c5 69 e1 | 4c ac 57 bc | d8 db 00 9b
+#   ctr ffffffff x4, key ffffffff x2 -> 408f276d 41c83b0e a20bc7c6 6d5451fd:
+#     6d 27 8f 40 | 0e 3b c8 41 | c6 c7 0b a2 | fd 51 54 6d
+#   ctr 243f6a88 85a308d3 13198a2e 03707344, key a4093822 299f31d0
+#     -> d16cfe09 94fdcceb 5001e420 24126ea1:
+#     09 fe 6c d1 | eb cc fd 94 | 20 e4 01 50 | a1 6e 12 24
+HAND_BLOCKS = [
+    # (i/4, j/4, head, offset, seed, p, rows of the keep pattern)
+    (0, 0, 0, 0, 0, 0.5, ["1100", "1101", "0101", "1101"]),
+    (0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFF, 0xFFFFFFFFFFFFFFFF, 0.5,
+     ["0010", "0010", "1101", "1000"]),
+    (0x85A308D3, 0x243F6A88, 0x13198A2E, 0x03707344, 0x299F31D0A4093822, 0.5,
+     ["0101", "1111", "0100", "1000"]),
+    (0x85A308D3, 0x243F6A88, 0x13198A2E, 0x03707344, 0x299F31D0A4093822, 0.25,
+     ["0111", "1111", "0101", "1100"]),
+]
+
+
+@pytest.mark.parametrize("blk", HAND_BLOCKS)
+def test_dropout_mask_layout_from_published_vectors(blk):
+    """Pins which counter word carries the key index and which the query index,
+    the seed's word order, the head and offset words, the word/byte choice
+    within a block and the threshold comparison: each hand-written pattern
+    comes from a published output vector, not from the oracle's code (swapping
+    the query and key roles, or words and bytes, gives other patterns)."""
+    i4, j4, bh, offset, seed, p, want = blk
+    keep = orc.dropout_keep(4 * i4 + np.arange(4), 4 * j4 + np.arange(4), bh, seed, offset, p)
+    got = ["".join("1" if x else "0" for x in row) for row in keep]
+    assert got == want
 
 
 def test_dropout_threshold_and_rate():
@@ -710,7 +731,7 @@ def test_tiled_recurrence_with_block_mask(Br, Bc):
     mask[0, 0] = 1
     for causal in (False, True):
         o1, l1 = orc.attention_fwd_head(q, k, v, 0.4, causal, block=(mask, 8, 16))
-        o2, l2 = orc.tiled_fwd_literal(q, k, v, 0.4, causal, Br, Bc, block=(mask, 8, 16))
+        o2, l2 = orc.tiled_fwd_partials(q, k, v, 0.4, causal, Br, Bc, block=(mask, 8, 16))
         live = np.isfinite(l1)
         np.testing.assert_allclose(o2, o1, atol=1e-12)
         np.testing.assert_allclose(l2[live], l1[live], atol=1e-12)

@@ -5,7 +5,7 @@ import pytest
 
 import fa_inputs
 from oracle import attention as orc
-from tests.util import assert_close, rounding_allowance, to_device, to_f64
+from tests.util import assert_close, bwd_allowance, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -114,7 +114,7 @@ def _run_bwd(x, tau, causal, mask, bq, bk):
     o, lse = fa.fwd(q, k, v, tau=tau, causal=causal, block_mask=m, block_size=(bq, bk))
     dq, dk, dv = fa.bwd(q, k, v, o, lse, do, tau=tau, causal=causal, block_mask=m,
                         block_size=(bq, bk))
-    return {"dq": to_f64(dq), "dk": to_f64(dk), "dv": to_f64(dv)}
+    return {"o": to_f64(o), "dq": to_f64(dq), "dk": to_f64(dk), "dv": to_f64(dv)}
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -130,11 +130,12 @@ def test_block_sparse_bwd_small(N, density, bq, bk, causal, d):
     qf, kf, vf, dof = (x[n].f64() for n in ("q", "k", "v", "do"))
     for b in range(B):
         for h in range(H):
-            # D from the saved bf16 output and the bf16-operand allowance:
-            # sparse rows can have few visible keys (P close to one)
+            # Exact gradients; the allowance models D formed from the stored
+            # bf16 O and the bf16 MFMA operands: sparse rows can have few
+            # visible keys (P close to one)
             ref = orc.attention_bwd_head(qf[b, h], kf[b, h], vf[b, h], dof[b, h], tau, causal,
-                                         d_from_saved_bf16=True, block=(mask[h], bq, bk))
-            extra = rounding_allowance(ref, qf[b, h], kf[b, h], dof[b, h], tau)
+                                         block=(mask[h], bq, bk))
+            extra = bwd_allowance(ref, g["o"][b, h], qf[b, h], kf[b, h], dof[b, h], tau)
             for name in ("dq", "dk", "dv"):
                 assert_close(g[name][b, h], ref[name], "bf16", "%s[%d,%d]" % (name, b, h),
                              ulp_allow=True, extra=extra[name])
@@ -153,6 +154,6 @@ def test_block_sparse_bwd_workload_shape():
     qf, kf, vf, dof = (x[n].f64() for n in ("q", "k", "v", "do"))
     for b, h in ((1, 2), (3, 9)):
         ref = orc.attention_bwd_head(qf[b, h], kf[b, h], vf[b, h], dof[b, h], w.tau, True,
-                                     d_from_saved_bf16=True, block=(mask[h], 128, 128))
+                                     block=(mask[h], 128, 128))
         for name in ("dq", "dk", "dv"):
             assert_close(g[name][b, h], ref[name], "bf16", "%s[%d,%d]" % (name, b, h))

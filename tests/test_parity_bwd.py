@@ -72,3 +72,30 @@ def test_bwd_deterministic():
     b = fa.bwd(q, k, v, o, lse, do, causal=True)
     for t1, t2 in zip(a, b):
         assert torch.equal(t1, t2)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("N", [100, 130])
+def test_bwd_very_negative_scores_ragged_tail(N, d):
+    """Every score near -100 or below (Q = 8, K = -1.6 + small noise), so each
+    row's LSE is below -88, where exp(-LSE) overflows float32; N is not a
+    multiple of the key tile, so the tail tile holds keys past N.  Those keys
+    must contribute nothing: dQ, dK, dV finite and equal to the exact
+    gradients (non-causal, where no diagonal masks the tail)."""
+    import io_aware_tiled_03_amd as fa
+    import torch
+    B, H = 1, 2
+    rng = np.random.default_rng(10600 + N + d)
+    q = np.full((B, H, N, d), 8.0)
+    k = -1.6 + 0.05 * rng.standard_normal((B, H, N, d))
+    v = rng.standard_normal((B, H, N, d))
+    do = rng.standard_normal((B, H, N, d))
+    dev = [torch.from_numpy(a.astype(np.float32)).to("cuda", torch.bfloat16) for a in (q, k, v, do)]
+    qf, kf, vf, dof = (to_f64(t) for t in dev)
+    tau = 1.0 / np.sqrt(d)
+    o, lse = fa.fwd(dev[0], dev[1], dev[2], tau=tau, causal=False)
+    assert to_f64(lse).max() < -88.0
+    dq, dk, dv = fa.bwd(dev[0], dev[1], dev[2], o, lse, dev[3], tau=tau, causal=False)
+    ref = orc.attention_bwd(qf, kf, vf, dof, tau, False)
+    for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
+        assert_close(to_f64(got), ref[name], "bf16", name)

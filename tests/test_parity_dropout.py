@@ -5,7 +5,7 @@ import pytest
 
 import fa_inputs
 from oracle import attention as orc
-from tests.util import assert_close, rounding_allowance, to_device, to_f64
+from tests.util import assert_close, bwd_allowance, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -119,7 +119,7 @@ def _bwd(x, tau, causal, drop):
     q, k, v, do = (to_device(x[n]) for n in ("q", "k", "v", "do"))
     o, lse = fa.fwd(q, k, v, tau=tau, causal=causal, dropout=drop)
     dq, dk, dv = fa.bwd(q, k, v, o, lse, do, tau=tau, causal=causal, dropout=drop)
-    return {"dq": to_f64(dq), "dk": to_f64(dk), "dv": to_f64(dv)}
+    return {"o": to_f64(o), "dq": to_f64(dq), "dk": to_f64(dk), "dv": to_f64(dv)}
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -134,13 +134,12 @@ def test_dropout_bwd_small(N, p, causal, d):
     qf, kf, vf, dof = (x[n].f64() for n in ("q", "k", "v", "do"))
     for b in range(2):
         for h in range(2):
-            # D from the saved bf16 output (as the kernels form it), and the
-            # rounding allowance of the bf16 MFMA operands: short causal rows
-            # put P close to one and Z = 1/(1-p) scales dP up
+            # Exact gradients; the allowance models D formed from the stored
+            # bf16 O and the bf16 MFMA operands P o Z and dS: short causal
+            # rows put P close to one and Z = 1/(1-p) scales dP up
             ref = orc.attention_bwd_head(qf[b, h], kf[b, h], vf[b, h], dof[b, h], tau, causal,
-                                         d_from_saved_bf16=True,
                                          drop=orc.head_dropout((drop[1], drop[2], p), b * 2 + h))
-            extra = rounding_allowance(ref, qf[b, h], kf[b, h], dof[b, h], tau)
+            extra = bwd_allowance(ref, g["o"][b, h], qf[b, h], kf[b, h], dof[b, h], tau)
             for name in ("dq", "dk", "dv"):
                 assert_close(g[name][b, h], ref[name], "bf16", "%s[%d,%d]" % (name, b, h),
                              ulp_allow=True, extra=extra[name])
@@ -161,7 +160,7 @@ def test_dropout_workload_shape():
     for b, h in ((0, 1), (3, 14)):
         hd = orc.head_dropout((drop[1], drop[2], drop[0]), b * w.H + h)
         ref = orc.attention_bwd_head(qf[b, h], kf[b, h], vf[b, h], dof[b, h], w.tau, True,
-                                     d_from_saved_bf16=True, drop=hd)
+                                     drop=hd)
         assert_close(o[b, h], ref["o"], "bf16", "O[%d,%d]" % (b, h))
         for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
             assert_close(got[b, h], ref[name], "bf16", "%s[%d,%d]" % (name, b, h))

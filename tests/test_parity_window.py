@@ -5,7 +5,7 @@ import pytest
 
 import fa_inputs
 from oracle import attention as orc
-from tests.util import assert_close, rounding_allowance, to_device, to_f64
+from tests.util import assert_close, bwd_allowance, to_device, to_f64
 
 pytestmark = pytest.mark.gpu
 
@@ -83,7 +83,7 @@ def _bwd(x, tau, window, sinks):
     q, k, v, do = (to_device(x[n]) for n in ("q", "k", "v", "do"))
     o, lse = fa.fwd(q, k, v, tau=tau, causal=True, window=window, sinks=sinks)
     dq, dk, dv = fa.bwd(q, k, v, o, lse, do, tau=tau, causal=True, window=window, sinks=sinks)
-    return {"dq": to_f64(dq), "dk": to_f64(dk), "dv": to_f64(dv)}
+    return {"o": to_f64(o), "dq": to_f64(dq), "dk": to_f64(dk), "dv": to_f64(dv)}
 
 
 @pytest.mark.parametrize("d", [64, 128])
@@ -97,13 +97,14 @@ def test_window_bwd_small(N, w, s, d):
     qf, kf, vf, dof = (x[n].f64() for n in ("q", "k", "v", "do"))
     for b in range(2):
         for h in range(2):
-            # D from the saved bf16 output, as the kernels compute it: with a
-            # window of a few keys P is close to one and D's rounding would
-            # otherwise pass into dS undamped.  Entries above |x| = 5 also get
-            # one bf16 ulp (their storage rounding alone exceeds 2e-2).
+            # Exact gradients; the allowance models the kernels' bf16 steps:
+            # D formed from the stored bf16 O (with a window of a few keys P
+            # is close to one and D's error passes into dS undamped), P and dS
+            # rounded to bf16 before their products, and one bf16 ulp for
+            # entries above |x| = 5 (their storage rounding alone exceeds 2e-2).
             ref = orc.attention_bwd_head(qf[b, h], kf[b, h], vf[b, h], dof[b, h], tau, True,
-                                         window=w, sinks=s, d_from_saved_bf16=True)
-            extra = rounding_allowance(ref, qf[b, h], kf[b, h], dof[b, h], tau)
+                                         window=w, sinks=s)
+            extra = bwd_allowance(ref, g["o"][b, h], qf[b, h], kf[b, h], dof[b, h], tau)
             for name in ("dq", "dk", "dv"):
                 assert_close(g[name][b, h], ref[name], "bf16", "%s[%d,%d]" % (name, b, h),
                              ulp_allow=True, extra=extra[name])
@@ -132,6 +133,6 @@ def test_window_bwd_workload():
     qf, kf, vf, dof = (x[n].f64() for n in ("q", "k", "v", "do"))
     for b, h in ((0, 3), (1, 10), (3, 15)):
         ref = orc.attention_bwd_head(qf[b, h], kf[b, h], vf[b, h], dof[b, h], wl.tau, True,
-                                     window=1024, sinks=4, d_from_saved_bf16=True)
+                                     window=1024, sinks=4)
         for name in ("dq", "dk", "dv"):
             assert_close(g[name][b, h], ref[name], "bf16", "%s[%d,%d]" % (name, b, h))

@@ -75,3 +75,33 @@ def rounding_allowance(g, q, k, do, tau):
     return {"dv": u * (np.abs(g["pz"]).T @ np.abs(do)),
             "dk": u * tau * (np.abs(g["ds"]).T @ np.abs(q)),
             "dq": u * tau * (np.abs(g["ds"]) @ np.abs(k))}
+
+
+def saved_o_allowance(g, o_gpu, q, k, do, tau):
+    """Per-element allowance on dQ and dK for the D the kernels form.
+
+    The backward takes D_i = dO_i . O_i from the O its forward stored (bf16),
+    not from the exact O, so D_gpu - D = dO_i . (O_gpu_i - O_i) plus the
+    float32 rounding of that length-d sum of exact bf16 products:
+        |dD_i| <= sum_c |dO_ic| |O_gpu_ic - O_ic| + 2^-17 sum_c |dO_ic| |O_gpu_ic|.
+    dS_ij = P_ij (dP_ij - D_i) (dropout: P_ij (Z_ij dP_ij - D_i)) then moves by
+    -P_ij dD_i, so
+        |d dQ_ic| <= tau |dD_i| sum_j P_ij |K_jc|,
+        |d dK_jc| <= tau sum_i P_ij |dD_i| |Q_ic|,
+    and dV does not depend on D.  P is the undropped softmax of the exact
+    scores.  g: the oracle's attention_bwd_head result; o_gpu: the forward's
+    output for the same head (float64 view of what the kernel stored)."""
+    o_gpu = np.asarray(o_gpu, dtype=np.float64)
+    do = np.abs(np.asarray(do, dtype=np.float64))
+    dD = (do * np.abs(o_gpu - g["o"])).sum(axis=1) + 2.0 ** -17 * (do * np.abs(o_gpu)).sum(axis=1)
+    p = g["p"]
+    return {"dq": tau * dD[:, None] * (p @ np.abs(k)),
+            "dk": tau * (p.T @ (dD[:, None] * np.abs(q))),
+            "dv": np.zeros_like(o_gpu)}
+
+
+def bwd_allowance(g, o_gpu, q, k, do, tau):
+    """rounding_allowance + saved_o_allowance, per output."""
+    a = rounding_allowance(g, q, k, do, tau)
+    b = saved_o_allowance(g, o_gpu, q, k, do, tau)
+    return {n: a[n] + b[n] for n in a}
