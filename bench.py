@@ -1,39 +1,46 @@
 """Throughput of the exact-attention path on one MI355X.
 
-One step = one pass of the whole path over the GPT-2-medium-shaped batch
-(B=8, H=16, N=1024, d=64, bf16, tau=1/8):
-    fa_fwd non-causal, fa_fwd causal, fa_bwd causal (its two kernels enqueued
-    one by one through fa_bwd_stage), and fa_decode with one query per sequence
-    against the same K/V as the cache (L_b = N for every b).
-value = algorithmic TFLOP/s of the step (forward 4*B*H*N^2*d, halved when
-causal; backward 10*B*H*N^2*d halved when causal; decode 4*B*H*N*d), from the
-wall clock around exactly --steps steps bracketed by device synchronisation.
+Headline step: the long-context causal prefill forward, fa_fwd on
+B=1, H=32, N=16384, d=128, bf16 Q/K/V drawn N(0,1) from the seeded recipe of
+fa_inputs (seeds 1003/1103/1203), causal, tau = 1/sqrt(128).  A materialised
+N x N score matrix of this shape would hold 512 MiB per head in fp16 ("Atenção
+eficiente — FlashAttention, sparse e híbrida", table of section "Por que isso
+importa"); the kernel never writes it.
+value = algorithmic TFLOP/s (4*B*H*N^2*d, halved for the causal mask) from the
+wall clock around exactly --steps calls bracketed by device synchronisation,
+inputs resident in HBM.
 
-The line also carries, measured in the same run:
-  * "kernels": every call of the step timed with HIP events on the stream the
-    library launches on, with TFLOP/s and GB/s of algorithmic work;
-  * "roofline": the kernel with the largest share of the step against its
-    peak (MFMA bf16 2.5 PFLOP/s; HBM 8 TB/s), with the HBM traffic read from
+The JSON line also carries, from the same run:
+  * "timing": every timed call bracketed by HIP events on the stream the
+    library launches on (median, p10, p90, mean);
+  * "roofline": the forward kernel against the dense bf16 MFMA peak
+    (algorithmic flops / mean event time) and its HBM traffic per launch from
     the committed rocprofv3 counter summary when it matches the sources;
-  * "also_measured": the long causal prefill (1x32x16384x128), the same
-    prefill as a sliding-window (local) layer with a 4096-key window and as a
-    block-sparse layer (band plus global blocks), the split-KV
-    decode (64x32, L_b ~ U[1024, 8192], d=128), the paged decode with grouped
-    KV heads (64 sequences, 32 query / 8 KV heads, 16-token pages, the same
-    key lengths), the causal backward (4x16x4096x64) and the same shape with
-    dropout p = 0.1 (forward and backward) at full size, each against its
-    roofline (skip: --no-extra);
-  * "cpu_baseline": the float64 oracle on the host over a bounded sample of
-    the same step (whole heads, about 10 s of CPU work).
+  * "sclk_mhz": the shader clock level read from sysfs while the kernel runs
+    back to back (null where the file is not readable);
+  * "bytes_avoided": the HBM traffic standard attention would spend on S and
+    P at this shape;
+  * "pages_context": the pages' own figures, quoted with their hardware;
+  * "also_measured" (skip: --no-extra): the GPT-2-medium-shaped step (fwd
+    non-causal, fwd causal, bwd causal, decode), the tiny fp32 forward, the
+    split-KV decode, the paged grouped-head decode, the 4k causal backward,
+    the prefill as a sliding-window and as a block-sparse layer, and dropout,
+    each against its roofline;
+  * "cpu_baseline" (skip: --no-cpu): the float64 oracle on the host over two
+    whole heads of the headline workload, with the GPU output of those heads
+    compared against it, plus the oracle's wall time on the other workloads.
 """
 from __future__ import annotations
 
 import argparse
+import glob
 import hashlib
 import json
 import math
 import os
+import subprocess
 import sys
+import threading
 import time
 
 import numpy as np
@@ -44,71 +51,54 @@ sys.path.insert(0, ROOT)
 PEAK_MFMA_BF16 = 2.5e15     # dense bf16 MFMA, FLOP/s
 PEAK_HBM = 8.0e12           # HBM3E, B/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+METRIC = "attention fwd/bwd TFLOP/s and % MFMA peak (bf16, d=64/128); decode HBM GB/s"
+
+# The headline kernel as rocprofv3 names it.
+HEADLINE_KERNELS = {"long_causal_prefill": ["fwd_bf16_kernel<128, 1, 128, 8, false>"]}
+
+# The pages' own figures that touch this path, quoted with their hardware.
+PAGES_CONTEXT = [
+    {"figure": "2-4x faster than standard attention (inference and training)",
+     "hardware": "not stated", "source": "FlashAttention: O Que É e Como Acelera LLMs na "
+                                         "Prática, section 'O Que É e Por Que Ela Muda o Jogo'"},
+    {"figure": "up to 10x less memory and about 3x faster at a 32k-token context, where "
+               "standard attention runs out of memory",
+     "hardware": "A100", "source": "FlashAttention: O Que É e Como Acelera LLMs na Prática, "
+                                   "section 'Exemplo Prático'"},
+    {"figure": "standard attention at GPT-2 medium, sequence 1024: 40.3 GB of HBM traffic "
+               "against 66.6 GFLOPs (memory-bound)",
+     "hardware": "A100 (HBM 1.5-2.0 TB/s)", "source": "flash-attention encyclopedia page, "
+                                                      "section 'o problema'"},
+]
 
 
-def src_digest():
+# The sources the headline kernel is built from: its HBM traffic record stays
+# valid while these are unchanged.
+HEADLINE_SOURCES = ("fa_fwd.hip", "fa_device.hpp", "fa_internal.h")
+
+
+def src_digest(names=None):
+    """Digest of the named sources under csrc/ (default: all of them)."""
     h = hashlib.sha256()
     d = os.path.join(ROOT, "io_aware_tiled_03_amd", "csrc")
-    for name in sorted(os.listdir(d)):
+    for name in sorted(os.listdir(d) if names is None else names):
         with open(os.path.join(d, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
 
 
-class Timer:
-    """HIP events recorded on the given stream around every call of one kind."""
-
-    def __init__(self, stream):
-        self.stream = stream
-        self.pairs = {}
-
-    def run(self, name, fn):
-        import torch
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record(self.stream)
-        fn()
-        b.record(self.stream)
-        self.pairs.setdefault(name, []).append((a, b))
-
-    def mean_ms(self, name):
-        p = self.pairs[name]
-        return sum(a.elapsed_time(b) for a, b in p) / len(p)
+def git_head():
+    try:
+        r = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short=12", "HEAD"],
+                           stdout=subprocess.PIPE, stderr=subprocess.DEVNULL, text=True, timeout=10)
+        return r.stdout.strip() or None
+    except (OSError, subprocess.SubprocessError):
+        return None
 
 
 def fwd_flops(B, H, N, d, causal):
     f = 4.0 * B * H * N * N * d
     return f / 2 if causal else f
-
-
-def make_step(fa, x, B, H, N, d, tau, timer=None):
-    """Returns a closure running one step; tensors are preallocated (no allocation inside)."""
-    import torch
-    q, k, v, do = x["q"], x["k"], x["v"], x["do"]
-    o_nc, lse_nc = torch.empty_like(q), torch.empty(B, H, N, device=q.device)
-    o_c, lse_c = torch.empty_like(q), torch.empty(B, H, N, device=q.device)
-    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
-    ws = torch.empty(fa.bwd_workspace_bytes(B, H, N) // 4, device=q.device)
-    qd = q[:, :, -1:, :].contiguous()
-    od, lsed = torch.empty_like(qd), torch.empty(B, H, device=q.device)
-    seq = torch.full((B,), N, dtype=torch.int32, device=q.device)
-    wsd = torch.empty(fa.decode_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
-
-    calls = [
-        ("fwd_noncausal", lambda: fa.fwd(q, k, v, tau, False, o_nc, lse_nc)),
-        ("fwd_causal", lambda: fa.fwd(q, k, v, tau, True, o_c, lse_c)),
-        ("bwd_dq", lambda: fa.bwd(q, k, v, o_c, lse_c, do, tau, True, dq, dk, dv, ws, stage=0)),
-        ("bwd_dkdv", lambda: fa.bwd(q, k, v, o_c, lse_c, do, tau, True, dq, dk, dv, ws, stage=1)),
-        ("decode", lambda: fa.decode(qd, k, v, seq, tau, 0, od, lsed, wsd)),
-    ]
-
-    def step():
-        for name, fn in calls:
-            if timer is None:
-                fn()
-            else:
-                timer.run(name, fn)
-    return step
 
 
 def window_pairs(N, window, sinks):
@@ -118,29 +108,22 @@ def window_pairs(N, window, sinks):
     return float((np.minimum(i + 1, window) + np.maximum(0, np.minimum(sinks, i - window + 1))).sum())
 
 
-def step_work(B, H, N, d):
-    """Algorithmic FLOPs and HBM bytes per call of the step (bf16 = 2 bytes)."""
-    e = 2
-    t = B * H * N * d * e          # one [B,H,N,d] bf16 tensor
-    lse = B * H * N * 4
-    n2 = B * H * N * N * d
-    return {
-        "fwd_noncausal": (4.0 * n2, 3 * t + t + lse),
-        "fwd_causal": (2.0 * n2, 3 * t + t + lse),
-        # dQ kernel: D = rowsum(dO o O) for its rows, then the dQ product (1 of
-        # the 5 backward GEMMs; its own S and dP recompute is not counted);
-        # reads Q, K, V, dO, O, LSE, writes dQ and D
-        "bwd_dq": (1.0 * n2 + 2.0 * B * H * N * d, 5 * t + 2 * lse + t),
-        # dK/dV kernel: S, dP, dV, dK products (4 of the 5 backward GEMMs), causal half
-        "bwd_dkdv": (4.0 * n2, 4 * t + 2 * lse + 2 * t),
-        "decode": (4.0 * B * H * N * d, 2 * t + 2 * B * H * d * e + B * H * 4),
-    }
+def bytes_avoided(B, H, N):
+    """HBM bytes standard attention moves for S and P at this shape: the N x N
+    fp16 score matrix per head ("Por que isso importa" table: 512 MiB per head
+    at N = 16384) written as S, read back, written as P and read by P V
+    ("flash-attention" page, "o problema")."""
+    per_head = N * N * 2
+    return {"per_head_MiB": per_head / 2 ** 20, "passes": 4,
+            "total_GiB": B * H * per_head * 4 / 2 ** 30,
+            "note": "S = Q K^T written, read for the softmax, P written, read for P V; fp16"}
 
 
-def algorithmic_step_flops(B, H, N, d):
-    """fwd nc 4BHN^2d + fwd causal 2BHN^2d + bwd causal 5BHN^2d + decode 4BHNd."""
-    n2 = B * H * N * N * d
-    return 4.0 * n2 + 2.0 * n2 + 5.0 * n2 + 4.0 * B * H * N * d
+def stats_ms(ts):
+    ts = sorted(ts)
+    q = lambda f: ts[min(len(ts) - 1, int(round(f * (len(ts) - 1))))]
+    return {"median": round(q(0.5), 5), "p10": round(q(0.1), 5), "p90": round(q(0.9), 5),
+            "mean": round(sum(ts) / len(ts), 5), "n": len(ts)}
 
 
 def load_traffic(kernel):
@@ -150,27 +133,15 @@ def load_traffic(kernel):
     except (OSError, ValueError):
         return None
     e = t.get("kernels", {}).get(kernel)
-    if not e or t.get("src_digest") != src_digest():
+    if not e or t.get("src_digest") != src_digest(HEADLINE_SOURCES):
         return None
     return e.get("bytes_per_launch")
-
-
-# The step's kernels as rocprofv3 names them (a decode with more than one
-# split also launches the merge; the step's decode has one split).
-STEP_KERNELS = {
-    "fwd_noncausal": ["fwd_bf16_kernel<64, 0, 64, 4, false>"],
-    "fwd_causal": ["fwd_bf16_kernel<64, 1, 64, 4, false>"],
-    "bwd_dq": ["bwd_dq_kernel<64, 1, false>"],
-    "bwd_dkdv": ["bwd_dkdv_kernel<64, 1, false>"],
-    "decode": ["decode_split_kernel<unsigned short, 64>", "decode_merge_kernel<unsigned short, 64>"],
-}
 
 
 def _counter_means(run_dir, counter):
     """Mean value of `counter` per dispatch, by kernel name, over the
     *counter_collection.csv files rocprofv3 wrote under run_dir."""
     import csv
-    import glob
     per = {}
     files = glob.glob(os.path.join(run_dir, "**", "*counter_collection.csv"), recursive=True)
     if not files:
@@ -187,25 +158,29 @@ def _counter_means(run_dir, counter):
     return {name: sum(d.values()) / len(d) for name, d in per.items()}
 
 
-def summarize_counters(fetch_step, fetch_copy, write_step, write_copy, copy_mib, commands):
-    """Writes profiles/traffic.json: HBM bytes per launch of the step's kernels
+def summarize_counters(fetch_run, fetch_copy, write_run, write_copy, copy_mib, commands,
+                       kernels=None):
+    """Writes profiles/traffic.json: HBM bytes per launch of the given kernels
     from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by what the
     same counter reads per byte of the plain device copy (--calibrate-copy)."""
+    kernels = HEADLINE_KERNELS if kernels is None else kernels
     copy_bytes = float(copy_mib << 20)
-    out = {"about": "HBM bytes per launch of the step's kernels (8x16x1024x64 bf16) from two "
-                    "rocprofv3 counter runs, FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each "
-                    "divided by what the same counter reads per byte of a plain %d MiB device "
-                    "copy (bench.py --calibrate-copy %d) run the same way." % (copy_mib, copy_mib),
-           "commands": commands, "copy_counter_per_byte": {}, "src_digest": src_digest(),
+    out = {"about": "HBM bytes per launch of the headline kernel (long causal prefill, "
+                    "1x32x16384x128 bf16) from two rocprofv3 counter runs, FETCH_SIZE and "
+                    "WRITE_SIZE (KiB per dispatch), each divided by what the same counter reads "
+                    "per byte of a plain %d MiB device copy (bench.py --calibrate-copy %d) run "
+                    "the same way." % (copy_mib, copy_mib),
+           "commands": commands, "copy_counter_per_byte": {},
+           "src_digest": src_digest(HEADLINE_SOURCES), "sources": list(HEADLINE_SOURCES),
            "kernels": {}}
     vals = {}
-    for counter, step_dir, copy_dir in (("FETCH_SIZE", fetch_step, fetch_copy),
-                                        ("WRITE_SIZE", write_step, write_copy)):
+    for counter, run_dir, copy_dir in (("FETCH_SIZE", fetch_run, fetch_copy),
+                                       ("WRITE_SIZE", write_run, write_copy)):
         cm = _counter_means(copy_dir, counter)
         copy_kib = max(cm.values())   # the copy is the largest dispatch of that run
         out["copy_counter_per_byte"][counter] = copy_kib * 1024.0 / copy_bytes
-        vals[counter] = _counter_means(step_dir, counter)
-    for bench_name, names in STEP_KERNELS.items():
+        vals[counter] = _counter_means(run_dir, counter)
+    for bench_name, names in kernels.items():
         e = {}
         for counter, key in (("FETCH_SIZE", "fetch"), ("WRITE_SIZE", "write")):
             kib = 0.0
@@ -224,118 +199,201 @@ def summarize_counters(fetch_step, fetch_copy, write_step, write_copy, copy_mib,
     print(json.dumps(out["kernels"]))
 
 
-def cpu_baseline(xh, B, H, N, d, tau, budget_s=10.0):
-    """The float64 oracle over whole heads of the same step until ~budget_s seconds."""
-    import numpy as np
-    from oracle import attention as orc
-    threads = None
-    try:
-        import threadpoolctl
-        info = threadpoolctl.threadpool_info()
-        threads = max((i.get("num_threads") or 0) for i in info) if info else None
-    except Exception:
-        pass
-    qf, kf, vf, dof = (xh[n].f64() for n in ("q", "k", "v", "do"))
-    heads, flops = 0, 0.0
+def read_sclk_mhz():
+    """The active shader clock level of the first GPU from sysfs, or None."""
+    for fn in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+        try:
+            with open(fn) as f:
+                for line in f:
+                    if "*" in line:
+                        tok = line.split(":")[-1].replace("*", "").strip().lower()
+                        return float(tok.replace("mhz", "").strip())
+        except (OSError, ValueError):
+            continue
+    return None
+
+
+def sample_clock(run, seconds=0.5):
+    """Runs `run` back to back for about `seconds` while sampling the sclk level."""
+    import torch
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            v = read_sclk_mhz()
+            if v is not None:
+                samples.append(v)
+            time.sleep(0.01)
+    t = threading.Thread(target=sampler, daemon=True)
+    t.start()
     t0 = time.perf_counter()
-    per_head = algorithmic_step_flops(1, 1, N, d)
-    for it in range(1 << 30):
-        b, h = divmod(it % (B * H), H)
-        orc.attention_fwd_head(qf[b, h], kf[b, h], vf[b, h], tau, False)
-        orc.attention_fwd_head(qf[b, h], kf[b, h], vf[b, h], tau, True)
-        orc.attention_bwd_head(qf[b, h], kf[b, h], vf[b, h], dof[b, h], tau, True)
-        orc.decode_fwd(qf[b:b + 1, h:h + 1, -1:], kf[b:b + 1, h:h + 1], vf[b:b + 1, h:h + 1],
-                       np.array([N]), tau)
-        heads += 1
-        flops += per_head
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s",
-            "cores": threads or os.cpu_count(), "kind": "oracle",
-            "sample": "%d (b,h) heads (cycling over the %d of the batch) of the step: fwd "
-                      "non-causal, fwd causal, bwd causal, decode; float64 NumPy, %.1f s"
-                      % (heads, B * H, dt)}
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(20):
+            run()
+        torch.cuda.synchronize()
+    stop.set()
+    t.join()
+    if not samples:
+        return None
+    s = sorted(samples)
+    return {"median": s[len(s) // 2], "min": s[0], "max": s[-1], "samples": len(s),
+            "source": "pp_dpm_sclk active level while the headline kernel runs back to back"}
+
+
+def time_events(fn, reps, warmup=10):
+    """Per-call HIP event times (ms) on the current stream, after warm-up calls."""
+    import torch
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(reps)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in ev]
+
+
+def upload(ht, dev="cuda"):
+    """HostTensor -> GPU tensor with exactly the same bits."""
+    import torch
+    if ht.dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(ht.raw).view(np.int16)).view(
+            torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(ht.raw)).to(dev)
+
+
+# --- the GPT-2-medium-shaped step (also measured) ---------------------------
+
+def gpt2m_step_work(B, H, N, d):
+    """Algorithmic FLOPs and HBM bytes per call of the step (bf16 = 2 bytes)."""
+    e = 2
+    t = B * H * N * d * e          # one [B,H,N,d] bf16 tensor
+    lse = B * H * N * 4
+    n2 = B * H * N * N * d
+    return {
+        "fwd_noncausal": (4.0 * n2, 3 * t + t + lse),
+        "fwd_causal": (2.0 * n2, 3 * t + t + lse),
+        # dQ kernel: D = rowsum(dO o O) for its rows, then the dQ product (1 of
+        # the 5 backward products; its own S and dP recompute is not counted)
+        "bwd_dq": (1.0 * n2 + 2.0 * B * H * N * d, 5 * t + 2 * lse + t),
+        # dK/dV kernel: S, dP, dV, dK products (4 of the 5 backward products), causal half
+        "bwd_dkdv": (4.0 * n2, 4 * t + 2 * lse + 2 * t),
+        "decode": (4.0 * B * H * N * d, 2 * t + 2 * B * H * d * e + B * H * 4),
+    }
+
+
+def gpt2m_step(fa, x, B, H, N, d, tau, reps):
+    """One step = fwd non-causal + fwd causal + bwd causal (its two kernels
+    enqueued one by one) + decode with one query per sequence against the same
+    K/V (L_b = N); each call timed with HIP events, and the step as a whole."""
+    import torch
+    q, k, v, do = x["q"], x["k"], x["v"], x["do"]
+    o_nc, lse_nc = torch.empty_like(q), torch.empty(B, H, N, device=q.device)
+    o_c, lse_c = torch.empty_like(q), torch.empty(B, H, N, device=q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    ws = torch.empty(fa.bwd_workspace_bytes(B, H, N) // 4, device=q.device)
+    qd = q[:, :, -1:, :].contiguous()
+    od, lsed = torch.empty_like(qd), torch.empty(B, H, device=q.device)
+    seq = torch.full((B,), N, dtype=torch.int32, device=q.device)
+    wsd = torch.empty(fa.decode_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=q.device)
+    calls = [
+        ("fwd_noncausal", lambda: fa.fwd(q, k, v, tau, False, o_nc, lse_nc)),
+        ("fwd_causal", lambda: fa.fwd(q, k, v, tau, True, o_c, lse_c)),
+        ("bwd_dq", lambda: fa.bwd(q, k, v, o_c, lse_c, do, tau, True, dq, dk, dv, ws, stage=0)),
+        ("bwd_dkdv", lambda: fa.bwd(q, k, v, o_c, lse_c, do, tau, True, dq, dk, dv, ws, stage=1)),
+        ("decode", lambda: fa.decode(qd, k, v, seq, tau, 0, od, lsed, wsd)),
+    ]
+
+    def step():
+        for _, fn in calls:
+            fn()
+    step_ms = stats_ms(time_events(step, reps))
+    work = gpt2m_step_work(B, H, N, d)
+    kernels = {}
+    for name, fn in calls:
+        ms = stats_ms(time_events(fn, reps))["median"]
+        fl, by = work[name]
+        kernels[name] = {"ms": ms, "TFLOP/s": round(fl / ms / 1e9, 2),
+                         "GB/s": round(by / ms / 1e6, 1),
+                         "frac_mfma_bf16": round(fl / ms / 1e-3 / PEAK_MFMA_BF16, 4)}
+    n2 = B * H * N * N * d
+    flops = 4.0 * n2 + 2.0 * n2 + 5.0 * n2 + 4.0 * B * H * N * d
+    out = {"shape": [B, H, N, d], "tau": tau, "step_ms": step_ms,
+           "TFLOP/s": round(flops / step_ms["median"] / 1e9, 2),
+           "frac_mfma_bf16": round(flops / step_ms["median"] / 1e-3 / PEAK_MFMA_BF16, 4),
+           "kernels": kernels}
+    return out, {"o_nc": o_nc, "lse_nc": lse_nc, "o_c": o_c, "lse_c": lse_c}
 
 
 def bench_extra(fa, reps=50):
-    """Full-size long-prefill, decode and backward workloads, each vs its roofline."""
+    """The other workloads at full size, each against its roofline."""
     import torch
-    out = {}
+
+    import fa_inputs
+    out, gpu_out = {}, {}
     dev = "cuda"
     g = torch.Generator(device=dev)
-    stream = torch.cuda.current_stream()
 
-    def time_it(fn, reps):
-        """Median of reps HIP-event pairs on the stream, after 10 warm-up calls."""
-        for _ in range(10):
-            fn()
-        torch.cuda.synchronize()
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-              for _ in range(reps)]
-        for a, b in ev:
-            a.record(stream)
-            fn()
-            b.record(stream)
-        torch.cuda.synchronize()
-        ts = sorted(a.elapsed_time(b) for a, b in ev)
-        return ts[len(ts) // 2]
+    def med(fn, n=reps):
+        return stats_ms(time_events(fn, n))["median"]
 
-    # long causal prefill: 1 x 32 x 16384 x 128, bf16
-    B, H, N, d = 1, 32, 16384, 128
-    g.manual_seed(1003)
-    q, k, v = (torch.randn(B, H, N, d, device=dev, generator=g).to(torch.bfloat16) for _ in range(3))
+    # GPT-2-medium-shaped step on the host recipe's inputs (8x16x1024x64 bf16)
+    w = fa_inputs.WORKLOADS[2]
+    xh = fa_inputs.dense_inputs(w.B, w.H, w.N, w.d, "bf16", w.seed, with_do=True)
+    x = {n: upload(xh[n]) for n in ("q", "k", "v", "do")}
+    out["gpt2m_step"], gpu_out["gpt2m"] = gpt2m_step(fa, x, w.B, w.H, w.N, w.d, w.tau, reps)
+    del x
+
+    # tiny fp32 forward (1x1x256x64, non-causal)
+    w = fa_inputs.WORKLOADS[1]
+    xh = fa_inputs.workload_inputs(w)
+    q, k, v = (upload(xh[n]) for n in ("q", "k", "v"))
     o = torch.empty_like(q)
-    lse = torch.empty(B, H, N, device=dev)
-    tau = 1 / math.sqrt(d)
-    ms = time_it(lambda: fa.fwd(q, k, v, tau, True, o, lse), reps)
-    fl = fwd_flops(B, H, N, d, True)
-    out["long_causal_prefill"] = {"shape": [B, H, N, d], "causal": True, "ms": round(ms, 4),
-                                  "TFLOP/s": round(fl / ms / 1e9, 2),
-                                  "frac_mfma_bf16": round(fl / ms / 1e-3 / PEAK_MFMA_BF16, 4)}
+    lse = torch.empty(1, 1, w.N, device=dev)
+    ms = med(lambda: fa.fwd(q, k, v, w.tau, False, o, lse))
+    out["tiny_fp32_fwd"] = {"shape": [w.B, w.H, w.N, w.d], "dtype": "f32", "ms": ms,
+                            "note": "launch-bound; checked for parity, no roofline"}
     del q, k, v, o, lse
 
-    # the same prefill as a local (sliding-window) layer: window 4096, no sinks
+    # the prefill as a local (sliding-window) layer: window 4096, no sinks
     B, H, N, d, wnd = 1, 32, 16384, 128, 4096
     g.manual_seed(1003)
     q, k, v = (torch.randn(B, H, N, d, device=dev, generator=g).to(torch.bfloat16) for _ in range(3))
     o = torch.empty_like(q)
     lse = torch.empty(B, H, N, device=dev)
-    ms = time_it(lambda: fa.fwd(q, k, v, 1 / math.sqrt(d), True, o, lse, window=wnd), reps)
+    ms = med(lambda: fa.fwd(q, k, v, 1 / math.sqrt(d), True, o, lse, window=wnd))
     fl = 4.0 * B * H * d * window_pairs(N, wnd, 0)
-    out["window_prefill"] = {"shape": [B, H, N, d], "window": wnd, "sinks": 0, "ms": round(ms, 4),
+    out["window_prefill"] = {"shape": [B, H, N, d], "window": wnd, "sinks": 0, "ms": ms,
                              "TFLOP/s": round(fl / ms / 1e9, 2),
                              "frac_mfma_bf16": round(fl / ms / 1e-3 / PEAK_MFMA_BF16, 4)}
-    del q, k, v, o, lse
 
     # the same prefill block-sparse: 128 x 128 blocks, a band of 3 blocks
     # around the diagonal plus the first key block (global tokens), causal
-    B, H, N, d, bs = 1, 32, 16384, 128, 128
+    bs = 128
     nb = N // bs
     bi, bj = np.meshgrid(np.arange(nb), np.arange(nb), indexing="ij")
     mask_np = ((np.abs(bi - bj) <= 1) | (bj == 0)).astype(np.uint8)
-    # visible pairs: whole blocks below the diagonal, half (with it) on it
     pairs = float(((mask_np == 1) & (bi > bj)).sum()) * bs * bs + nb * bs * (bs + 1) / 2
-    g.manual_seed(1003)
-    q, k, v = (torch.randn(B, H, N, d, device=dev, generator=g).to(torch.bfloat16) for _ in range(3))
-    o = torch.empty_like(q)
-    lse = torch.empty(B, H, N, device=dev)
     bm = torch.from_numpy(mask_np[None]).to(dev)
-    ms = time_it(lambda: fa.fwd(q, k, v, 1 / math.sqrt(d), True, o, lse, block_mask=bm,
-                                block_size=(bs, bs)), reps)
+    ms = med(lambda: fa.fwd(q, k, v, 1 / math.sqrt(d), True, o, lse, block_mask=bm,
+                            block_size=(bs, bs)))
     fl = 4.0 * B * H * d * pairs
     out["block_sparse_prefill"] = {"shape": [B, H, N, d], "block": [bs, bs],
                                    "pattern": "band +-1 block and global first key block, causal",
-                                   "density": round(pairs / (N * (N + 1) / 2), 4),
-                                   "ms": round(ms, 4), "TFLOP/s": round(fl / ms / 1e9, 2),
+                                   "density": round(pairs / (N * (N + 1) / 2), 4), "ms": ms,
+                                   "TFLOP/s": round(fl / ms / 1e9, 2),
                                    "frac_mfma_bf16": round(fl / ms / 1e-3 / PEAK_MFMA_BF16, 4)}
-    del q, k, v, o, lse
+    del q, k, v, o, lse, bm
 
-    # decode: 64 x 32 x 8192 x 128, L_b ~ U[1024, 8192]
-    B, H, N, d = 64, 32, 8192, 128
-    import fa_inputs
-    seqlens = fa_inputs.decode_seqlens(B, 1024, 8192, 1004 + 400)
-    g.manual_seed(1004)
+    # split-KV decode: 64 x 32 x 8192 x 128, L_b ~ U[1024, 8192]
+    w = fa_inputs.WORKLOADS[4]
+    B, H, N, d = w.B, w.H, w.N, w.d
+    seqlens = fa_inputs.decode_seqlens(B, w.lmin, w.lmax, w.seed + fa_inputs.SEED_OFFSET["seqlens"])
+    g.manual_seed(w.seed)
     q = torch.randn(B, H, 1, d, device=dev, generator=g).to(torch.bfloat16)
     k = torch.empty(B, H, N, d, device=dev, dtype=torch.bfloat16)
     v = torch.empty_like(k)
@@ -346,19 +404,18 @@ def bench_extra(fa, reps=50):
     o = torch.empty_like(q)
     lse = torch.empty(B, H, device=dev)
     ws = torch.empty(fa.decode_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
-    ms = time_it(lambda: fa.decode(q, k, v, sl, 1 / math.sqrt(d), 0, o, lse, ws), reps * 2)
+    ms = med(lambda: fa.decode(q, k, v, sl, w.tau, 0, o, lse, ws), 2 * reps)
     if not bool(torch.isfinite(o.float()).all()):
         raise RuntimeError("decode produced non-finite output")
     nbytes = float(seqlens.astype("int64").sum()) * H * d * 2 * 2 + 2 * B * H * d * 2 + B * H * 4
     out["decode_splitkv"] = {"shape": [B, H, N, d], "seqlens_sum": int(seqlens.sum()),
                              "num_splits": fa.decode_num_splits(B, H, N, d),
-                             "ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1),
+                             "ms": ms, "GB/s": round(nbytes / ms / 1e6, 1),
                              "frac_hbm": round(nbytes / ms / 1e-3 / PEAK_HBM, 4)}
     del q, k, v, o, lse, ws
 
     # paged decode with grouped KV heads: B=64, Hq=32, Hkv=8, 16-token pages,
     # d=128, the dense decode's key lengths; pages assigned in a seeded random order
-    import fa_inputs
     w = fa_inputs.PAGED_WORKLOAD
     B, Hq, Hkv, P, d = w.B, w.Hq, w.Hkv, w.page_size, w.d
     seqlens = fa_inputs.decode_seqlens(B, w.lmin, w.lmax, w.seqlens_seed)
@@ -384,8 +441,7 @@ def bench_extra(fa, reps=50):
     lse = torch.empty(B, Hq, device=dev)
     ws = torch.empty(fa.decode_paged_workspace_bytes(B, Hq, Hkv, P, maxp, d), dtype=torch.uint8,
                      device=dev)
-    ms = time_it(lambda: fa.decode_paged(q, kp, vp, table, sl, 1 / math.sqrt(d), 0, o, lse, ws),
-                 reps * 2)
+    ms = med(lambda: fa.decode_paged(q, kp, vp, table, sl, w.tau, 0, o, lse, ws), 2 * reps)
     if not bool(torch.isfinite(o.float()).all()):
         raise RuntimeError("paged decode produced non-finite output")
     nbytes = (float(seqlens.astype("int64").sum()) * Hkv * d * 2 * 2 + 2 * B * Hq * d * 2
@@ -393,60 +449,145 @@ def bench_extra(fa, reps=50):
     out["decode_paged_gqa"] = {"shape": {"B": B, "Hq": Hq, "Hkv": Hkv, "page_size": P, "d": d},
                                "seqlens_sum": int(seqlens.sum()),
                                "num_splits": fa.decode_paged_num_splits(B, Hq, Hkv, P, maxp, d),
-                               "ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1),
+                               "ms": ms, "GB/s": round(nbytes / ms / 1e6, 1),
                                "frac_hbm": round(nbytes / ms / 1e-3 / PEAK_HBM, 4)}
     del q, kp, vp, o, lse, ws, table
 
     # backward: 4 x 16 x 4096 x 64, causal
-    B, H, N, d = 4, 16, 4096, 64
-    g.manual_seed(1005)
+    w = fa_inputs.WORKLOADS[5]
+    B, H, N, d = w.B, w.H, w.N, w.d
+    g.manual_seed(w.seed)
     q, k, v, do = (torch.randn(B, H, N, d, device=dev, generator=g).to(torch.bfloat16)
                    for _ in range(4))
-    tau = 1 / math.sqrt(d)
-    o, lse = fa.fwd(q, k, v, tau, True)
+    o, lse = fa.fwd(q, k, v, w.tau, True)
     dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     ws = torch.empty(B * H * N, device=dev)
-    ms = time_it(lambda: fa.bwd(q, k, v, o, lse, do, tau, True, dq, dk, dv, ws), reps)
+    ms = med(lambda: fa.bwd(q, k, v, o, lse, do, w.tau, True, dq, dk, dv, ws))
+    ms_dq = med(lambda: fa.bwd(q, k, v, o, lse, do, w.tau, True, dq, dk, dv, ws, stage=0))
+    ms_dkdv = med(lambda: fa.bwd(q, k, v, o, lse, do, w.tau, True, dq, dk, dv, ws, stage=1))
     fl = 10.0 * B * H * N * N * d / 2
-    out["bwd_recompute"] = {"shape": [B, H, N, d], "causal": True, "ms": round(ms, 4),
+    out["bwd_recompute"] = {"shape": [B, H, N, d], "causal": True, "ms": ms,
                             "TFLOP/s": round(fl / ms / 1e9, 2),
-                            "frac_mfma_bf16": round(fl / ms / 1e-3 / PEAK_MFMA_BF16, 4)}
+                            "frac_mfma_bf16": round(fl / ms / 1e-3 / PEAK_MFMA_BF16, 4),
+                            "dq_kernel_ms": ms_dq, "dkdv_kernel_ms": ms_dkdv,
+                            "flops_convention": "10*B*H*N^2*d/2 (5 products incl. the S "
+                                                "recompute, causal half)"}
 
     # the same shape with dropout p = 0.1 (Philox mask regenerated in the backward)
     drop = (0.1, 1005, 0)
-    ms_f = time_it(lambda: fa.fwd(q, k, v, tau, True, o, lse, dropout=drop), reps)
-    ms_b = time_it(lambda: fa.bwd(q, k, v, o, lse, do, tau, True, dq, dk, dv, ws, dropout=drop),
-                   reps)
+    ms_f = med(lambda: fa.fwd(q, k, v, w.tau, True, o, lse, dropout=drop))
+    ms_b = med(lambda: fa.bwd(q, k, v, o, lse, do, w.tau, True, dq, dk, dv, ws, dropout=drop))
     ffl = 4.0 * B * H * N * N * d / 2
     out["dropout"] = {"shape": [B, H, N, d], "causal": True, "p": 0.1,
-                      "fwd_ms": round(ms_f, 4), "fwd_TFLOP/s": round(ffl / ms_f / 1e9, 2),
-                      "bwd_ms": round(ms_b, 4), "bwd_TFLOP/s": round(fl / ms_b / 1e9, 2)}
+                      "fwd_ms": ms_f, "fwd_TFLOP/s": round(ffl / ms_f / 1e9, 2),
+                      "bwd_ms": ms_b, "bwd_TFLOP/s": round(fl / ms_b / 1e9, 2)}
+    return out, gpu_out
+
+
+def _blas_threads():
+    try:
+        import threadpoolctl
+        info = threadpoolctl.threadpool_info()
+        return max((i.get("num_threads") or 0) for i in info) if info else None
+    except Exception:
+        return None
+
+
+def cpu_baseline(xh3, o3, lse3, gpu_extra=None):
+    """The float64 oracle on the host.
+
+    Headline: two whole heads of the long causal prefill (every row), timed;
+    the rate in TFLOP/s is that of the oracle on those heads, and the GPU's O
+    and LSE of the same heads are compared with it.  Also: the oracle's wall
+    time on the other workloads (whole, or a stated sample extrapolated)."""
+    from oracle import attention as orc
+
+    import fa_inputs
+    w = fa_inputs.WORKLOADS[3]
+    qf, kf, vf = (xh3[n].f64() for n in ("q", "k", "v"))
+    heads = (0, 31)
+    t0 = time.perf_counter()
+    ref = [orc.attention_fwd_head(qf[0, h], kf[0, h], vf[0, h], w.tau, True) for h in heads]
+    dt = time.perf_counter() - t0
+    fl = fwd_flops(1, len(heads), w.N, w.d, True)
+    err_o = np.concatenate([np.abs(o3[0, h] - r[0]).ravel() for h, r in zip(heads, ref)])
+    err_l = np.concatenate([np.abs(lse3[0, h] - r[1]).ravel() for h, r in zip(heads, ref)])
+    out = {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s",
+           "cores": _blas_threads() or os.cpu_count(), "kind": "oracle",
+           "sample": "heads %s of the long causal prefill (1x32x16384x128, every row), float64 "
+                     "NumPy with explicit score rows, %.1f s; the full 32-head job extrapolates "
+                     "to %.0f s" % (list(heads), dt, dt * 16),
+           "parity_sampled_heads": {"O_max_abs": float(err_o.max()), "O_mean_abs": float(err_o.mean()),
+                                    "LSE_max_abs": float(err_l.max()),
+                                    "bounds": "O max 2e-2, mean 2e-3; LSE 1e-3"}}
+    other = {}
+    # tiny fp32 forward: whole
+    w1 = fa_inputs.WORKLOADS[1]
+    x1 = fa_inputs.workload_inputs(w1)
+    t0 = time.perf_counter()
+    orc.attention_fwd(*(x1[n].f64() for n in ("q", "k", "v")), w1.tau, False)
+    other["tiny_fp32_fwd"] = {"wall_s": round(time.perf_counter() - t0, 4), "sample": "whole"}
+    # GPT-2-medium shape: both masks, whole; GPU outputs compared when given
+    w2 = fa_inputs.WORKLOADS[2]
+    x2 = fa_inputs.workload_inputs(w2)
+    q2, k2, v2 = (x2[n].f64() for n in ("q", "k", "v"))
+    t0 = time.perf_counter()
+    r_nc = orc.attention_fwd(q2, k2, v2, w2.tau, False)
+    r_c = orc.attention_fwd(q2, k2, v2, w2.tau, True)
+    e = {"wall_s": round(time.perf_counter() - t0, 3), "sample": "whole, non-causal and causal"}
+    if gpu_extra and "gpt2m" in gpu_extra:
+        gm = gpu_extra["gpt2m"]
+        for tag, key, r in (("noncausal", "o_nc", r_nc), ("causal", "o_c", r_c)):
+            d = np.abs(gm[key] - r[0])
+            e["O_%s_max_abs" % tag] = float(d.max())
+            e["O_%s_mean_abs" % tag] = float(d.mean())
+    other["gpt2m_fwd"] = e
+    # backward workload: 4 of 64 heads, extrapolated x16
+    w5 = fa_inputs.WORKLOADS[5]
+    x5 = fa_inputs.workload_inputs(w5)
+    q5, k5, v5, d5 = (x5[n].f64() for n in ("q", "k", "v", "do"))
+    t0 = time.perf_counter()
+    for b, h in ((0, 0), (1, 5), (2, 10), (3, 15)):
+        orc.attention_bwd_head(q5[b, h], k5[b, h], v5[b, h], d5[b, h], w5.tau, True)
+    t = time.perf_counter() - t0
+    other["bwd_recompute"] = {"wall_s": round(t * 16, 2),
+                              "sample": "4 of 64 heads (forward and gradients), extrapolated x16"}
+    # split-KV decode: 8 of 64 sequences, extrapolated by their key count
+    w4 = fa_inputs.WORKLOADS[4]
+    sl = fa_inputs.decode_seqlens(w4.B, w4.lmin, w4.lmax, w4.seed + fa_inputs.SEED_OFFSET["seqlens"])
+    x4 = fa_inputs.decode_inputs(8, w4.H, w4.N, w4.d, "bf16", w4.seed, sl[:8])
+    t0 = time.perf_counter()
+    orc.decode_fwd(x4["q"].f64(), x4["k"].f64(), x4["v"].f64(), x4["seqlens"], w4.tau)
+    t = time.perf_counter() - t0
+    other["decode_splitkv"] = {"wall_s": round(t * float(sl.sum()) / float(sl[:8].sum()), 2),
+                               "sample": "8 of 64 sequences, extrapolated by key count"}
+    out["other_workloads"] = other
     return out
 
 
 def main(argv=None):
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times "
                          "(scales the HBM byte counters of a profiler run) and exit")
     ap.add_argument("--summarize-counters", nargs=4, default=None,
-                    metavar=("FETCH_STEP", "FETCH_COPY", "WRITE_STEP", "WRITE_COPY"),
+                    metavar=("FETCH_RUN", "FETCH_COPY", "WRITE_RUN", "WRITE_COPY"),
                     help="write profiles/traffic.json from four rocprofv3 --pmc output "
-                         "directories (FETCH_SIZE and WRITE_SIZE, each over a step run and a "
+                         "directories (FETCH_SIZE and WRITE_SIZE, each over a headline run and a "
                          "--calibrate-copy 1024 run) and exit; runs on the host, no GPU")
     args = ap.parse_args(argv)
     if args.summarize_counters:
         d = args.summarize_counters
         cmds = ["rocprofv3 --pmc %s --output-format csv -d %s -o %s -- python -u bench.py %s"
                 % (c, r, o, a) for c, r, o, a in (
-                    ("FETCH_SIZE", d[0], "step", "--steps 3 --warmup 1 --no-extra --no-cpu"),
+                    ("FETCH_SIZE", d[0], "run", "--steps 5 --warmup 1 --no-extra --no-cpu"),
                     ("FETCH_SIZE", d[1], "copy", "--calibrate-copy 1024"),
-                    ("WRITE_SIZE", d[2], "step", "--steps 3 --warmup 1 --no-extra --no-cpu"),
+                    ("WRITE_SIZE", d[2], "run", "--steps 5 --warmup 1 --no-extra --no-cpu"),
                     ("WRITE_SIZE", d[3], "copy", "--calibrate-copy 1024"))]
         summarize_counters(d[0], d[1], d[2], d[3], 1024, cmds)
         return 0
@@ -456,7 +597,6 @@ def main(argv=None):
               % args.gpus, file=sys.stderr)
         return 2
 
-    import numpy as np
     import torch
 
     import fa_inputs
@@ -476,69 +616,76 @@ def main(argv=None):
         print(json.dumps({"copy_bytes": n, "launches": 5}))
         return 0
 
-    w = fa_inputs.WORKLOADS[2]
+    w = fa_inputs.WORKLOADS[3]
     B, H, N, d, tau = w.B, w.H, w.N, w.d, w.tau
-    xh = fa_inputs.dense_inputs(B, H, N, d, "bf16", w.seed, with_do=True)
-    x = {n: torch.from_numpy(np.ascontiguousarray(xh[n].raw).view(np.int16)).view(
-        torch.bfloat16).cuda() for n in ("q", "k", "v", "do")}
+    xh = fa_inputs.workload_inputs(w)
+    q, k, v = (upload(xh[n]) for n in ("q", "k", "v"))
+    o = torch.empty_like(q)
+    lse = torch.empty(B, H, N, device="cuda")
+    run = lambda: fa.fwd(q, k, v, tau, True, o, lse)
+    flops = fwd_flops(B, H, N, d, True)
 
-    plain = make_step(fa, x, B, H, N, d, tau)
     for _ in range(args.warmup):
-        plain()
+        run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        plain()
+    for a, b in ev:
+        a.record(stream)
+        run()
+        b.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    ev_ms = [a.elapsed_time(b) for a, b in ev]
+    timing = stats_ms(ev_ms)
     ms_step = wall / args.steps * 1e3
-    step_flops = algorithmic_step_flops(B, H, N, d)
-    value = step_flops / (wall / args.steps) / 1e12
-
-    # per-call HIP events over a second timed pass of the same steps
-    stream = torch.cuda.current_stream()
-    timer = Timer(stream)
-    timed = make_step(fa, x, B, H, N, d, tau, timer)
-    torch.cuda.synchronize()
-    for _ in range(args.steps):
-        timed()
-    torch.cuda.synchronize()
-    work = step_work(B, H, N, d)
-    kernels = {}
-    for name in work:
-        ms = timer.mean_ms(name)
-        fl, by = work[name]
-        kernels[name] = {"ms": round(ms, 5), "TFLOP/s": round(fl / ms / 1e9, 2),
-                         "GB/s": round(by / ms / 1e6, 1)}
-    dom = max(kernels, key=lambda n: kernels[n]["ms"])
-    fl, by = work[dom]
-    dms = timer.mean_ms(dom)
-    if fl / by > 300:
-        roof = {"bound": "mfma", "achieved": round(fl / dms / 1e9, 2), "peak": PEAK_MFMA_BF16 / 1e12,
-                "unit": "TFLOP/s"}
-    else:
-        roof = {"bound": "hbm", "achieved": round(by / dms / 1e6, 1), "peak": PEAK_HBM / 1e9,
-                "unit": "GB/s"}
-    roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
-    roof["kernel"] = dom
-    roof["traffic"] = load_traffic(dom)
+    value = flops / (wall / args.steps) / 1e12
+    achieved = flops / timing["mean"] / 1e9
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_MFMA_BF16 / 1e12,
+            "unit": "TFLOP/s", "frac": round(achieved * 1e12 / PEAK_MFMA_BF16, 4),
+            "kernel": HEADLINE_KERNELS["long_causal_prefill"][0],
+            "algorithmic_flops_per_launch": flops,
+            "traffic": load_traffic("long_causal_prefill"),
+            "algorithmic_bytes_per_launch": 4 * B * H * N * d * 2 + B * H * N * 4}
+    o_host = o.float().cpu().numpy().astype(np.float64)
+    lse_host = lse.cpu().numpy().astype(np.float64)
+    if not (np.isfinite(o_host).all() and np.isfinite(lse_host).all()):
+        raise RuntimeError("the headline forward produced non-finite output")
+    clock = sample_clock(run)
 
     line = {
-        "metric": "attention fwd/bwd TFLOP/s and % MFMA peak (bf16, d=64/128); decode HBM GB/s",
-        "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": "gpt2-medium-shaped attention step: fwd non-causal + fwd causal "
-                               "+ bwd causal + decode (L_b=N)", "B": B, "H": H, "N": N, "d": d,
-                   "tau": tau, "parallelism": "single GPU"},
+        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: fp32 N(0,1) draws from PCG64 rounded to bf16 (seeds 1003, 1103, 1203)",
+        "config": {"workload": "long-context causal prefill forward: B=1, H=32, N=16384, d=128, "
+                               "bf16, causal, tau=1/sqrt(128)",
+                   "B": B, "H": H, "N": N, "d": d, "tau": tau, "causal": True,
+                   "seeds": {"q": w.seed, "k": w.seed + 100, "v": w.seed + 200},
+                   "parallelism": "single GPU"},
         "frac_of_mfma_peak": round(value * 1e12 / PEAK_MFMA_BF16, 4),
-        "kernels": kernels,
+        "timing_ms": timing,
         "roofline": roof,
+        "sclk_mhz": clock,
+        "bytes_avoided": bytes_avoided(B, H, N),
+        "pages_context": PAGES_CONTEXT,
+        "git": git_head(),
+        "src_digest": src_digest(),
     }
+    del q, k, v, o, lse
+    torch.cuda.empty_cache()
+    gpu_extra = None
     if not args.no_extra:
-        line["also_measured"] = bench_extra(fa)
+        line["also_measured"], gpu_extra = bench_extra(fa)
+        if gpu_extra:
+            gm = gpu_extra["gpt2m"]
+            gpu_extra = {"gpt2m": {"o_nc": gm["o_nc"].float().cpu().numpy().astype(np.float64),
+                                   "o_c": gm["o_c"].float().cpu().numpy().astype(np.float64)}}
     if not args.no_cpu:
-        line["cpu_baseline"] = cpu_baseline(xh, B, H, N, d, tau)
+        line["cpu_baseline"] = cpu_baseline(xh, o_host, lse_host, gpu_extra)
     print(json.dumps(line), flush=True)
     return 0
 

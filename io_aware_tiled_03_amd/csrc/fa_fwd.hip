@@ -195,103 +195,119 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
 #pragma unroll
             for (int kb = 0; kb < NKB; ++kb) bbit[kb] = block_bit(k0 + 32 * kb);
         }
-        f32x16 s[NKB];
+        // S^T = K Q^T for the tile (rows: keys in kperm order, columns: this
+        // wave's queries), with -inf where a key is not visible
+        auto scores = [&](f32x16 (&s)[NKB]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kb = 0; kb < NKB; ++kb) {
-            u32x4 ka[D / 16];   // all operands of the block first, then the MFMA chain
+            for (int kb = 0; kb < NKB; ++kb) {
+                u32x4 ka[D / 16];   // all operands of the block first, then the MFMA chain
 #pragma unroll
-            for (int ks = 0; ks < D / 16; ++ks) ka[ks] = ld16(&sk[k_off + kb * 32 * KSTR + ks * 16]);
-            s[kb] = mfma32x32x16_zero(ka[0], qf[0]);
+                for (int ks = 0; ks < D / 16; ++ks) ka[ks] = ld16(&sk[k_off + kb * 32 * KSTR + ks * 16]);
+                s[kb] = mfma32x32x16_zero(ka[0], qf[0]);
 #pragma unroll
-            for (int ks = 1; ks < D / 16; ++ks) s[kb] = mfma32x32x16(ka[ks], qf[ks], s[kb]);
-        }
+                for (int ks = 1; ks < D / 16; ++ks) s[kb] = mfma32x32x16(ka[ks], qf[ks], s[kb]);
+            }
 #if FA_FWD_SCHED
-        if constexpr (D == 128 && !DROP && !BLK) {
-            // the score products as a scheduling region of their own: AH K
-            // operand reads first, then two products per two further reads
-            constexpr int NR = NKB * D / 16, AH = FA_FWD_SCHED;
-            __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);
+            if constexpr (D == 128 && !DROP && !BLK) {
+                // the score products as a scheduling region of their own: AH K
+                // operand reads first, then two products per two further reads
+                constexpr int NR = NKB * D / 16, AH = FA_FWD_SCHED;
+                __builtin_amdgcn_sched_group_barrier(0x100, AH, 0);
 #pragma unroll
-            for (int i = 0; i < (NR - AH) / 2; ++i) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
-                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                for (int i = 0; i < (NR - AH) / 2; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+                }
+                __builtin_amdgcn_sched_group_barrier(0x008, AH, 0);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            __builtin_amdgcn_sched_group_barrier(0x008, AH, 0);
-            __builtin_amdgcn_sched_barrier(0);
-        }
 #endif
-        if constexpr (MASK) {
+            if constexpr (MASK) {
 #pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
+                for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7);
-                    if (key >= N ||
-                        (CAUSAL && (key > qrow || (WIN && qrow - key >= window && key >= sinks))) ||
-                        (BLK && !bbit[kb]))
-                        s[kb][r] = neg_inf();
-                }
-        }
-        float mx = s[0][0];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-        mx = fmaxf(mx, xor32(mx));
-        // Move the reference max only when some score exceeds it by more than
-        // 2^FA_FWD_RESCALE_LOG2 (then P <= 2^8 stays well inside fp32/bf16 range).
-        const bool grow = (mx - m) * scale_log2 > FA_FWD_RESCALE_LOG2;
-        if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-            const float mnew = fmaxf(m, mx);
-            // under a window or a block mask a row may have seen no visible key
-            // yet (m = mnew = -inf, l and O still zero): keep it as it is
-            const float alpha = (SPARSE_ROWS && m == mnew) ? 1.f : fast_exp2((m - mnew) * scale_log2);
-            l *= alpha;
-#pragma unroll
-            for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-            m = mnew;
-        }
-        // a row with no visible key so far keeps m = -inf; its scores are all
-        // -inf as well, so any finite reference gives p = 0
-        const float mc = (SPARSE_ROWS && MASK && m == neg_inf()) ? 0.f : m * scale_log2;
-        // Dropout words, one generator call per lane per 32-key block: the four
-        // lanes of a quad hold rows of one 4-row block, so lane r computes the
-        // block of key group r (keys 16(r/2) + 8hf + 4(r%2) + 0..3) and a quad
-        // transpose hands every lane its own row's word of all four groups.
-        u32x4 dwq[NKB];
-        if constexpr (DROP) {
-            const int r4 = qrow & 3;
-#pragma unroll
-            for (int kb = 0; kb < NKB; ++kb)
-                dwq[kb] = quad_transpose(
-                    drop.block(k0 + kb * 32 + 16 * (r4 >> 1) + 8 * hf + 4 * (r4 & 1), qrow, bh), r4);
-        }
-        u32x4 pf[NKB][2];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) {
-                // dropout words of this lane's row for keys k0+32kb+16t+8hf+0..3 and +4..7
-                uint32_t dw[2] = {0u, 0u};
-                if constexpr (DROP) {
-                    dw[0] = dwq[kb][2 * t];
-                    dw[1] = dwq[kb][2 * t + 1];
-                }
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const int r = 8 * t + 2 * w;
-                    float p0 = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, -mc));
-                    float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], scale_log2, -mc));
-                    l += p0 + p1;
-                    if constexpr (DROP) {   // keys 2(w%2), 2(w%2)+1 of the 4-key group w/2
-                        p0 = drop.keep(dw[w >> 1], 2 * (w & 1)) ? p0 : 0.f;
-                        p1 = drop.keep(dw[w >> 1], 2 * (w & 1) + 1) ? p1 : 0.f;
+                    for (int r = 0; r < 16; ++r) {
+                        const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7);
+                        if (key >= N ||
+                            (CAUSAL && (key > qrow || (WIN && qrow - key >= window && key >= sinks))) ||
+                            (BLK && !bbit[kb]))
+                            s[kb][r] = neg_inf();
                     }
-                    pf[kb][t][w] = pack_bf16x2(p0, p1);
-                }
             }
+        };
+        // Move the reference to the tile's maximum where that exceeds it by
+        // more than 2^min_log2 (rescaling O and l); returns the reference in
+        // log2 units for the exponent.
+        auto rebase = [&](const f32x16 (&s)[NKB], float min_log2) __attribute__((always_inline)) {
+            float mx = s[0][0];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+            mx = fmaxf(mx, xor32(mx));
+            const bool grow = (mx - m) * scale_log2 > min_log2;
+            if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+                const float mnew = fmaxf(m, mx);
+                // under a window or a block mask a row may have seen no visible key
+                // yet (m = mnew = -inf, l and O still zero): keep it as it is
+                const float alpha = (SPARSE_ROWS && m == mnew) ? 1.f : fast_exp2((m - mnew) * scale_log2);
+                l *= alpha;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+                m = mnew;
+            }
+            // a row with no visible key so far keeps m = -inf; its scores are all
+            // -inf as well, so any finite reference gives p = 0
+            return (SPARSE_ROWS && m == neg_inf()) ? 0.f : m * scale_log2;
+        };
+        // P = exp2(S tau log2(e) - mc) for the tile, packed to bf16 as the B
+        // operand of the P V product; returns this lane's sum of the
+        // (undropped) probabilities.
+        auto probs = [&](const f32x16 (&s)[NKB], float mc, u32x4 (&pf)[NKB][2]) __attribute__((always_inline)) {
+            // Dropout words, one generator call per lane per 32-key block: the four
+            // lanes of a quad hold rows of one 4-row block, so lane r computes the
+            // block of key group r (keys 16(r/2) + 8hf + 4(r%2) + 0..3) and a quad
+            // transpose hands every lane its own row's word of all four groups.
+            u32x4 dwq[NKB];
+            if constexpr (DROP) {
+                const int r4 = qrow & 3;
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+                    dwq[kb] = quad_transpose(
+                        drop.block(k0 + kb * 32 + 16 * (r4 >> 1) + 8 * hf + 4 * (r4 & 1), qrow, bh), r4);
+            }
+            float lt = 0.f;
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    // dropout words of this lane's row for keys k0+32kb+16t+8hf+0..3 and +4..7
+                    uint32_t dw[2] = {0u, 0u};
+                    if constexpr (DROP) {
+                        dw[0] = dwq[kb][2 * t];
+                        dw[1] = dwq[kb][2 * t + 1];
+                    }
+#pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const int r = 8 * t + 2 * w;
+                        float p0 = fast_exp2(__builtin_fmaf(s[kb][r], scale_log2, -mc));
+                        float p1 = fast_exp2(__builtin_fmaf(s[kb][r + 1], scale_log2, -mc));
+                        lt += p0 + p1;
+                        if constexpr (DROP) {   // keys 2(w%2), 2(w%2)+1 of the 4-key group w/2
+                            p0 = drop.keep(dw[w >> 1], 2 * (w & 1)) ? p0 : 0.f;
+                            p1 = drop.keep(dw[w >> 1], 2 * (w & 1) + 1) ? p1 : 0.f;
+                        }
+                        pf[kb][t][w] = pack_bf16x2(p0, p1);
+                    }
+                }
+            return lt;
+        };
+        f32x16 s[NKB];
+        u32x4 pf[NKB][2];
+        scores(s);
+        l += probs(s, rebase(s, FA_FWD_RESCALE_LOG2), pf);
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll

@@ -36,11 +36,12 @@ def test_summarize_counters_scales_by_the_copy_and_maps_kernels(tmp_path, monkey
     copy_kib = mib * 1024   # a 1 GiB copy read as 1 GiB: 1 KiB per KiB
     step = []
     did = 0
-    for bench_name, names in bench.STEP_KERNELS.items():
+    for bench_name, names in bench.HEADLINE_KERNELS.items():
         for rep in range(2):   # two dispatches each; the mean is taken
-            for i, n in enumerate(names[:1]):   # the step's decode has no merge
+            for i, n in enumerate(names[:1]):
                 did += 1
                 step.append((did, _kname(n), 100.0 + 10 * rep + i))
+    step.append((did + 1, _kname("other_kernel<1>"), 7.0))   # not the headline: ignored
     for counter, scale in (("FETCH_SIZE", 0.5), ("WRITE_SIZE", 1.0)):
         _write(str(tmp_path / ("s_" + counter)), counter, step)
         _write(str(tmp_path / ("c_" + counter)), counter,
@@ -51,8 +52,8 @@ def test_summarize_counters_scales_by_the_copy_and_maps_kernels(tmp_path, monkey
                              mib, ["cmd"])
     t = json.loads(out.read_text())
     assert t["copy_counter_per_byte"] == {"FETCH_SIZE": 0.5, "WRITE_SIZE": 1.0}
-    assert t["src_digest"] == bench.src_digest()
-    for name in bench.STEP_KERNELS:
+    assert t["src_digest"] == bench.src_digest(bench.HEADLINE_SOURCES)
+    for name in bench.HEADLINE_KERNELS:
         e = t["kernels"][name]
         assert e["FETCH_SIZE_KiB"] == 105.0 and e["WRITE_SIZE_KiB"] == 105.0
         # FETCH reads half a KiB per KiB moved, so 105 KiB counted are 210 KiB moved
@@ -60,4 +61,22 @@ def test_summarize_counters_scales_by_the_copy_and_maps_kernels(tmp_path, monkey
         assert e["write_bytes"] == 105.0 * 1024
         assert e["bytes_per_launch"] == int(105.0 * 1024 * 3)
     # the bench line reads it back while the digest matches the sources
-    assert bench.load_traffic("bwd_dkdv") == int(105.0 * 1024 * 3)
+    assert bench.load_traffic("long_causal_prefill") == int(105.0 * 1024 * 3)
+
+
+def test_bytes_avoided_matches_the_pages_table():
+    """512 MiB per head of fp16 scores at N = 16384, four passes over 32 heads."""
+    b = bench.bytes_avoided(1, 32, 16384)
+    assert b["per_head_MiB"] == 512 and b["total_GiB"] == 64
+
+
+def test_timing_stats_and_flop_convention():
+    s = bench.stats_ms([float(x) for x in range(1, 102)])
+    assert s["median"] == 51 and s["p10"] == 11 and s["p90"] == 91 and s["n"] == 101
+    assert bench.fwd_flops(1, 32, 16384, 128, True) == 4 * 32 * 16384 ** 2 * 128 / 2
+    assert bench.window_pairs(10, 10, 0) == 55 and bench.window_pairs(10, 1, 0) == 10
+
+
+def test_bench_refuses_more_than_one_gpu(capsys):
+    assert bench.main(["--gpus", "2"]) == 2
+    assert "one GPU" in capsys.readouterr().err
