@@ -53,8 +53,10 @@ typedef enum {
     FA_ERR_WORKSPACE = 4,    /* workspace NULL or smaller than required        */
     FA_ERR_HIP = 5,          /* the HIP runtime reported a launch error        */
     FA_ERR_ALIGN = 6,        /* a pointer is not 16-byte aligned               */
-    FA_ERR_ARG = 7           /* a value out of range: tau, split count, window,
+    FA_ERR_ARG = 7,          /* a value out of range: tau, split count, window,
                                 sinks, stage, dropout probability, block size   */
+    FA_ERR_SCRATCH = 8       /* fa_decode_noalloc: the call needs more than the
+                                library's fixed scratch array                   */
 } fa_status;
 
 typedef enum { FA_F32 = 0, FA_BF16 = 1 } fa_dtype;
@@ -188,6 +190,29 @@ int fa_decode(const void* q, const void* k, const void* v, const int* seqlens_k,
               int B, int H, int N_max, int d, float tau, void* o, float* lse,
               int num_splits, void* workspace, size_t workspace_bytes,
               int dtype, void* stream);
+
+/*
+ * fa_decode_noalloc - fa_decode for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels, split count and results as fa_decode, but
+ * the split partials live in a fixed array the library holds on each GPU
+ * (FA_DECODE_NOALLOC_SCRATCH_BYTES, allocated with the library's code object
+ * and kept until the process ends) instead of a workspace argument.
+ *
+ * Arguments as for fa_decode, without the workspace.  The call allocates
+ * nothing; its first call on a device looks up that device's array address.
+ * It returns FA_ERR_SCRATCH (launching nothing) when
+ * fa_decode_workspace_bytes(B, H, N_max, d, num_splits) exceeds
+ * FA_DECODE_NOALLOC_SCRATCH_BYTES; one split (automatic for N_max <= 1024)
+ * uses no partials at all.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (other streams, other host threads) race and
+ * must be ordered by the caller.  Nothing in the array needs clearing: each
+ * call writes every partial it reads.
+ */
+#define FA_DECODE_NOALLOC_SCRATCH_BYTES (16u << 20)
+int fa_decode_noalloc(const void* q, const void* k, const void* v, const int* seqlens_k,
+                      int B, int H, int N_max, int d, float tau, void* o, float* lse,
+                      int num_splits, int dtype, void* stream);
 
 /*
  * fa_decode_paged_num_splits / fa_decode_paged_workspace_bytes - the split

@@ -23,7 +23,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_F32, FA_BF16 = 0, 1
 STATUS = {0: "FA_OK", 1: "FA_ERR_NULL", 2: "FA_ERR_SHAPE", 3: "FA_ERR_UNSUPPORTED",
-          4: "FA_ERR_WORKSPACE", 5: "FA_ERR_HIP", 6: "FA_ERR_ALIGN", 7: "FA_ERR_ARG"}
+          4: "FA_ERR_WORKSPACE", 5: "FA_ERR_HIP", 6: "FA_ERR_ALIGN", 7: "FA_ERR_ARG",
+          8: "FA_ERR_SCRATCH"}
 
 # (name, restype, argtypes) of every symbol that fa.h declares.
 _P, _I, _F, _Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
@@ -37,6 +38,7 @@ SIGNATURES = {
     "fa_decode_workspace_bytes": (_Z, [_I, _I, _I, _I, _I]),
     "fa_decode_num_splits": (_I, [_I, _I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _I, _P, _Z, _I, _P]),
+    "fa_decode_noalloc": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _F, _P, _P, _I, _I, _P]),
     "fa_decode_paged_num_splits": (_I, [_I, _I, _I, _I, _I, _I, _I]),
     "fa_decode_paged_workspace_bytes": (_Z, [_I, _I, _I, _I, _I, _I, _I]),
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _I, _P,
@@ -247,6 +249,32 @@ def decode(q, k, v, seqlens_k, tau=None, num_splits=0, o=None, lse=None, workspa
                          workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                          _dtype_code(q), _stream(q))
     check("fa_decode", st)
+    return o, lse
+
+
+def decode_noalloc(q, k, v, seqlens_k, tau=None, num_splits=0, o=None, lse=None):
+    """fa_decode without a workspace argument, via fa_decode_noalloc: the split
+    partials live in the library's fixed per-GPU array, so the call allocates
+    nothing when o and lse are given.  Arguments as for decode."""
+    import torch
+    if k.dim() != 4:
+        raise ValueError("k must be [B, H, N_max, d]")
+    B, H, N_max, d = k.shape
+    _dtype_code(q)
+    tau = 1.0 / math.sqrt(d) if tau is None else float(tau)
+    o = torch.empty_like(q) if o is None else o
+    lse = torch.empty((B, H), dtype=torch.float32, device=q.device) if lse is None else lse
+    _expect(q, "q", (B, H, 1, d), q.dtype)
+    _expect(k, "k", (B, H, N_max, d), q.dtype)
+    _expect(v, "v", (B, H, N_max, d), q.dtype)
+    _expect(o, "o", (B, H, 1, d), q.dtype)
+    _expect(lse, "lse", (B, H), torch.float32)
+    _expect(seqlens_k, "seqlens_k", (B,), torch.int32)
+    _same_gpu([("q", q), ("k", k), ("v", v), ("seqlens_k", seqlens_k), ("o", o), ("lse", lse)])
+    st = lib().fa_decode_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), seqlens_k.data_ptr(),
+                                 B, H, N_max, d, tau, o.data_ptr(), lse.data_ptr(),
+                                 int(num_splits), _dtype_code(q), _stream(q))
+    check("fa_decode_noalloc", st)
     return o, lse
 
 

@@ -34,6 +34,34 @@ int after_launch() {
 
 }  // namespace
 
+namespace fa {
+
+int decode_prepare(const void* q, const void* k, const void* v, const int* seqlens_k, int B, int H,
+                   int N_max, int d, float tau, void* o, float* lse, int num_splits, int dtype,
+                   DecodeArgs* a, size_t* ws_bytes) {
+    if (!q || !k || !v || !seqlens_k || !o || !lse) return FA_ERR_NULL;
+    int st = check_common(B, H, N_max, d, tau, dtype);
+    if (st != FA_OK) return st;
+    if (num_splits < 0 || num_splits > 1024) return FA_ERR_ARG;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse) ||
+        !aligned4(seqlens_k))
+        return FA_ERR_ALIGN;
+    const int S = decode_splits(B, H, N_max, d, num_splits);
+    if (!grid_ok((long long)S * B * H, 256)) return FA_ERR_SHAPE;
+    *a = DecodeArgs{q, k, v, seqlens_k, B, H, N_max, d, tau, o, lse, S,
+                    decode_chunk(N_max, S), nullptr, nullptr, dtype};
+    *ws_bytes = decode_ws_bytes(B, H, d, S);
+    return FA_OK;
+}
+
+void decode_set_workspace(DecodeArgs* a, void* ws) {
+    float* w = static_cast<float*>(ws);
+    a->ws_o = w;
+    a->ws_lse = w + (size_t)a->num_splits * a->B * a->H * a->d;
+}
+
+}  // namespace fa
+
 extern "C" {
 
 int fa_fwd(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H, int N,
@@ -154,22 +182,14 @@ size_t fa_decode_workspace_bytes(int B, int H, int N_max, int d, int num_splits)
 int fa_decode(const void* q, const void* k, const void* v, const int* seqlens_k, int B, int H,
               int N_max, int d, float tau, void* o, float* lse, int num_splits, void* workspace,
               size_t workspace_bytes, int dtype, void* stream) {
-    if (!q || !k || !v || !seqlens_k || !o || !lse) return FA_ERR_NULL;
-    int st = check_common(B, H, N_max, d, tau, dtype);
+    fa::DecodeArgs a;
+    size_t need = 0;
+    int st = fa::decode_prepare(q, k, v, seqlens_k, B, H, N_max, d, tau, o, lse, num_splits, dtype,
+                                &a, &need);
     if (st != FA_OK) return st;
-    if (num_splits < 0 || num_splits > 1024) return FA_ERR_ARG;
-    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned4(lse) ||
-        !aligned4(seqlens_k))
-        return FA_ERR_ALIGN;
-    const int S = fa::decode_splits(B, H, N_max, d, num_splits);
-    const size_t need = fa::decode_ws_bytes(B, H, d, S);
     if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
     if (!aligned16(workspace)) return FA_ERR_ALIGN;
-    if (!grid_ok((long long)S * B * H, 256)) return FA_ERR_SHAPE;
-    float* ws = (float*)workspace;
-    const size_t n_o = (size_t)S * B * H * d;
-    fa::DecodeArgs a{q, k, v, seqlens_k, B, H, N_max, d, tau, o, lse, S,
-                     fa::decode_chunk(N_max, S), ws, ws + n_o, dtype};
+    fa::decode_set_workspace(&a, workspace);
     (void)hipGetLastError();
     fa::launch_decode(a, (hipStream_t)stream);
     return after_launch();
@@ -330,6 +350,9 @@ const char* fa_status_string(int status) {
         case FA_ERR_WORKSPACE: return "workspace missing or too small";
         case FA_ERR_HIP: return "HIP launch error";
         case FA_ERR_ALIGN: return "a pointer is not aligned (16 bytes for tensors)";
+        case FA_ERR_SCRATCH:
+            return "the call needs more than the fixed scratch of fa_decode_noalloc "
+                   "(FA_DECODE_NOALLOC_SCRATCH_BYTES)";
         case FA_ERR_ARG:
             return "bad argument value (tau finite and > 0, num_splits 0..1024, window >= 1, "
                    "sinks >= 0, stage 0..1, dropout probability in [0, 255/256], block sizes "

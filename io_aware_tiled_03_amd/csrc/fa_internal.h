@@ -49,6 +49,15 @@ struct DecodeArgs {
     int dtype;
 };
 void launch_decode(const DecodeArgs& a, hipStream_t st);
+// Host checks of a decode call (every argument except the workspace, in the
+// order fa_decode documents); on FA_OK fills *a without workspace pointers and
+// *ws_bytes with the workspace the call needs.  Touches no device memory.
+int decode_prepare(const void* q, const void* k, const void* v, const int* seqlens_k, int B, int H,
+                   int N_max, int d, float tau, void* o, float* lse, int num_splits, int dtype,
+                   DecodeArgs* a, size_t* ws_bytes);
+// Points the partial outputs and partial LSEs of *a into a workspace of at
+// least decode_ws_bytes bytes: [S, B, H, d] floats, then [S, B, H] floats.
+void decode_set_workspace(DecodeArgs* a, void* ws);
 int decode_splits(int B, int H, int N_max, int d, int requested);
 int decode_chunk(int N_max, int splits);
 size_t decode_ws_bytes(int B, int H, int d, int splits);

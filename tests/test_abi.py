@@ -36,7 +36,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     fa, lib = _lib()
-    for code in range(8):
+    for code in range(9):
         assert lib.fa_status_string(code)
     assert lib.fa_status_string(99) == b"unknown status"
 
