@@ -286,6 +286,9 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N);
  * dq, dk, dv       : [B, H, N, d] outputs, dtype `dtype`.
  * workspace        : >= fa_bwd_workspace_bytes(B, H, N) bytes; on return it
  *                    holds D as float [B, H, N].
+ * dtype            : FA_BF16 (bf16 MFMA products, fp32 accumulation) or FA_F32
+ *                    (float vector arithmetic throughout, for tight checks;
+ *                    not a performance path).
  */
 int fa_bwd(const void* q, const void* k, const void* v, const void* o, const float* lse,
            const void* dout, void* dq, void* dk, void* dv,
@@ -310,7 +313,7 @@ int fa_bwd_window(const void* q, const void* k, const void* v, const void* o, co
  * (p_drop, seed, offset); with Z = keep / (1 - p): dV = (P o Z)^T dO,
  * dS = P o (Z o dP - D) and D_i = dO_i . O_i as before.  o and lse must come
  * from fa_fwd_dropout with the same arguments.  Arguments as fa_bwd plus the
- * dropout state (bf16 only).
+ * dropout state.
  */
 int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, const float* lse,
                    const void* dout, void* dq, void* dk, void* dv,

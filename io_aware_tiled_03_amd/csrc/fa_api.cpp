@@ -269,7 +269,7 @@ int bwd_common(int stages, const void* q, const void* k, const void* v, const vo
     int st = check_common(B, H, N, d, tau, dtype);
     if (st != FA_OK) return st;
     if (causal != 0 && causal != 1) return FA_ERR_UNSUPPORTED;
-    if (dtype != FA_BF16) return FA_ERR_UNSUPPORTED;
+    if (bs && dtype != FA_BF16) return FA_ERR_UNSUPPORTED;   // block-sparse: bf16 only
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o) || !aligned16(dout) ||
         !aligned16(dq) || !aligned16(dk) || !aligned16(dv) || !aligned4(lse))
         return FA_ERR_ALIGN;

@@ -50,23 +50,24 @@ template <int N_> using ic = std::integral_constant<int, N_>;
 // instruction fills 1 KB of LDS; every lane loads the 16-byte chunk that
 // belongs at its LDS position (padding positions load a duplicate chunk that
 // is never read).  Rows past N read as zeros through the buffer descriptor.
+// The byte offsets are recomputed at each issue (a few integer operations):
+// held in an array inside the struct, which the kernels' lambdas capture by
+// reference, they were kept in scratch memory in some variants.
 template <int ROWS, int D, int STR, int NWAVES>
 struct TileCopy {
     static constexpr int CPR = STR / 8, NI = ROWS * CPR / 64, PW = (NI + NWAVES - 1) / NWAVES;
     static_assert(ROWS * CPR % 64 == 0, "whole wave instructions");
-    uint32_t off[PW];
-    __device__ void init(int wave, int lane) {
-#pragma unroll
-        for (int t = 0; t < PW; ++t) {
-            const int pos = (wave + NWAVES * t) * 64 + lane, row = pos / CPR, c = pos % CPR;
-            off[t] = (uint32_t)(row * D + (c < D / 8 ? c : 0) * 8) * 2;
-        }
-    }
-    __device__ void issue(rsrc_t rs, int row0, uint16_t* lds, int wave) const {
+    int wave, lane;
+    __device__ void init(int wave_, int lane_) { wave = wave_; lane = lane_; }
+    __device__ void issue(rsrc_t rs, int row0, uint16_t* lds, int) const {
         const uint32_t t0 = (uint32_t)row0 * (D * 2);
 #pragma unroll
         for (int t = 0; t < PW; ++t)
-            if (wave + NWAVES * t < NI) buf_ld16_lds(rs, off[t] + t0, lds + (wave + NWAVES * t) * 512);
+            if (wave + NWAVES * t < NI) {
+                const int pos = (wave + NWAVES * t) * 64 + lane, row = pos / CPR, c = pos % CPR;
+                const uint32_t off = (uint32_t)(row * D + (c < D / 8 ? c : 0) * 8) * 2;
+                buf_ld16_lds(rs, off + t0, lds + (wave + NWAVES * t) * 512);
+            }
     }
 };
 
@@ -617,6 +618,10 @@ void launch_d(const BwdArgs& a, int stages, hipStream_t st) {
 }  // namespace
 
 void launch_bwd(const BwdArgs& a, int stages, hipStream_t st) {
+    if (a.dtype == kF32) {
+        launch_bwd_f32(a, stages, st);
+        return;
+    }
     a.d == 64 ? launch_d<64>(a, stages, st) : launch_d<128>(a, stages, st);
 }
 

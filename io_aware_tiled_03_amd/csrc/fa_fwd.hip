@@ -427,81 +427,16 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
     }
 }
 
-// fp32 path: one wave per 64 query rows, one row per lane, VALU arithmetic in
-// fp32, K/V tiles of 32 rows in LDS (read as broadcasts).
-template <int D, bool CAUSAL>
-__global__ __launch_bounds__(64) void fwd_f32_kernel(
-    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    float* __restrict__ O, float* __restrict__ LSE, int BH, int N, float scale_log2, float tau,
-    int n_qtiles, int window, int sinks, Dropout drop) {
-    constexpr int BR = 64, BC = 32;
-    __shared__ float sK[BC][D];
-    __shared__ float sV[BC][D];
-    const int lane = threadIdx.x;
-    const int qt = n_qtiles - 1 - (int)(blockIdx.x / BH);
-    const int bh = (int)(blockIdx.x % BH);
-    const size_t base = (size_t)bh * N * D;
-    const int q0 = qt * BR, row = q0 + lane;
-
-    float q[D], o[D];
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-        q[d] = row < N ? Q[base + (size_t)row * D + d] : 0.f;
-        o[d] = 0.f;
-    }
-    float m = neg_inf(), l = 0.f;
-    const int kend = CAUSAL ? min(N, q0 + BR) : N;
-    for (int k0 = 0; k0 < kend; k0 += BC) {
-        __syncthreads();
-        for (int idx = lane; idx < BC * D; idx += 64) {
-            const int r = idx / D, d = idx % D, key = k0 + r;
-            sK[r][d] = key < N ? K[base + (size_t)key * D + d] : 0.f;
-            sV[r][d] = key < N ? V[base + (size_t)key * D + d] : 0.f;
-        }
-        __syncthreads();
-        float s[BC];
-        float mx = neg_inf();
-        for (int c = 0; c < BC; ++c) {
-            float acc = 0.f;
-#pragma unroll
-            for (int d = 0; d < D; ++d) acc = __builtin_fmaf(q[d], sK[c][d], acc);
-            const int key = k0 + c;
-            const bool vis = !CAUSAL || (key <= row && (row - key < window || key < sinks));
-            s[c] = (key < N && vis) ? acc : neg_inf();
-            mx = fmaxf(mx, s[c]);
-        }
-        const float mnew = fmaxf(m, mx);
-        // a row with no visible key so far (window) keeps m = -inf, l = 0, o = 0
-        const float alpha = m == mnew ? 1.f : fast_exp2((m - mnew) * scale_log2);
-        const float mc = mnew == neg_inf() ? 0.f : mnew * scale_log2;
-        l *= alpha;
-#pragma unroll
-        for (int d = 0; d < D; ++d) o[d] *= alpha;
-        for (int c = 0; c < BC; ++c) {
-            float p = fast_exp2(__builtin_fmaf(s[c], scale_log2, -mc));
-            l += p;
-            if (drop.thr > 0) {   // dropout after the softmax; l keeps the undropped sum
-                const uint32_t w = Dropout::row_word(drop.block(k0 + c, row, bh), row & 3);
-                p = drop.keep(w, (k0 + c) & 3) ? p : 0.f;
-            }
-#pragma unroll
-            for (int d = 0; d < D; ++d) o[d] = __builtin_fmaf(p, sV[c][d], o[d]);
-        }
-        m = mnew;
-    }
-    if (row < N) {
-        const float inv = (drop.thr > 0 ? drop.scale : 1.f) / l;
-#pragma unroll
-        for (int d = 0; d < D; ++d) O[base + (size_t)row * D + d] = o[d] * inv;
-        LSE[(size_t)bh * N + row] = m * tau + logf(l);
-    }
-}
-
 // Tile shapes measured on MI355X: d=128 runs 128-key tiles in 8-wave (256-row)
 // workgroups, one per CU (143 KB of LDS); d=64 runs 64-key tiles in 4-wave
 // workgroups, several per CU.
-template <int D> struct FwdShape { static constexpr int BC = 64, NW = 4; };
-template <> struct FwdShape<128> { static constexpr int BC = 128, NW = 8; };
+// The d=128 variants with dropout or a block mask carry more live registers
+// (generator words, block bits) and take 64-key tiles, which halves the
+// per-tile scores and probabilities and keeps them out of scratch.
+template <int D, int MODE, bool DROP> struct FwdShape { static constexpr int BC = 64, NW = 4; };
+template <int MODE, bool DROP> struct FwdShape<128, MODE, DROP> {
+    static constexpr int BC = (DROP || MODE >= kMaskBlock) ? 64 : 128, NW = 8;
+};
 
 Dropout make_dropout(int thr, unsigned long long seed, unsigned int offset) {
     Dropout d;
@@ -515,23 +450,13 @@ Dropout make_dropout(int thr, unsigned long long seed, unsigned int offset) {
 
 template <int D, int MODE, bool DROP>
 void launch_bf16(const FwdArgs& a, hipStream_t st) {
-    constexpr int BC = FwdShape<D>::BC, NW = FwdShape<D>::NW;
+    constexpr int BC = FwdShape<D, MODE, DROP>::BC, NW = FwdShape<D, MODE, DROP>::NW;
     const int bh = a.B * a.H;
     const int nq = (a.N + 32 * NW - 1) / (32 * NW);
     hipLaunchKernelGGL((fwd_bf16_kernel<D, MODE, BC, NW, DROP>), dim3(nq * bh), dim3(64 * NW), 0,
                        st, (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                        (uint16_t*)a.o, a.lse, bh, a.N, a.tau * kLog2e, a.tau, nq, a.window,
                        a.sinks, make_dropout(a.drop_thr, a.seed, a.offset), a.blk);
-}
-
-template <int D, bool C>
-void launch_f32(const FwdArgs& a, hipStream_t st) {
-    const int nq = (a.N + 63) / 64;
-    const int bh = a.B * a.H;
-    hipLaunchKernelGGL((fwd_f32_kernel<D, C>), dim3(nq * bh), dim3(64), 0, st, (const float*)a.q,
-                       (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse, bh, a.N,
-                       a.tau * kLog2e, a.tau, nq, a.window, a.sinks,
-                       make_dropout(a.drop_thr, a.seed, a.offset));
 }
 
 template <int D>
@@ -559,8 +484,7 @@ void launch_fwd(const FwdArgs& a, hipStream_t st) {
     if (a.dtype == kBF16) {
         a.d == 64 ? launch_bf16_d<64>(a, st) : launch_bf16_d<128>(a, st);
     } else {
-        if (a.d == 64) a.causal ? launch_f32<64, true>(a, st) : launch_f32<64, false>(a, st);
-        else a.causal ? launch_f32<128, true>(a, st) : launch_f32<128, false>(a, st);
+        launch_fwd_f32(a, st);
     }
 }
 

@@ -34,6 +34,7 @@ struct FwdArgs {
     BlockSparse blk;           // block-sparse when blk.mask != nullptr
 };
 void launch_fwd(const FwdArgs& a, hipStream_t st);
+void launch_fwd_f32(const FwdArgs& a, hipStream_t st);   // dtype kF32 (no block mask)
 
 struct DecodeArgs {
     const void *q, *k, *v;
@@ -97,5 +98,6 @@ struct BwdArgs {
 };
 // stages: bit 0 = D preprocess, bit 1 = dK/dV, bit 2 = dQ (launched in that order)
 void launch_bwd(const BwdArgs& a, int stages, hipStream_t st);
+void launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t st);   // dtype kF32 (no block mask)
 
 }  // namespace fa

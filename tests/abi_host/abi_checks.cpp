@@ -149,6 +149,10 @@ void check_block_sparse() {
     CHECK(fa_bwd_block_sparse(P, P, P, P, L, P, P, P, P, 2, 3, 1000, 64, 0.125f, 0, M, 1, 32, 1024,
                               P, 2 * 3 * 1000 * 4, FA_BF16, nullptr) == FA_OK);
     CHECK(n_bwd == n0 + 1 && last_bwd.blk.nbq == 32 && last_bwd.blk.nbk == 1);
+    expect_reject(FA_ERR_UNSUPPORTED, [&] {
+        return fa_bwd_block_sparse(P, P, P, P, L, P, P, P, P, 2, 3, 1000, 64, 0.125f, 0, M, 1, 32, 1024,
+                                   P, 2 * 3 * 1000 * 4, FA_F32, nullptr);
+    });
 }
 
 void check_decode() {
@@ -238,6 +242,7 @@ void check_bwd() {
     expect_reject(FA_ERR_WORKSPACE, [&] { return bwd(1, ws - 1, FA_BF16); });
     expect_reject(FA_ERR_UNSUPPORTED, [&] { return bwd(2, ws, FA_BF16); });
     expect_reject(FA_ERR_UNSUPPORTED, [&] { return bwd(1, ws, 9); });
+    CHECK(bwd(0, ws, FA_F32) == FA_OK && last_bwd.dtype == FA_F32);
     CHECK(bwd(1, ws, FA_BF16) == FA_OK);
     CHECK(last_stages == 3 && last_bwd.D == static_cast<float*>(P) && last_bwd.causal == 1);
     for (int stage : {0, 1}) {

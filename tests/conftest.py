@@ -27,3 +27,36 @@ def pytest_collection_modifyitems(config, items):
     for item in items:
         if "gpu" in item.keywords:
             item.add_marker(skip)
+
+
+def pytest_sessionfinish(session, exitstatus):
+    """Writes the per-workload error table (max and mean |GPU - oracle| of
+    each output over everything compared) to the file FA_PARITY_LOG names."""
+    path = os.environ.get("FA_PARITY_LOG")
+    if not path:
+        return
+    import json
+    from tests.util import RECORDS
+    table = {}
+    for r in RECORDS:
+        e = table.setdefault((r["config"], r["output"]), {"max_abs": 0.0, "sum_abs": 0.0, "n": 0})
+        e["max_abs"] = max(e["max_abs"], r["max_abs"])
+        e["sum_abs"] += r["sum_abs"]
+        e["n"] += r["n"]
+    rows = [{"config": c, "output": o, "max_abs": e["max_abs"], "mean_abs": e["sum_abs"] / e["n"],
+             "elements": e["n"]} for (c, o), e in sorted(table.items())]
+    os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+    with open(path, "w") as f:
+        json.dump({"exitstatus": int(exitstatus), "rows": rows}, f, indent=1)
+    with open(os.path.splitext(path)[0] + ".md", "w") as f:
+        f.write(error_table_markdown(rows, int(exitstatus)))
+
+
+def error_table_markdown(rows, exitstatus):
+    """The error table as Markdown (one row per workload and output)."""
+    out = ["| workload | output | elements compared | max abs err | mean abs err |",
+           "|---|---|---|---|---|"]
+    for r in rows:
+        out.append("| %s | %s | %d | %.3g | %.3g |" % (r["config"], r["output"], r["elements"],
+                                                       r["max_abs"], r["mean_abs"]))
+    return "\n".join(out) + "\n\n(pytest exit status %d)\n" % exitstatus

@@ -100,8 +100,8 @@ def test_dropout_rejects_bad_arguments():
     b = [P, P, P, P, P, P, P, P, P, 1, 2, 64, 64, 0.125, 1, 0.1, 5, 0, P, 1 << 20, 1, None]
     bad = list(b); bad[15] = 1.0
     assert lib.fa_bwd_dropout(*bad) == 7
-    bad = list(b); bad[20] = 0
-    assert lib.fa_bwd_dropout(*bad) == 3
+    bad = list(b); bad[20] = 9
+    assert lib.fa_bwd_dropout(*bad) == 3    # unknown dtype
     bad = list(b); bad[18] = None
     assert lib.fa_bwd_dropout(*bad) == 4
 
@@ -227,7 +227,7 @@ def test_bwd_rejects_bad_arguments():
     assert _bwd(lib, dv=None) == 1
     assert _bwd(lib, N=0) == 2
     assert _bwd(lib, d=80) == 3
-    assert _bwd(lib, dtype=0) == 3
+    assert _bwd(lib, dtype=9) == 3
     assert _bwd(lib, ws=None) == 4
     assert _bwd(lib, wsb=1 * 2 * 64 * 4 - 1) == 4
     assert _bwd(lib, dq=P + 2) == 6
@@ -242,8 +242,8 @@ def test_bwd_window_rejects_bad_arguments():
     assert lib.fa_bwd_window(*bad) == 7
     bad = list(args); bad[15] = -2
     assert lib.fa_bwd_window(*bad) == 7
-    bad = list(args); bad[18] = 0
-    assert lib.fa_bwd_window(*bad) == 3    # bf16 only
+    bad = list(args); bad[18] = 9
+    assert lib.fa_bwd_window(*bad) == 3    # unknown dtype
     bad = list(args); bad[16] = None
     assert lib.fa_bwd_window(*bad) == 4
 

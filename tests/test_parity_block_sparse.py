@@ -102,7 +102,8 @@ def test_block_sparse_long_prefill_bigbird_pattern():
     for h in (0, 11, 25, 31):
         ro, rl = orc.attention_fwd_head(qf[0, h], kf[0, h], vf[0, h], w.tau, True, rows=rows,
                                         block=(mask[0], 128, 128))
-        assert_close(o[0, h, rows], ro, "bf16", "O[h=%d]" % h)
+        assert_close(o[0, h, rows], ro, "bf16", "O[h=%d]" % h,
+                     tag=("next 4: block-sparse band+global, 1x32x16384x128 (sampled rows)", "O"))
         _lse_close(lse[0, h, rows], rl, "LSE[h=%d]" % h)
 
 
@@ -156,4 +157,6 @@ def test_block_sparse_bwd_workload_shape():
         ref = orc.attention_bwd_head(qf[b, h], kf[b, h], vf[b, h], dof[b, h], w.tau, True,
                                      block=(mask[h], 128, 128))
         for name in ("dq", "dk", "dv"):
-            assert_close(g[name][b, h], ref[name], "bf16", "%s[%d,%d]" % (name, b, h))
+            assert_close(g[name][b, h], ref[name], "bf16", "%s[%d,%d]" % (name, b, h),
+                         tag=("next 4: block-sparse 50% of 128x128 blocks, backward 4x16x4096x64 "
+                              "(2 heads)", name))

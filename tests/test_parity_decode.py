@@ -60,8 +60,9 @@ def test_decode_workload_full():
         vb = fa_inputs.bf16_bits_to_f64(x["v"].raw[b:b + 1, :, :L])
         ob, lb = orc.decode_fwd(qf[b:b + 1], kb, vb, np.array([L]), w.tau)
         ro[b], rl[b] = ob[0], lb[0]
-    assert_close(o, ro, "bf16", "O")
-    assert_close(lse, rl, "bf16", "LSE", kind="lse")
+    tag = "4: split-KV decode 64x32, L~U[1024,8192], d=128"
+    assert_close(o, ro, "bf16", "O", tag=(tag, "O"))
+    assert_close(lse, rl, "bf16", "LSE", kind="lse", tag=(tag, "LSE"))
 
 
 def test_decode_one_split_matches_merge_bits():

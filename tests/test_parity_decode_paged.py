@@ -102,5 +102,6 @@ def test_paged_workload_full():
     x = fa_inputs.paged_workload_inputs(w)
     o, lse = _run(x, w.tau)
     ro, rl = _oracle(x, w.tau)
-    assert_close(o, ro, "bf16", "O")
-    assert_close(lse, rl, "bf16", "LSE", kind="lse")
+    tag = "next 1: paged GQA decode 64 seq, 32/8 heads, 16-token pages"
+    assert_close(o, ro, "bf16", "O", tag=(tag, "O"))
+    assert_close(lse, rl, "bf16", "LSE", kind="lse", tag=(tag, "LSE"))

@@ -161,6 +161,7 @@ def test_dropout_workload_shape():
         hd = orc.head_dropout((drop[1], drop[2], drop[0]), b * w.H + h)
         ref = orc.attention_bwd_head(qf[b, h], kf[b, h], vf[b, h], dof[b, h], w.tau, True,
                                      drop=hd)
-        assert_close(o[b, h], ref["o"], "bf16", "O[%d,%d]" % (b, h))
+        tag = "next 3: dropout p=0.1, causal 4x16x4096x64 (2 heads)"
+        assert_close(o[b, h], ref["o"], "bf16", "O[%d,%d]" % (b, h), tag=(tag, "O"))
         for name, got in (("dq", dq), ("dk", dk), ("dv", dv)):
-            assert_close(got[b, h], ref[name], "bf16", "%s[%d,%d]" % (name, b, h))
+            assert_close(got[b, h], ref[name], "bf16", "%s[%d,%d]" % (name, b, h), tag=(tag, name))

@@ -47,37 +47,46 @@ def test_fwd_tiny_fp32_workload():
     w = fa_inputs.WORKLOADS[1]
     x, tau, o, lse = _run(w.B, w.H, w.N, w.d, w.dtype, False, w.seed, tau=w.tau)
     ro, rl = orc.attention_fwd(*(x[n].f64() for n in ("q", "k", "v")), w.tau, False)
-    assert_close(o, ro, "f32", "O")
-    assert_close(lse, rl, "f32", "LSE", kind="lse")
+    tag = "1: tiny fp32 forward 1x1x256x64"
+    assert_close(o, ro, "f32", "O", tag=(tag, "O"))
+    assert_close(lse, rl, "f32", "LSE", kind="lse", tag=(tag, "LSE"))
 
 
 @pytest.mark.parametrize("causal", [False, True])
 def test_fwd_gpt2_medium_workload(causal):
-    """Workload 2 at full size (8x16x1024x64 bf16): every row of 6 sampled heads."""
+    """Workload 2 at full size (8x16x1024x64 bf16): every row of every head."""
     w = fa_inputs.WORKLOADS[2]
     x, tau, o, lse = _run(w.B, w.H, w.N, w.d, w.dtype, causal, w.seed, tau=w.tau)
-    qf, kf, vf = (x[n].f64() for n in ("q", "k", "v"))
-    for b, h in ((0, 0), (1, 5), (3, 15), (5, 8), (7, 0), (7, 15)):
-        ro, rl = orc.attention_fwd_head(qf[b, h], kf[b, h], vf[b, h], w.tau, causal)
-        assert_close(o[b, h], ro, "bf16", "O[%d,%d]" % (b, h))
-        assert_close(lse[b, h], rl, "bf16", "LSE[%d,%d]" % (b, h), kind="lse")
-    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    ro, rl = orc.attention_fwd(*(x[n].f64() for n in ("q", "k", "v")), w.tau, causal)
+    tag = "2: GPT-2-medium-shaped forward 8x16x1024x64, %s" % ("causal" if causal else "non-causal")
+    assert_close(o, ro, "bf16", "O", tag=(tag, "O"))
+    assert_close(lse, rl, "bf16", "LSE", kind="lse", tag=(tag, "LSE"))
+
+
+def _long_rows(seed):
+    """Rows of one head of the long prefill: both edges of every 128-row block
+    (the key tile; query tiles are 256 rows, waves 32) and 256 more drawn
+    uniformly: 512 rows."""
+    edges = np.concatenate([np.arange(0, 16384, 128), np.arange(127, 16384, 128)])
+    rng = np.random.Generator(np.random.PCG64(seed))
+    rest = np.setdiff1d(np.arange(16384), edges)
+    return np.sort(np.concatenate([edges, rng.choice(rest, 256, replace=False)]))
 
 
 def test_fwd_long_causal_workload():
-    """Workload 3 at full size (1x32x16384x128 bf16, causal): sampled rows of 4 heads,
-    including the first rows, tile edges and the last rows."""
+    """Workload 3 at full size (1x32x16384x128 bf16, causal): all 32 heads, every
+    row of heads 0 and 31 and 512 rows (every tile edge included) of the others."""
     w = fa_inputs.WORKLOADS[3]
     x, tau, o, lse = _run(w.B, w.H, w.N, w.d, w.dtype, True, w.seed, tau=w.tau)
-    qf, kf, vf = (x[n].f64() for n in ("q", "k", "v"))
-    rng = np.random.Generator(np.random.PCG64(33))
-    rows = np.unique(np.concatenate([[0, 1, 63, 64, 127, 128, 8191, 8192, 16255, 16256, 16383],
-                                     rng.integers(0, w.N, 120)]))
-    for h in (0, 9, 22, 31):
-        ro, rl = orc.attention_fwd_head(qf[0, h], kf[0, h], vf[0, h], w.tau, True, rows=rows)
-        assert_close(o[0, h, rows], ro, "bf16", "O[h=%d]" % h)
-        assert_close(lse[0, h, rows], rl, "bf16", "LSE[h=%d]" % h, kind="lse")
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+    qf, kf, vf = (x[n].f64() for n in ("q", "k", "v"))
+    tag = "3: long causal prefill 1x32x16384x128"
+    for h in range(w.H):
+        rows = None if h in (0, 31) else _long_rows(3300 + h)
+        ro, rl = orc.attention_fwd_head(qf[0, h], kf[0, h], vf[0, h], w.tau, True, rows=rows)
+        sel = slice(None) if rows is None else rows
+        assert_close(o[0, h, sel], ro, "bf16", "O[h=%d]" % h, tag=(tag, "O"))
+        assert_close(lse[0, h, sel], rl, "bf16", "LSE[h=%d]" % h, kind="lse", tag=(tag, "LSE"))
 
 
 def test_fwd_ones_value_gives_ones():

@@ -73,8 +73,9 @@ def test_window_long_prefill(w, s):
     for h in (0, 7, 20, 31):
         ro, rl = orc.attention_fwd_head(qf[0, h], kf[0, h], vf[0, h], wl.tau, True, rows=rows,
                                         window=w, sinks=s)
-        assert_close(o[0, h, rows], ro, "bf16", "O[h=%d]" % h)
-        assert_close(lse[0, h, rows], rl, "bf16", "LSE[h=%d]" % h, kind="lse")
+        tag = "next 2: window %d + %d sinks, 1x32x16384x128 (sampled rows)" % (w, s)
+        assert_close(o[0, h, rows], ro, "bf16", "O[h=%d]" % h, tag=(tag, "O"))
+        assert_close(lse[0, h, rows], rl, "bf16", "LSE[h=%d]" % h, kind="lse", tag=(tag, "LSE"))
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
 
 
@@ -135,4 +136,5 @@ def test_window_bwd_workload():
         ref = orc.attention_bwd_head(qf[b, h], kf[b, h], vf[b, h], dof[b, h], wl.tau, True,
                                      window=1024, sinks=4)
         for name in ("dq", "dk", "dv"):
-            assert_close(g[name][b, h], ref[name], "bf16", "%s[%d,%d]" % (name, b, h))
+            assert_close(g[name][b, h], ref[name], "bf16", "%s[%d,%d]" % (name, b, h),
+                         tag=("next 2: window 1024 + 4 sinks backward 4x16x4096x64 (3 heads)", name))

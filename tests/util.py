@@ -35,7 +35,21 @@ def bf16_ulp(x):
     return np.exp2(np.floor(np.log2(ax)) - 7)
 
 
-def assert_close(got, ref, dtype, what, kind="out", ulp_allow=False, extra=None):
+# Max and mean |GPU - oracle| of the outputs compared at each workload's full
+# size, collected over the test session; conftest writes them out when
+# FA_PARITY_LOG names a file.
+RECORDS = []
+
+
+def record(config, output, got, ref):
+    """Keeps the error of one compared output for the session's error table."""
+    d = np.abs(np.asarray(got, dtype=np.float64) - np.asarray(ref, dtype=np.float64))
+    if d.size:
+        RECORDS.append({"config": config, "output": output, "max_abs": float(d.max()),
+                        "sum_abs": float(d.sum()), "n": int(d.size)})
+
+
+def assert_close(got, ref, dtype, what, kind="out", ulp_allow=False, extra=None, tag=None):
     """|got - ref| within TOL.  ulp_allow (bf16 outputs only) adds one bf16 unit
     of the reference value to the max bound per element: an output stored in
     bf16 can be off by that much through its own rounding, which exceeds the
@@ -46,6 +60,8 @@ def assert_close(got, ref, dtype, what, kind="out", ulp_allow=False, extra=None)
     ref = np.asarray(ref, dtype=np.float64)
     assert got.shape == ref.shape, (what, got.shape, ref.shape)
     assert np.all(np.isfinite(got)), "%s: non-finite values" % what
+    if tag is not None:
+        record(tag[0], tag[1], got, ref)
     mx, mean = err_stats(got, ref)
     tol = TOL[dtype]
     if kind == "lse":
