@@ -334,23 +334,27 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     phase(max(0, pm1), pu, ic<0>{});
     phase(max(0, pu), npos, ic<1>{});
 
-    if (key < N) {
-        uint16_t* dkr = dK + base + (size_t)key * D;
-        uint16_t* dvr = dV + base + (size_t)key * D;
+    // Epilogue through LDS (stage_piece / store_rows); the staging buffers are
+    // free: every tile ended with a barrier and no copy is in flight.
+    {
+        constexpr int WPB = BR / 32;   // waves' row blocks per staging buffer
+        uint16_t* const kr = (wave < WPB ? sQ0 : sQ1) + (wave % WPB) * 32 * STR;
+        uint16_t* const vr = (wave < WPB ? sdO0 : sdO1) + (wave % WPB) * 32 * STR;
+        const float vs = DROP ? drop.scale : 1.f;   // Z's scale, factored out of dV
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
                 const int d = db * 32 + 8 * g + 4 * hf;
-                u32x2 wk, wv;
-                wk[0] = pack_bf16x2(dkacc[db][4 * g] * tau, dkacc[db][4 * g + 1] * tau);
-                wk[1] = pack_bf16x2(dkacc[db][4 * g + 2] * tau, dkacc[db][4 * g + 3] * tau);
-                const float vs = DROP ? drop.scale : 1.f;   // Z's scale, factored out of dV
-                wv[0] = pack_bf16x2(dvacc[db][4 * g] * vs, dvacc[db][4 * g + 1] * vs);
-                wv[1] = pack_bf16x2(dvacc[db][4 * g + 2] * vs, dvacc[db][4 * g + 3] * vs);
-                *reinterpret_cast<u32x2*>(dkr + d) = wk;
-                *reinterpret_cast<u32x2*>(dvr + d) = wv;
+                const f32x16& ka = dkacc[db];
+                const f32x16& va = dvacc[db];
+                stage_piece(kr, STR, ln, d, ka[4 * g] * tau, ka[4 * g + 1] * tau, ka[4 * g + 2] * tau,
+                            ka[4 * g + 3] * tau);
+                stage_piece(vr, STR, ln, d, va[4 * g] * vs, va[4 * g + 1] * vs, va[4 * g + 2] * vs,
+                            va[4 * g + 3] * vs);
             }
+        store_rows<D>(kr, STR, dK + base + (size_t)kw * D, N - kw, lane);
+        store_rows<D>(vr, STR, dV + base + (size_t)kw * D, N - kw, lane);
     }
 }
 
@@ -575,18 +579,19 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     phase(p1, p2, ic<0>{});
     phase(p2, p3, ic<1>{});
 
-    if (qrow < N) {
-        uint16_t* dqr = dQ + base + (size_t)qrow * D;
+    // Epilogue through LDS (stage_piece / store_rows); the K staging buffers
+    // are free: every tile ended with a barrier and no copy is in flight.
+    {
+        uint16_t* const tile = (wave < BC / 32 ? sK0 : sK1) + (wave % (BC / 32)) * 32 * STR;
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int d = db * 32 + 8 * g + 4 * hf;
-                u32x2 w;
-                w[0] = pack_bf16x2(dqacc[db][4 * g] * tau, dqacc[db][4 * g + 1] * tau);
-                w[1] = pack_bf16x2(dqacc[db][4 * g + 2] * tau, dqacc[db][4 * g + 3] * tau);
-                *reinterpret_cast<u32x2*>(dqr + d) = w;
+                const f32x16& a = dqacc[db];
+                stage_piece(tile, STR, ln, db * 32 + 8 * g + 4 * hf, a[4 * g] * tau, a[4 * g + 1] * tau,
+                            a[4 * g + 2] * tau, a[4 * g + 3] * tau);
             }
+        store_rows<D>(tile, STR, dQ + base + (size_t)qw * D, N - qw, lane);
     }
 }
 

@@ -270,4 +270,41 @@ __device__ __forceinline__ void buf_ld16_lds(rsrc_t r, uint32_t byte_off, void* 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 __device__ __forceinline__ void st16(void* p, const u32x4& v) { *reinterpret_cast<u32x4*>(p) = v; }
 
+// Epilogue stores through LDS.  The accumulators of the O^T-shaped products
+// leave each lane 16 head-dim entries per 32-wide block of one row, so direct
+// stores write 8-byte pieces of 32 different rows per instruction.  A wave
+// instead writes its 32 rows, packed to bf16, into a wave-private LDS tile
+// (stage_piece), then stores whole rows, 16 bytes per lane (store_rows).  A
+// wave reads back only what it wrote, and one wave's LDS operations complete
+// in order, so no barrier is needed between the two.
+//
+// stage_piece: row `row` (this lane's), head-dim entries d .. d+3.  The write
+// is an asm ds_write_b64 (a store: no register result; the memory clobber
+// orders it before the reads in store_rows).  As an ordinary C++ store into
+// the staging buffers, which the main loops fill only with direct-to-LDS
+// copies, it changed how the compiler treats the loops' LDS reads and pushed
+// the 128-key-tile forward from 224 VGPRs to 256 plus spills.
+__device__ __forceinline__ void stage_piece(uint16_t* tile, int stride, int row, int d, float a,
+                                            float b, float c, float e) {
+    u32x2 w;
+    w[0] = pack_bf16x2(a, b);
+    w[1] = pack_bf16x2(c, e);
+    // the low 32 bits of a generic LDS address are the LDS byte address
+    const uint32_t p = (uint32_t)(uintptr_t)(tile + row * stride + d);
+    asm volatile("ds_write_b64 %0, %1" ::"v"(p), "v"(w) : "memory");
+}
+// store_rows: rows 0 .. nrows-1 (at most 32) of the tile to dst (row-major, D
+// entries per row).
+template <int D>
+__device__ __forceinline__ void store_rows(const uint16_t* tile, int stride, uint16_t* dst, int nrows,
+                                           int lane) {
+    constexpr int CPR = D / 8;   // 16-byte pieces per row
+#pragma unroll
+    for (int t = 0; t < 32 * CPR / 64; ++t) {
+        const int pos = t * 64 + lane, row = pos / CPR, c = (pos % CPR) * 8;
+        const u32x4 v = ld16(tile + row * stride + c);
+        if (row < nrows) st16(dst + (size_t)row * D + c, v);
+    }
+}
+
 }  // namespace fa

@@ -410,20 +410,36 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
     l += xor32(l);
     // a row that saw no key (block-sparse) keeps the empty sum: O = 0, LSE = -inf
     const float inv = (BLK && l == 0.f) ? 0.f : (DROP ? drop.scale : 1.f) / l;
-    if (qrow < N) {
-        uint16_t* orow = O + base + (size_t)qrow * D;
+    if (qrow < N && hf == 0)
+        LSE[(size_t)bh * N + qrow] = (BLK && l == 0.f) ? neg_inf() : m * tau + __logf(l);
+    // O through LDS (stage_piece / store_rows): the staging buffers are free
+    // (every tile ended with a wait for its copies and a barrier).  Wave w
+    // takes 32-row block w of the K buffers, then of the V buffers.
+    {
+        constexpr int RB = BC / 32;   // 32-row blocks per staging buffer
+        static_assert(NW <= 4 * RB, "the staging buffers hold every wave's rows");
+        uint16_t* tile;
+        int stride = KSTR;
+        if constexpr (NW <= 2 * RB) {
+            tile = (wave < RB ? sK0 : sK1) + (wave % RB) * 32 * KSTR;
+        } else {
+            const int blk = wave % RB, buf = wave / RB;
+            if (buf < 2) {
+                tile = (buf == 0 ? sK0 : sK1) + blk * 32 * KSTR;
+            } else {
+                tile = (buf == 2 ? sV0 : sV1) + blk * 32 * VSTR;
+                stride = VSTR;
+            }
+        }
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
             for (int g = 0; g < 4; ++g) {
-                const int d = db * 32 + 8 * g + 4 * hf;
-                u32x2 w;
-                w[0] = pack_bf16x2(oacc[db][4 * g] * inv, oacc[db][4 * g + 1] * inv);
-                w[1] = pack_bf16x2(oacc[db][4 * g + 2] * inv, oacc[db][4 * g + 3] * inv);
-                *reinterpret_cast<u32x2*>(orow + d) = w;
+                const f32x16& a = oacc[db];
+                stage_piece(tile, stride, ln, db * 32 + 8 * g + 4 * hf, a[4 * g] * inv,
+                            a[4 * g + 1] * inv, a[4 * g + 2] * inv, a[4 * g + 3] * inv);
             }
-        if (hf == 0)
-            LSE[(size_t)bh * N + qrow] = (BLK && l == 0.f) ? neg_inf() : m * tau + __logf(l);
+        store_rows<D>(tile, stride, O + base + (size_t)qw * D, N - qw, lane);
     }
 }
 
