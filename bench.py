@@ -25,7 +25,8 @@ The JSON line also carries, from the same run:
     non-causal, fwd causal, bwd causal, decode), the tiny fp32 forward, the
     split-KV decode, the paged grouped-head decode, the 4k causal backward,
     the prefill as a sliding-window and as a block-sparse layer, and dropout,
-    each against its roofline;
+    each against its roofline (the decodes alternate between two copies of
+    their caches, so that no call is served from the caches by the previous);
   * "cpu_baseline" (skip: --no-cpu): the float64 oracle on the host over two
     whole heads of the headline workload, with the GPU output of those heads
     compared against it, plus the oracle's wall time on the other workloads.
@@ -35,6 +36,7 @@ from __future__ import annotations
 import argparse
 import glob
 import hashlib
+import itertools
 import json
 import math
 import os
@@ -240,6 +242,11 @@ def sample_clock(run, seconds=0.5):
             "source": "pp_dpm_sclk active level while the headline kernel runs back to back"}
 
 
+def alternating(items):
+    """An endless iterator over items in turn."""
+    return itertools.cycle(items)
+
+
 def time_events(fn, reps, warmup=10):
     """Per-call HIP event times (ms) on the current stream, after warm-up calls."""
     import torch
@@ -404,15 +411,18 @@ def bench_extra(fa, reps=50):
     o = torch.empty_like(q)
     lse = torch.empty(B, H, device=dev)
     ws = torch.empty(fa.decode_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
-    ms = med(lambda: fa.decode(q, k, v, sl, w.tau, 0, o, lse, ws), 2 * reps)
+    # successive calls alternate between the cache and a copy of it at other
+    # addresses, so no call finds the previous call's rows in the caches
+    kv = alternating([(k, v), (k.clone(), v.clone())])
+    ms = med(lambda: fa.decode(q, *next(kv), sl, w.tau, 0, o, lse, ws), 2 * reps)
     if not bool(torch.isfinite(o.float()).all()):
         raise RuntimeError("decode produced non-finite output")
     nbytes = float(seqlens.astype("int64").sum()) * H * d * 2 * 2 + 2 * B * H * d * 2 + B * H * 4
     out["decode_splitkv"] = {"shape": [B, H, N, d], "seqlens_sum": int(seqlens.sum()),
                              "num_splits": fa.decode_num_splits(B, H, N, d),
-                             "ms": ms, "GB/s": round(nbytes / ms / 1e6, 1),
+                             "input_copies": 2, "ms": ms, "GB/s": round(nbytes / ms / 1e6, 1),
                              "frac_hbm": round(nbytes / ms / 1e-3 / PEAK_HBM, 4)}
-    del q, k, v, o, lse, ws
+    del q, k, v, o, lse, ws, kv
 
     # paged decode with grouped KV heads: B=64, Hq=32, Hkv=8, 16-token pages,
     # d=128, the dense decode's key lengths; pages assigned in a seeded random order
@@ -441,7 +451,8 @@ def bench_extra(fa, reps=50):
     lse = torch.empty(B, Hq, device=dev)
     ws = torch.empty(fa.decode_paged_workspace_bytes(B, Hq, Hkv, P, maxp, d), dtype=torch.uint8,
                      device=dev)
-    ms = med(lambda: fa.decode_paged(q, kp, vp, table, sl, w.tau, 0, o, lse, ws), 2 * reps)
+    kv = alternating([(kp, vp), (kp.clone(), vp.clone())])   # as for the dense decode
+    ms = med(lambda: fa.decode_paged(q, *next(kv), table, sl, w.tau, 0, o, lse, ws), 2 * reps)
     if not bool(torch.isfinite(o.float()).all()):
         raise RuntimeError("paged decode produced non-finite output")
     nbytes = (float(seqlens.astype("int64").sum()) * Hkv * d * 2 * 2 + 2 * B * Hq * d * 2
@@ -449,9 +460,9 @@ def bench_extra(fa, reps=50):
     out["decode_paged_gqa"] = {"shape": {"B": B, "Hq": Hq, "Hkv": Hkv, "page_size": P, "d": d},
                                "seqlens_sum": int(seqlens.sum()),
                                "num_splits": fa.decode_paged_num_splits(B, Hq, Hkv, P, maxp, d),
-                               "ms": ms, "GB/s": round(nbytes / ms / 1e6, 1),
+                               "input_copies": 2, "ms": ms, "GB/s": round(nbytes / ms / 1e6, 1),
                                "frac_hbm": round(nbytes / ms / 1e-3 / PEAK_HBM, 4)}
-    del q, kp, vp, o, lse, ws, table
+    del q, kp, vp, o, lse, ws, table, kv
 
     # backward: 4 x 16 x 4096 x 64, causal
     w = fa_inputs.WORKLOADS[5]
