@@ -69,6 +69,21 @@ def test_paged_splits_and_pages(num_splits, page_size):
     assert_close(lse, rl, "bf16", "LSE", kind="lse")
 
 
+def test_paged_split_layout_edges():
+    """Two splits of 1024 keys: split 0 takes the whole first chunk, the last
+    split the rest.  Lengths: both splits whole (L = 2 * 1024), the last split
+    empty (1024), the first split empty and the last one holding 1023 keys or
+    a single key, and one key after a whole chunk (1025)."""
+    import io_aware_tiled_03_amd as fa
+    seqlens = [2048, 1024, 1023, 1025, 1]
+    x = fa_inputs.paged_decode_inputs(len(seqlens), 8, 2, 16, 64, "bf16", 9450, seqlens)
+    assert fa.decode_paged_num_splits(len(seqlens), 8, 2, 16, 2048 // 16, 64, 2) == 2
+    o, lse = _run(x, 0.125, 2)
+    ro, rl = _oracle(x, 0.125)
+    assert_close(o, ro, "bf16", "O")
+    assert_close(lse, rl, "bf16", "LSE", kind="lse")
+
+
 def test_paged_empty_sequence():
     """L_b = 0: O = 0 and LSE = -inf; the other sequences are unaffected."""
     x = fa_inputs.paged_decode_inputs(3, 8, 2, 16, 128, "bf16", 9500, [0, 40, 0])
