@@ -140,6 +140,12 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 __device__ __forceinline__ u32x4 buf_ld16_nt(rsrc_t r, uint32_t byte_off) {
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 2));
 }
+// a ^ b ^ c in one instruction (v_bitop3_b32 with the three-input parity
+// table 0x96; the compiler emits two XORs for the plain expression).
+__device__ __forceinline__ uint32_t xor3(uint32_t a, uint32_t b, uint32_t c) {
+    return __builtin_amdgcn_bitop3_b32(a, b, c, 0x96);
+}
+
 // Philox4x32 with 10 rounds (J. K. Salmon et al., "Parallel random numbers:
 // as easy as 1, 2, 3", SC11): each round multiplies counter words 0 and 2 by
 // the two round constants (one 32x32 -> 64-bit product each) and outputs
@@ -155,8 +161,8 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
         }
         const uint64_t p0 = (uint64_t)c0 * 0xD2511F53u;
         const uint64_t p1 = (uint64_t)c2 * 0xCD9E8D57u;
-        const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
-        const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+        const uint32_t n0 = xor3((uint32_t)(p1 >> 32), c1, k0);
+        const uint32_t n2 = xor3((uint32_t)(p0 >> 32), c3, k1);
         c1 = (uint32_t)p1;
         c3 = (uint32_t)p0;
         c0 = n0;
