@@ -8,8 +8,9 @@
 //   instruction of a wave reads whole consecutive rows; the dot products are
 //   reduced across the lanes of a row, and each wave keeps its own running
 //   max m, sum l and output o (the block recurrence of the "flash-attention"
-//   page, "como funciona").  The four waves are merged through LDS and the
-//   split writes o_s = o/l and lse_s = tau*m + ln(l) (or -inf when empty).
+//   page, "como funciona").  The waves (4, or 16 in a grid smaller than
+//   the part's CU count) are merged through LDS and the split writes
+//   o_s = o/l and lse_s = tau*m + ln(l) (or -inf when empty).
 // decode_merge_kernel: one wave per (b, h) combines the splits with the same
 //   merge rule: LSE = ln sum_s exp(lse_s), O = sum_s exp(lse_s - LSE) o_s.
 // Key rows at or beyond L_b are never read: padding may hold anything.
@@ -92,8 +93,8 @@ __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) void decode_split_kernel(
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(64 * NW) void decode_split_kernel(
     const T* __restrict__ Q, const T* __restrict__ K, const T* __restrict__ V,
     const int* __restrict__ seqlens, int B, int H, int N_max, int chunk, float scale_log2,
     float tau, float* __restrict__ ws_o, float* __restrict__ ws_lse, T* __restrict__ O,
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         m = mnew;
     };
 
-    // The chunk is walked in stages of KPI keys; wave w takes stages w, w+4, ...
+    // The chunk is walked in stages of KPI keys; wave w takes stages w, w+NW, ...
     // Two register stages: the loads of the next keys are in flight while the
     // current ones are consumed.
     const int nst = (ke - kb + KPI - 1) / KPI;
@@ -196,11 +197,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         u32x4 ka[U], va[U], kn[U], vn[U];
         load(ka, va, stage_key(t));
         while (true) {
-            const int t1 = t + 4;
+            const int t1 = t + NW;
             if (t1 < nst) load(kn, vn, stage_key(t1));
             consume(ka, va, stage_key(t));
             if (t1 >= nst) break;
-            const int t2 = t1 + 4;
+            const int t2 = t1 + NW;
             if (t2 < nst) load(ka, va, stage_key(t2));
             consume(kn, vn, stage_key(t1));
             if (t2 >= nst) break;
@@ -223,8 +224,8 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
         }
         m = mn;
     }
-    // combine the four waves
-    __shared__ float sm[4], sl[4], so[4][D];
+    // combine the NW waves
+    __shared__ float sm[NW], sl[NW], so[NW][D];
     if (g == 0) {
 #pragma unroll
         for (int i = 0; i < PER; ++i) so[wave][c * PER + i] = o[i];
@@ -232,10 +233,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(
     }
     __syncthreads();
     if (tid < D) {
-        float M = fmaxf(fmaxf(sm[0], sm[1]), fmaxf(sm[2], sm[3]));
+        float M = sm[0];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) M = fmaxf(M, sm[w]);
         float lt = 0.f, ot = 0.f;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) {
+        for (int w = 0; w < NW; ++w) {
             const float a = (sm[w] == neg_inf()) ? 0.f : fast_exp2((sm[w] - M) * scale_log2);
             lt += sl[w] * a;
             ot += so[w][tid] * a;
@@ -531,10 +534,20 @@ void launch_paged(const PagedDecodeArgs& a, hipStream_t st) {
 
 template <typename T, int D>
 void launch(const DecodeArgs& a, hipStream_t st) {
-    hipLaunchKernelGGL((decode_split_kernel<T, D>), dim3(a.num_splits * a.B * a.H), dim3(256), 0, st,
-                       (const T*)a.q, (const T*)a.k, (const T*)a.v, a.seqlens, a.B, a.H, a.N_max,
-                       a.chunk, a.tau * kLog2e, a.tau, a.ws_o, a.ws_lse,
-                       a.num_splits == 1 ? (T*)a.o : nullptr, a.num_splits == 1 ? a.lse : nullptr);
+    // A grid with fewer workgroups than the part has CUs (a small decode in
+    // one split) takes 16 waves per workgroup, so that enough rows are in
+    // flight per sequence; larger grids take 4.
+    const unsigned grid = (unsigned)a.num_splits * a.B * a.H;
+    T* const o1 = a.num_splits == 1 ? (T*)a.o : nullptr;
+    float* const lse1 = a.num_splits == 1 ? a.lse : nullptr;
+    if (grid < 256)
+        hipLaunchKernelGGL((decode_split_kernel<T, D, 16>), dim3(grid), dim3(1024), 0, st,
+                           (const T*)a.q, (const T*)a.k, (const T*)a.v, a.seqlens, a.B, a.H,
+                           a.N_max, a.chunk, a.tau * kLog2e, a.tau, a.ws_o, a.ws_lse, o1, lse1);
+    else
+        hipLaunchKernelGGL((decode_split_kernel<T, D, 4>), dim3(grid), dim3(256), 0, st,
+                           (const T*)a.q, (const T*)a.k, (const T*)a.v, a.seqlens, a.B, a.H,
+                           a.N_max, a.chunk, a.tau * kLog2e, a.tau, a.ws_o, a.ws_lse, o1, lse1);
     if (a.num_splits > 1)
         hipLaunchKernelGGL((decode_merge_kernel<T, D>), dim3(a.B * a.H), dim3(64), 0, st, a.ws_o,
                            a.ws_lse, a.num_splits, a.B * a.H, (T*)a.o, a.lse);
