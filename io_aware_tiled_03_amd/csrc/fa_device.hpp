@@ -198,21 +198,28 @@ struct Dropout {
 // a[r].  Two butterfly stages (partner lane r^1, then r^2) exchange one
 // element per pair of indices through DPP quad permutes.
 __device__ __forceinline__ u32x4 quad_transpose(u32x4 a, int r) {
-#pragma unroll
-    for (int k = 1; k <= 2; k <<= 1) {
-        const bool hi = (r & k) != 0;
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            if (w & k) continue;   // pair (w, w + k)
-            const uint32_t send = hi ? a[w] : a[w + k];
-            const uint32_t recv = (uint32_t)(k == 1
-                ? __builtin_amdgcn_mov_dpp((int)send, kDppXor1, 0xF, 0xF, false)
-                : __builtin_amdgcn_mov_dpp((int)send, kDppXor2, 0xF, 0xF, false));
-            if (hi) a[w] = recv;
-            else a[w + k] = recv;
-        }
+    // The four words as named scalars: indexing the vector with a choice of
+    // two positions made the compiler build run-time-indexed extracts
+    // (compares and select chains) around every exchange.
+    uint32_t a0 = a[0], a1 = a[1], a2 = a[2], a3 = a[3];
+    const bool h1 = (r & 1) != 0, h2 = (r & 2) != 0;
+    {   // partner r ^ 1: pairs (0, 1) and (2, 3)
+        const uint32_t t0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(h1 ? a0 : a1), kDppXor1, 0xF, 0xF, false);
+        const uint32_t t1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(h1 ? a2 : a3), kDppXor1, 0xF, 0xF, false);
+        a0 = h1 ? t0 : a0;
+        a1 = h1 ? a1 : t0;
+        a2 = h1 ? t1 : a2;
+        a3 = h1 ? a3 : t1;
     }
-    return a;
+    {   // partner r ^ 2: pairs (0, 2) and (1, 3)
+        const uint32_t t0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(h2 ? a0 : a2), kDppXor2, 0xF, 0xF, false);
+        const uint32_t t1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)(h2 ? a1 : a3), kDppXor2, 0xF, 0xF, false);
+        a0 = h2 ? t0 : a0;
+        a2 = h2 ? a2 : t0;
+        a1 = h2 ? t1 : a1;
+        a3 = h2 ? a3 : t1;
+    }
+    return u32x4{a0, a1, a2, a3};
 }
 
 // 4 x 4 byte transpose inside one lane: out[e] holds byte e of in[0..3]
