@@ -229,12 +229,16 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                 kb4 = quad_transpose(byte_transpose(
                           drop.block(key, qs + 16 * (e >> 1) + 8 * hf + 4 * (e & 1), bh)), e);
             }
+            // register r holds query qb0 + d_r, d_r = 16 (r / 8) + r % 8: the mask
+            // tests compare the constant d_r with per-lane limits
+            const int qb0 = qs + 8 * hf;
+            const int lim_c = key - qb0, lim_w = key - qb0 + window;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float p = fast_exp2(__builtin_fmaf(sacc[r], scale_log2, -lq[r >> 2][r & 3]));
                 if constexpr (MASK) {
-                    const int q = qs + 16 * (r >> 3) + 8 * hf + (r & 7);
-                    if (CAUSAL && (key > q || (WIN && q - key >= window && key >= sinks))) p = 0.f;
+                    const int dr = 16 * (r >> 3) + (r & 7);
+                    if (CAUSAL && (dr < lim_c || (WIN && dr >= lim_w && key >= sinks))) p = 0.f;
                 }
                 if constexpr (DROP) {
                     const bool kept = drop.keep(kb4[r >> 2], r & 3);
@@ -471,13 +475,16 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
                 dw = quad_transpose(
                     drop.block(k0 + kb * 32 + 16 * (r4 >> 1) + 8 * hf + 4 * (r4 & 1), qrow, bh), r4);
             }
+            // register r holds key kb0 + d_r, d_r = 16 (r / 8) + r % 8: the mask
+            // tests compare the constant d_r with per-lane limits
+            const int kb0 = k0 + kb * 32 + 8 * hf;
+            const int lim_n = N - kb0, lim_c = qrow - kb0, lim_w = qrow - kb0 - window, lim_s = sinks - kb0;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 float p = fast_exp2(__builtin_fmaf(sacc[r], scale_log2, -lse2));
                 if constexpr (MASK) {
-                    const int kk = k0 + kb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7);
-                    if (kk >= N ||
-                        (CAUSAL && (kk > qrow || (WIN && qrow - kk >= window && kk >= sinks))))
+                    const int dr = 16 * (r >> 3) + (r & 7);
+                    if (dr >= lim_n || (CAUSAL && (dr > lim_c || (WIN && dr <= lim_w && dr >= lim_s))))
                         p = 0.f;
                 }
                 if constexpr (DROP) {

@@ -223,16 +223,22 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
             }
 #endif
             if constexpr (MASK) {
+                // register r of block kb holds key kb0 + d_r, with kb0 per lane
+                // and d_r = 16 (r / 8) + r % 8 fixed: each test below compares
+                // the constant d_r with one per-lane limit
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb)
+                for (int kb = 0; kb < NKB; ++kb) {
+                    const int kb0 = k0 + kb * 32 + 8 * hf;
+                    const int lim_n = N - kb0, lim_c = qrow - kb0;
+                    const int lim_w = qrow - kb0 - window, lim_s = sinks - kb0;
 #pragma unroll
                     for (int r = 0; r < 16; ++r) {
-                        const int key = k0 + kb * 32 + 16 * (r >> 3) + 8 * hf + (r & 7);
-                        if (key >= N ||
-                            (CAUSAL && (key > qrow || (WIN && qrow - key >= window && key >= sinks))) ||
+                        const int dr = 16 * (r >> 3) + (r & 7);
+                        if (dr >= lim_n || (CAUSAL && (dr > lim_c || (WIN && dr <= lim_w && dr >= lim_s))) ||
                             (BLK && !bbit[kb]))
                             s[kb][r] = neg_inf();
                     }
+                }
             }
         };
         // Move the reference to the tile's maximum where that exceeds it by
