@@ -255,37 +255,54 @@ __global__ __launch_bounds__(64 * NW) void decode_split_kernel(
 
 // One wave per (b, h): lane t owns head-dim entries t and t + 64 (d = 128) or
 // t (d = 64).  The split LSEs are read by the lanes in parallel (64 at a
-// time) and reduced across the wave; the partial outputs of all splits are
-// then loaded independently, so no load waits on another.
+// time) and reduced across the wave; the partial outputs are loaded
+// independently of them (the first 16 splits' before the reduction).
 template <typename T, int D>
 __global__ __launch_bounds__(64) void decode_merge_kernel(
     const float* __restrict__ ws_o, const float* __restrict__ ws_lse, int S, int BH,
     T* __restrict__ O, float* __restrict__ LSE) {
     const int bh = blockIdx.x, t = threadIdx.x;
+    constexpr int PL = D / 64;
+    // The partial outputs of the first PRE splits are loaded before the LSEs
+    // are reduced (their addresses do not depend on the weights), so that a
+    // call with at most PRE splits waits for memory once.
+    constexpr int PRE = 16;
+    float po[PRE][PL];
+#pragma unroll
+    for (int j = 0; j < PRE; ++j)
+#pragma unroll
+        for (int i = 0; i < PL; ++i)
+            po[j][i] = j < S ? ws_o[((size_t)j * BH + bh) * D + t + 64 * i] : 0.f;
     float M = neg_inf();
     for (int s0 = 0; s0 < S; s0 += 64)
         if (s0 + t < S) M = fmaxf(M, ws_lse[(size_t)(s0 + t) * BH + bh]);
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-    constexpr int PL = D / 64;
     float acc[PL];
 #pragma unroll
     for (int i = 0; i < PL; ++i) acc[i] = 0.f;
     float sum = 0.f;
-    if (M != neg_inf()) {
-        for (int s0 = 0; s0 < S; s0 += 64) {
-            // lane t holds the weight of split s0 + t
-            const float ls = s0 + t < S ? ws_lse[(size_t)(s0 + t) * BH + bh] : neg_inf();
-            const float wt = ls == neg_inf() ? 0.f : __expf(ls - M);
-            const int n = min(64, S - s0);
-#pragma unroll 8
-            for (int j = 0; j < n; ++j) {
-                const float w = __shfl(wt, j, 64);
-                sum += w;
-                const float* src = ws_o + ((size_t)(s0 + j) * BH + bh) * D + t;
+    // (with every split empty, M = -inf and every weight is 0: O = 0, LSE = -inf)
+    for (int s0 = 0; s0 < S; s0 += 64) {
+        // lane t holds the weight of split s0 + t
+        const float ls = s0 + t < S ? ws_lse[(size_t)(s0 + t) * BH + bh] : neg_inf();
+        const float wt = ls == neg_inf() ? 0.f : __expf(ls - M);
+        const int n = min(64, S - s0);
+        if (s0 == 0) {
 #pragma unroll
-                for (int i = 0; i < PL; ++i) acc[i] += w * src[64 * i];
+            for (int j = 0; j < PRE; ++j) {
+                const float w = __shfl(wt, j, 64);   // 0 for j >= S
+                sum += w;
+#pragma unroll
+                for (int i = 0; i < PL; ++i) acc[i] += w * po[j][i];
             }
+        }
+        for (int j = s0 == 0 ? PRE : 0; j < n; ++j) {
+            const float w = __shfl(wt, j, 64);
+            sum += w;
+            const float* src = ws_o + ((size_t)(s0 + j) * BH + bh) * D + t;
+#pragma unroll
+            for (int i = 0; i < PL; ++i) acc[i] += w * src[64 * i];
         }
     }
     const float inv = sum > 0.f ? 1.f / sum : 0.f;
