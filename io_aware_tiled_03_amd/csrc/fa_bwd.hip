@@ -175,8 +175,98 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     }
     auto block_bit = [&](int q) { return bmcol[(size_t)min(q >> bs.lgbq, bs.nbq - 1) * bs.nbk] != 0; };
 
+    // Unmasked tiles without dropout or a block mask (every 32-query block
+    // runs, dS = P o (dP - D) with -D in dP's accumulator): the same arithmetic
+    // as compute() below, software-pipelined over the blocks.  Block qb's S
+    // and dP products are issued before block qb-1's dV and dK products, and
+    // block qb's softmax does not depend on those, so one wave's vector and
+    // matrix work can overlap instead of waiting on each other in turn (4k
+    // causal backward, outputs bit-identical: dK/dV 2% faster at d = 64, 7% at
+    // d = 128).  The general body keeps its order: held across a block, the
+    // packed operands cost 16 registers, which the dropout variants lack.
+    auto compute_pipe = [&](auto bufc, int q0) __attribute__((always_inline)) {
+        constexpr bool B1 = decltype(bufc)::value != 0;
+        const uint16_t* q_lds = B1 ? sQ1 : sQ0;
+        const uint16_t* o_lds = B1 ? sdO1 : sdO0;
+        const float* l_lds = B1 ? sL1 : sL0;
+        const float* d_lds = B1 ? sD1 : sD0;
+        auto sdp = [&](int qb, f32x16& sacc, f32x16& dp, f32x4* lq) __attribute__((always_inline)) {
+            u32x4 qa[D / 16], oa[D / 16];
+#pragma unroll
+            for (int ks = 0; ks < D / 16; ++ks) {
+                qa[ks] = ld16(q_lds + qb * 32 * STR + a_off + ks * 16);
+                oa[ks] = ld16(o_lds + qb * 32 * STR + a_off + ks * 16);
+            }
+            f32x4 dq4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lq[i] = *reinterpret_cast<const f32x4*>(&l_lds[qb * 32 + 16 * (i >> 1) + 8 * hf + 4 * (i & 1)]);
+                dq4[i] = *reinterpret_cast<const f32x4*>(&d_lds[qb * 32 + 16 * (i >> 1) + 8 * hf + 4 * (i & 1)]);
+            }
+            f32x16 negd;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) negd[r] = dq4[r >> 2][r & 3];
+            sacc = mfma32x32x16_zero(qa[0], kf[0]);
+            dp = mfma32x32x16(oa[0], vf[0], negd);
+#pragma unroll
+            for (int ks = 1; ks < D / 16; ++ks) {
+                sacc = mfma32x32x16(qa[ks], kf[ks], sacc);
+                dp = mfma32x32x16(oa[ks], vf[ks], dp);
+            }
+        };
+        auto soft = [&](const f32x16& sacc, const f32x16& dp, const f32x4* lq, u32x4* pf, u32x4* dsf)
+            __attribute__((always_inline)) {
+            float pv[16], dv[16];
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                pv[r] = fast_exp2(__builtin_fmaf(sacc[r], scale_log2, -lq[r >> 2][r & 3]));
+                dv[r] = pv[r] * dp[r];
+            }
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    pf[t][w] = pack_bf16x2(pv[8 * t + 2 * w], pv[8 * t + 2 * w + 1]);
+                    dsf[t][w] = pack_bf16x2(dv[8 * t + 2 * w], dv[8 * t + 2 * w + 1]);
+                }
+        };
+        auto acc = [&](int qb, const u32x4* pf, const u32x4* dsf) __attribute__((always_inline)) {
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int tb = t_off + (qb * 32 + 16 * t) * STR;
+                u32x4 ot[D / 32], qt4[D / 32];
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    ot[db] = lds_read_tr16_x2(o_lds + tb + db * 32, o_lds + tb + db * 32 + 4 * STR);
+                    qt4[db] = lds_read_tr16_x2(q_lds + tb + db * 32, q_lds + tb + db * 32 + 4 * STR);
+                }
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db) {
+                    dvacc[db] = mfma32x32x16(ot[db], pf[t], dvacc[db]);
+                    dkacc[db] = mfma32x32x16(qt4[db], dsf[t], dkacc[db]);
+                }
+            }
+        };
+        f32x16 sacc, dp;
+        f32x4 lq[4];
+        u32x4 pf[2], dsf[2];
+        sdp(0, sacc, dp, lq);
+        soft(sacc, dp, lq, pf, dsf);
+#pragma unroll
+        for (int qb = 1; qb < BR / 32; ++qb) {
+            sdp(qb, sacc, dp, lq);
+            acc(qb - 1, pf, dsf);
+            soft(sacc, dp, lq, pf, dsf);
+        }
+        acc(BR / 32 - 1, pf, dsf);
+    };
+
     auto compute = [&](auto bufc, int q0, auto maskc) __attribute__((always_inline)) {
         constexpr bool MASK = decltype(maskc)::value != 0;
+        if constexpr (!MASK && !BLK && !DROP) {
+            compute_pipe(bufc, q0);
+            return;
+        }
         constexpr bool B1 = decltype(bufc)::value != 0;
         const uint16_t* q_lds = B1 ? sQ1 : sQ0;
         const uint16_t* o_lds = B1 ? sdO1 : sdO0;
