@@ -24,7 +24,8 @@ The JSON line also carries, from the same run:
   * "also_measured" (skip: --no-extra): the GPT-2-medium-shaped step (fwd
     non-causal, fwd causal, bwd causal, decode), the tiny fp32 forward, the
     split-KV decode, the paged grouped-head decode, the 4k causal backward,
-    the prefill as a sliding-window and as a block-sparse layer, and dropout,
+    the prefill as a sliding-window and as a block-sparse layer (forward and
+    backward), and dropout,
     each against its roofline (the decodes alternate between two copies of
     their caches, so that no call is served from the caches by the previous);
   * "cpu_baseline" (skip: --no-cpu): the float64 oracle on the host over two
@@ -379,6 +380,14 @@ def bench_extra(fa, reps=50):
     out["window_prefill"] = {"shape": [B, H, N, d], "window": wnd, "sinks": 0, "ms": ms,
                              "TFLOP/s": round(fl / ms / 1e9, 2),
                              "frac_mfma_bf16": round(fl / ms / 1e-3 / PEAK_MFMA_BF16, 4)}
+    # its backward (dQ, then dK and dV), 5 products over the visible pairs
+    do = torch.randn(B, H, N, d, device=dev, generator=g).to(torch.bfloat16)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    bws = torch.empty(fa.bwd_workspace_bytes(B, H, N), dtype=torch.uint8, device=dev)
+    ms = med(lambda: fa.bwd(q, k, v, o, lse, do, 1 / math.sqrt(d), True, dq, dk, dv, bws,
+                            window=wnd), reps // 2)
+    out["window_prefill"].update({"bwd_ms": ms, "bwd_TFLOP/s": round(2.5 * fl / ms / 1e9, 2),
+                                  "bwd_frac_mfma_bf16": round(2.5 * fl / ms / 1e-3 / PEAK_MFMA_BF16, 4)})
 
     # the same prefill block-sparse: 128 x 128 blocks, a band of 3 blocks
     # around the diagonal plus the first key block (global tokens), causal
@@ -396,7 +405,15 @@ def bench_extra(fa, reps=50):
                                    "density": round(pairs / (N * (N + 1) / 2), 4), "ms": ms,
                                    "TFLOP/s": round(fl / ms / 1e9, 2),
                                    "frac_mfma_bf16": round(fl / ms / 1e-3 / PEAK_MFMA_BF16, 4)}
-    del q, k, v, o, lse, bm
+    # its backward: the workgroup holding the global key block walks every query tile
+    ms = med(lambda: fa.bwd(q, k, v, o, lse, do, 1 / math.sqrt(d), True, dq, dk, dv, bws,
+                            block_mask=bm, block_size=(bs, bs)), reps // 2)
+    out["block_sparse_prefill"].update({
+        "bwd_ms": ms, "bwd_TFLOP/s": round(2.5 * fl / ms / 1e9, 2),
+        "bwd_frac_mfma_bf16": round(2.5 * fl / ms / 1e-3 / PEAK_MFMA_BF16, 4),
+        "bwd_note": "bound by the dK/dV workgroup of the global key block, which walks all 256 "
+                    "query tiles while the others walk about 4 (no partial-sum split)"})
+    del q, k, v, o, lse, bm, do, dq, dk, dv, bws
 
     # split-KV decode: 64 x 32 x 8192 x 128, L_b ~ U[1024, 8192]
     w = fa_inputs.WORKLOADS[4]
