@@ -405,15 +405,16 @@ def bench_extra(fa, reps=50):
                                    "density": round(pairs / (N * (N + 1) / 2), 4), "ms": ms,
                                    "TFLOP/s": round(fl / ms / 1e9, 2),
                                    "frac_mfma_bf16": round(fl / ms / 1e-3 / PEAK_MFMA_BF16, 4)}
-    # its backward: the workgroup holding the global key block walks every query tile
-    ms = med(lambda: fa.bwd(q, k, v, o, lse, do, 1 / math.sqrt(d), True, dq, dk, dv, bws,
+    # its backward, with the workspace that lets the global key block's long
+    # list of query tiles be split over several workgroups
+    sws = torch.empty(fa.bwd_block_sparse_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
+    ms = med(lambda: fa.bwd(q, k, v, o, lse, do, 1 / math.sqrt(d), True, dq, dk, dv, sws,
                             block_mask=bm, block_size=(bs, bs)), reps // 2)
     out["block_sparse_prefill"].update({
         "bwd_ms": ms, "bwd_TFLOP/s": round(2.5 * fl / ms / 1e9, 2),
         "bwd_frac_mfma_bf16": round(2.5 * fl / ms / 1e-3 / PEAK_MFMA_BF16, 4),
-        "bwd_note": "bound by the dK/dV workgroup of the global key block, which walks all 256 "
-                    "query tiles while the others walk about 4 (no partial-sum split)"})
-    del q, k, v, o, lse, bm, do, dq, dk, dv, bws
+        "bwd_workspace_MiB": round(sws.numel() / 2 ** 20, 1)})
+    del q, k, v, o, lse, bm, do, dq, dk, dv, bws, sws
 
     # split-KV decode: 64 x 32 x 8192 x 128, L_b ~ U[1024, 8192]
     w = fa_inputs.WORKLOADS[4]

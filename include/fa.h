@@ -322,10 +322,30 @@ int fa_bwd_dropout(const void* q, const void* k, const void* v, const void* o, c
                    void* workspace, size_t workspace_bytes, int dtype, void* stream);
 
 /*
+ * fa_bwd_block_sparse_workspace_bytes - workspace with which
+ * fa_bwd_block_sparse splits long key-tile lists: D, a split plan and
+ * clamp(items / 16, 32, 256) slots of 2 * 128 * d floats (items = B * H *
+ * ceil(N / 128)).  0 for invalid sizes or d other than 64 and 128.  A larger
+ * workspace gives more slots (at most 4096).
+ */
+size_t fa_bwd_block_sparse_workspace_bytes(int B, int H, int N, int d);
+
+/*
  * fa_bwd_block_sparse - backward of fa_fwd_block_sparse (same mask and block
  * sizes; o and lse from that forward).  Query and key tiles holding no set
  * block are skipped; rows with no visible key receive zero gradient.
  * Arguments as fa_bwd plus the block mask.
+ *
+ * The dK/dV pass walks, for each 128-key tile, the list of query tiles that
+ * hold a set block for it; under a mask with global key blocks one such list
+ * can be far longer than the rest.  With a workspace of at least
+ * fa_bwd_block_sparse_workspace_bytes (anything from D plus the plan plus two
+ * slots on), the call first counts every list on the device, cuts lists
+ * longer than a planned part into parts taken by extra workgroups, and the
+ * last part of each list to finish adds the fp32 partials of all its parts in
+ * part order (deterministic; lists beyond the slots are walked whole).  With
+ * fa_bwd_workspace_bytes(B, H, N) bytes every list is walked whole by one
+ * workgroup.  Calls that share a workspace must not overlap.
  */
 int fa_bwd_block_sparse(const void* q, const void* k, const void* v, const void* o,
                         const float* lse, const void* dout, void* dq, void* dk, void* dv,

@@ -51,6 +51,7 @@ SIGNATURES = {
                            _I, _P]),
     "fa_bwd_dropout": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _F, _U64,
                             _U32, _P, _Z, _I, _P]),
+    "fa_bwd_block_sparse_workspace_bytes": (_Z, [_I, _I, _I, _I]),
     "fa_bwd_block_sparse": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _F, _I, _P,
                                  _I, _I, _I, _P, _Z, _I, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
@@ -329,6 +330,10 @@ def bwd_workspace_bytes(B, H, N):
     return int(lib().fa_bwd_workspace_bytes(B, H, N))
 
 
+def bwd_block_sparse_workspace_bytes(B, H, N, d):
+    return int(lib().fa_bwd_block_sparse_workspace_bytes(B, H, N, d))
+
+
 def bwd(q, k, v, o, lse, do, tau=None, causal=False, dq=None, dk=None, dv=None, workspace=None,
         stage=None, window=None, sinks=0, dropout=None, block_mask=None, block_size=(128, 128)):
     """dQ, dK, dV of fa_fwd's output given dO, via fa_bwd (workspace holds D on return).
@@ -337,7 +342,9 @@ def bwd(q, k, v, o, lse, do, tau=None, causal=False, dq=None, dk=None, dv=None, 
     and D, 1: dK and dV, which reads D).  With
     window (causal only): the backward of the sliding-window forward, via fa_bwd_window.
     With dropout = (p, seed, offset): the backward of fa_fwd_dropout, via fa_bwd_dropout.
-    With block_mask: the backward of fa_fwd_block_sparse, via fa_bwd_block_sparse."""
+    With block_mask: the backward of fa_fwd_block_sparse, via fa_bwd_block_sparse; the
+    default workspace there is bwd_block_sparse_workspace_bytes, with which long key-tile
+    lists are split over several workgroups (a D-sized one walks each list whole)."""
     import torch
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, d]")
@@ -349,10 +356,14 @@ def bwd(q, k, v, o, lse, do, tau=None, causal=False, dq=None, dk=None, dv=None, 
     dv = torch.empty_like(v) if dv is None else dv
     _check_dense((("q", q), ("k", k), ("v", v), ("o", o), ("do", do), ("dq", dq), ("dk", dk),
                   ("dv", dv)), lse, B, H, N, d, q.dtype)
-    workspace = _workspace(workspace, bwd_workspace_bytes(B, H, N), q.device)
     bargs = None
     if block_mask is not None:
         bargs = _block_args(block_mask, block_size, H, N)
+    # a block-sparse call splits long key-tile lists when given the larger
+    # workspace (allocated here by default); D alone is enough otherwise
+    want = (bwd_block_sparse_workspace_bytes(B, H, N, d) if block_mask is not None and workspace is None
+            else bwd_workspace_bytes(B, H, N))
+    workspace = _workspace(workspace, want, q.device)
     _same_gpu([("q", q), ("k", k), ("v", v), ("o", o), ("lse", lse), ("do", do), ("dq", dq),
                ("dk", dk), ("dv", dv), ("workspace", workspace)]
               + ([("block_mask", block_mask)] if block_mask is not None else []))

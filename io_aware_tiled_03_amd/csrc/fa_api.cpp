@@ -264,7 +264,7 @@ int bwd_common(int stages, const void* q, const void* k, const void* v, const vo
                int N, int d, float tau, int causal, void* workspace, size_t workspace_bytes,
                int dtype, void* stream, int window = 0, int sinks = 0, int drop_thr = 0,
                unsigned long long seed = 0, unsigned int offset = 0,
-               const fa::BlockSparse* bs = nullptr) {
+               const fa::BlockSparse* bs = nullptr, bool split = false) {
     if (!q || !k || !v || !o || !lse || !dout || !dq || !dk || !dv) return FA_ERR_NULL;
     int st = check_common(B, H, N, d, tau, dtype);
     if (st != FA_OK) return st;
@@ -286,6 +286,17 @@ int bwd_common(int stages, const void* q, const void* k, const void* v, const vo
     a.seed = seed;
     a.offset = offset;
     if (bs) a.blk = *bs;
+    if (bs && split) {   // room for the split plan and at least two slots: split long lists
+        const size_t fixed = fa::blk_split_fixed_bytes(B, H, N), slot = fa::blk_split_slot_bytes(d);
+        if (workspace_bytes >= fixed + 2 * slot) {
+            char* const w = (char*)workspace;
+            a.split.plan = (int*)(w + fa::align256((size_t)B * H * N * sizeof(float)));
+            a.split.meta = (int*)(w + fixed - 256);
+            a.split.pool = (float*)(w + fixed);
+            const size_t n = (workspace_bytes - fixed) / slot;
+            a.split.slots = (int)(n < (size_t)fa::kBlkMaxSlots ? n : fa::kBlkMaxSlots);
+        }
+    }
     (void)hipGetLastError();
     fa::launch_bwd(a, stages, (hipStream_t)stream);
     return after_launch();
@@ -329,7 +340,15 @@ int fa_bwd_block_sparse(const void* q, const void* k, const void* v, const void*
     const int st = block_sparse_args(block_mask, mask_heads, block_q, block_k, H, N, &bs);
     if (st != FA_OK) return st;
     return bwd_common(3, q, k, v, o, lse, dout, dq, dk, dv, B, H, N, d, tau, causal, workspace,
-                      workspace_bytes, dtype, stream, 0, 0, 0, 0, 0, &bs);
+                      workspace_bytes, dtype, stream, 0, 0, 0, 0, 0, &bs, true);
+}
+
+size_t fa_bwd_block_sparse_workspace_bytes(int B, int H, int N, int d) {
+    if (B < 1 || H < 1 || N < 1 || (d != 64 && d != 128)) return 0;
+    const size_t items = fa::blk_split_items(B, H, N);
+    size_t slots = items / 16;   // every slot also launches one (possibly idle) helper workgroup
+    slots = slots < 32 ? 32 : (slots > 256 ? 256 : slots);
+    return fa::blk_split_fixed_bytes(B, H, N) + slots * fa::blk_split_slot_bytes(d);
 }
 
 int fa_bwd_stage(int stage, const void* q, const void* k, const void* v, const void* o,

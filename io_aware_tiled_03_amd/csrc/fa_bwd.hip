@@ -75,6 +75,133 @@ struct TileCopy {
 // (key j visible to query i iff j <= i and (i - j < window or j < sinks)).
 enum : int { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2, kMaskBlock = 3, kMaskBlockCausal = 4 };
 
+// Block-sparse dK/dV: whether query tile t (rows t*BR .. t*BR+BR-1) holds a
+// set block against key blocks kb0 .. kb1 of mask head mh (before the causal
+// diagonal, t < qt0, it never does).
+template <int BR, bool CAUSAL>
+__device__ __forceinline__ bool blk_qtile_active(const BlockSparse& bs, const unsigned char* mh, int t,
+                                                 int qt0, int kb0, int kb1) {
+    if (CAUSAL && t < qt0) return false;
+    const int rb0 = (t * BR) >> bs.lgbq, rb1 = min((t * BR + BR - 1) >> bs.lgbq, bs.nbq - 1);
+    bool act = false;
+    for (int rb = rb0; rb <= rb1; ++rb)
+        for (int kb = kb0; kb <= kb1; ++kb) act |= mh[(size_t)rb * bs.nbk + kb] != 0;
+    return act;
+}
+
+// Split plan, pass 1: one wave per (key tile, head) item counts the active
+// query tiles of its list (the same predicate the dK/dV workgroup lists them
+// with) into plan[4 item] and clears the item's arrival count.
+template <int BR, bool CAUSAL>
+__global__ __launch_bounds__(256) void blk_count_kernel(BlockSparse bs, int BH, int N, int n_items,
+                                                        int* __restrict__ plan) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int item = (int)blockIdx.x * 4 + wave;
+    if (item >= n_items) return;
+    const int kt = item / BH, bh = item % BH, k0 = kt * kBlkKeys;
+    const int head = bs.heads > 1 ? bh % bs.H : 0;
+    const unsigned char* mh = bs.mask + (size_t)head * bs.nbq * bs.nbk;
+    const int kb0 = k0 >> bs.lgbk, kb1 = (min(k0 + kBlkKeys, N) - 1) >> bs.lgbk;
+    const int n_qt = (N + BR - 1) / BR, qt0 = CAUSAL ? k0 / BR : 0;
+    int count = 0;
+    for (int c = 0; c < n_qt; c += 64) {
+        const int t = c + lane;
+        const bool act = t < n_qt && blk_qtile_active<BR, CAUSAL>(bs, mh, t, qt0, kb0, kb1);
+        count += __builtin_popcountll(__builtin_amdgcn_ballot_w64(act));
+    }
+    if (lane == 0) {
+        plan[4 * item] = count;
+        plan[4 * item + 3] = 0;
+    }
+}
+
+// Exclusive prefix sum over the 1024 threads of a workgroup; *total receives
+// the sum.  sh: 16 ints of LDS.
+__device__ __forceinline__ int block_excl_scan(int v, int* sh, int* total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int x = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == 63) sh[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+        int w = lane < 16 ? sh[lane] : 0;
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) {
+            const int y = __shfl_up(w, o);
+            if (lane >= o) w += y;
+        }
+        if (lane < 16) sh[lane] = w;
+    }
+    __syncthreads();
+    const int off = wave ? sh[wave - 1] : 0;
+    *total = sh[15];
+    __syncthreads();
+    return off + x - v;
+}
+
+// Split plan, pass 2 (one workgroup of 1024 threads, each taking a run of
+// consecutive items): a part holds at most T query tiles, T = max(kBlkMinPart, twice
+// the mean list length, the total over the resident workgroups); an item of
+// two or more parts gets one slot per part and one helper per part after the
+// first, in item order while slots last (later items keep nh = 0 and are
+// walked whole by their owner).  Writes plan[4 i] = helpers, [4 i + 1] =
+// first helper, [4 i + 2] = first slot and meta[0] = helpers in use.
+__global__ __launch_bounds__(1024) void blk_plan_kernel(int* __restrict__ plan, int* __restrict__ meta,
+                                                        int n_items, int slots, int conc) {
+    __shared__ int sh[16];
+    __shared__ long long shl[16];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int per = (n_items + 1023) / 1024, i0 = min(tid * per, n_items), i1 = min(i0 + per, n_items);
+    long long mine = 0;
+    for (int i = i0; i < i1; ++i) mine += plan[4 * i];
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) mine += __shfl_xor(mine, o);
+    if (lane == 0) shl[wave] = mine;
+    __syncthreads();
+    long long total = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) total += shl[w];
+    const long long t = max((long long)kBlkMinPart, max((2 * total + n_items - 1) / n_items, (total + conc - 1) / conc));
+    const int T = (int)min(t, 1LL << 30);
+    auto parts_of = [&](int i) { return (plan[4 * i] + T - 1) / T; };
+    // Slot demand per thread, capped at slots + 1: the prefix stays exact
+    // below the slot count and exceeds it whenever the true sum does.
+    int need_sum = 0;
+    for (int i = i0; i < i1; ++i) {
+        const int p = parts_of(i);
+        need_sum = min(need_sum + (p >= 2 ? p : 0), slots + 1);
+    }
+    int tot_s;
+    int sb = min(block_excl_scan(need_sum, sh, &tot_s), slots + 1);
+    // helpers: the items that fit take parts - 1 each (slots run out in item order)
+    int nh_sum = 0;
+    {
+        int run = sb;
+        for (int i = i0; i < i1; ++i) {
+            const int p = parts_of(i), need = p >= 2 ? p : 0;
+            if (need && run + need <= slots) nh_sum += p - 1;
+            run = min(run + need, slots + 1);
+        }
+    }
+    int tot_h;
+    int hb = block_excl_scan(nh_sum, sh, &tot_h);
+    for (int i = i0; i < i1; ++i) {
+        const int p = parts_of(i), need = p >= 2 ? p : 0;
+        const int nh = (need && sb + need <= slots) ? p - 1 : 0;
+        // every read of plan[4 i] above precedes this store (same thread)
+        plan[4 * i] = nh;
+        plan[4 * i + 1] = hb;
+        plan[4 * i + 2] = sb;
+        sb = min(sb + need, slots + 1);
+        hb += nh;
+    }
+    if (tid == 0) meta[0] = tot_h;
+}
+
 // DROP: the forward dropped P with the mask of Dropout::block; with
 // Z = keep / (1 - p): dV = (P o Z)^T dO and dS = P o (Z o dP - D).
 template <int D, int MODE, bool DROP>
@@ -82,13 +209,14 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     const uint16_t* __restrict__ dO, const float* __restrict__ LSE, const float* __restrict__ Dv,
     uint16_t* __restrict__ dK, uint16_t* __restrict__ dV, int BH, int N, float scale_log2,
-    float tau, int window, int sinks, Dropout drop, BlockSparse bs) {
+    float tau, int window, int sinks, Dropout drop, BlockSparse bs, BlkSplit split) {
     constexpr bool CAUSAL = MODE == kMaskCausal || MODE == kMaskWindow || MODE == kMaskBlockCausal;
     constexpr bool WIN = MODE == kMaskWindow, BLK = MODE >= kMaskBlock;
     // d = 64 streams 128-query tiles (measured 4% faster than 64 on the 1k and
     // 4k causal backward); d = 128 and the block-sparse variants keep 64, where
     // the larger tile would cost occupancy or is unmeasured.
     constexpr int BC = 128, BR = (D == 64 && !BLK) ? 128 : 64;
+    static_assert(!BLK || (BC == kBlkKeys && BR == 64), "the split plan counts 64-row query tiles of 128 keys");
     constexpr int STR = D + 8;                 // padded row (16 * odd bytes)
     // Without dropout, dS = P o (dP - D) takes -D as the starting accumulator
     // of the dP = dO V^T product, so the subtraction costs nothing; LDS then
@@ -110,8 +238,33 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform, in an SGPR
     const int ln = lane & 31, hf = lane >> 5;
-    const int kt = (int)(blockIdx.x / BH);      // causal: low key tiles carry the most work
-    const int bh = (int)(blockIdx.x % BH);
+    // Block-sparse with a split plan: the first split.slots workgroups are
+    // helpers (helper g takes part g - first + 1 of the item whose helper range
+    // holds g; unused helpers leave at once), the rest own one item each.
+    int item = (int)blockIdx.x, part = 0, nparts = 1, sbase = 0;
+    if constexpr (BLK) {
+        if (split.plan) {
+            const int n_items = (int)gridDim.x - split.slots;
+            if ((int)blockIdx.x < split.slots) {
+                const int g = (int)blockIdx.x;
+                if (g >= split.meta[0]) return;
+                int lo = 0, hi = n_items - 1;   // the last item whose first helper is <= g
+                while (lo < hi) {
+                    const int mid = (lo + hi + 1) >> 1;
+                    if (split.plan[4 * mid + 1] <= g) lo = mid;
+                    else hi = mid - 1;
+                }
+                item = lo;
+                part = g - split.plan[4 * item + 1] + 1;
+                nparts = split.plan[4 * item] + 1;
+                sbase = split.plan[4 * item + 2];
+            } else {
+                item = (int)blockIdx.x - split.slots;   // reads its plan entry once its list is known
+            }
+        }
+    }
+    const int kt = item / BH;      // causal: low key tiles carry the most work
+    const int bh = item % BH;
     const size_t base = (size_t)bh * N * D;
     const int k0 = kt * BC, kw = k0 + 32 * wave, key = kw + ln;
 
@@ -382,34 +535,46 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         const int head = bs.heads > 1 ? bh % bs.H : 0;
         const unsigned char* mh = bs.mask + (size_t)head * bs.nbq * bs.nbk;
         const int kb0 = k0 >> bs.lgbk, kb1 = (min(k0 + BC, N) - 1) >> bs.lgbk;
-        auto active = [&](int t) {
-            if (CAUSAL && t < qt0) return false;
-            const int rb0 = (t * BR) >> bs.lgbq, rb1 = min((t * BR + BR - 1) >> bs.lgbq, bs.nbq - 1);
-            bool act = false;
-            for (int rb = rb0; rb <= rb1; ++rb)
-                for (int kb = kb0; kb <= kb1; ++kb) act |= mh[(size_t)rb * bs.nbk + kb] != 0;
-            return act;
-        };
+        auto active = [&](int t) { return blk_qtile_active<BR, CAUSAL>(bs, mh, t, qt0, kb0, kb1); };
         npos = build_tile_list<4>(active, n_qt, s_list, s_bal, s_off, wave, lane, tid);
         pm1 = pu = 0;   // every listed tile runs the masked body
+    }
+    // positions [pbeg, pend) of the list are this workgroup's part
+    int pbeg = 0, pend = npos;
+    if constexpr (BLK) {
+        // An owner's list can only have been split if it is longer than the
+        // smallest part (kBlkMinPart tiles); a short list skips the plan read.
+        if (split.plan && (int)blockIdx.x >= split.slots && npos > kBlkMinPart) {
+            nparts = split.plan[4 * item] + 1;
+            sbase = split.plan[4 * item + 2];
+        }
+        if (nparts > 1) {   // npos <= 4096 and nparts <= npos: no overflow
+            pbeg = part * npos / nparts;
+            pend = (part + 1) * npos / nparts;
+        }
     }
     auto qt_at = [&](int p) {
         if constexpr (BLK) return (int)s_list[min(p, max(npos - 1, 0))];
         return qt0 + p;
     };
-    if (npos > 0) {
-        stage(qt_at(0), ic<0>{});
-        stage_ld(ic<0>{});
+    if (pbeg < pend) {
+        if (pbeg & 1) {
+            stage(qt_at(pbeg), ic<1>{});
+            stage_ld(ic<1>{});
+        } else {
+            stage(qt_at(pbeg), ic<0>{});
+            stage_ld(ic<0>{});
+        }
         wait_vmem();
         __syncthreads();
     }
     auto tile_b = [&](int p, auto bufc, auto maskc) __attribute__((always_inline)) {   // position p lives in buffer bufc
         constexpr ic<1 - decltype(bufc)::value> other{};
-        if (p + 1 < npos) stage(qt_at(p + 1), other);
+        if (p + 1 < pend) stage(qt_at(p + 1), other);
         const int q0 = qt_at(p) * BR;
         if (!(CAUSAL && q0 + BR - 1 < kw) && !(WIN && q0 - (kw + 31) >= window && kw >= sinks))
             compute(bufc, q0, maskc);
-        if (p + 1 < npos) stage_ld(other);
+        if (p + 1 < pend) stage_ld(other);
         wait_vmem();
         __syncthreads();
     };
@@ -424,9 +589,65 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
         }
         if (p < pe) tile_b(p, ic<0>{}, maskc);
     };
-    phase(0, pm1, ic<1>{});
-    phase(max(0, pm1), pu, ic<0>{});
-    phase(max(0, pu), npos, ic<1>{});
+    if constexpr (BLK) {
+        phase(pbeg, pend, ic<1>{});
+    } else {
+        phase(0, pm1, ic<1>{});
+        phase(max(0, pm1), pu, ic<0>{});
+        phase(max(0, pu), npos, ic<1>{});
+    }
+
+    // A part of a split list: write this part's fp32 partials to its slot
+    // (lane-contiguous float4 pieces in the accumulator layout), publish them,
+    // count the arrival; the part that arrives last adds every part's slot in
+    // part order (so the sum does not depend on which part finished last) and
+    // goes on to the epilogue, the others leave.  No workgroup waits for another.
+    if constexpr (BLK) {
+        if (nparts > 1) {
+            constexpr int SLOT = 2 * kBlkKeys * D;   // floats per slot
+            auto piece = [&](int which, int db, int g) {
+                return ((((which * 4 + wave) * (D / 32) + db) * 4 + g) * 64 + lane) * 4;
+            };
+            float* const mine = split.pool + (size_t)(sbase + part) * SLOT;
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    *reinterpret_cast<f32x4*>(mine + piece(0, db, g)) =
+                        f32x4{dkacc[db][4 * g], dkacc[db][4 * g + 1], dkacc[db][4 * g + 2], dkacc[db][4 * g + 3]};
+                    *reinterpret_cast<f32x4*>(mine + piece(1, db, g)) =
+                        f32x4{dvacc[db][4 * g], dvacc[db][4 * g + 1], dvacc[db][4 * g + 2], dvacc[db][4 * g + 3]};
+                }
+            __shared__ int s_last;
+            __threadfence();
+            __syncthreads();
+            if (tid == 0)
+                s_last = __hip_atomic_fetch_add(split.plan + 4 * item + 3, 1, __ATOMIC_ACQ_REL,
+                                                __HIP_MEMORY_SCOPE_AGENT) == nparts - 1;
+            __syncthreads();
+            if (!s_last) return;
+            __threadfence();
+#pragma unroll
+            for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) { dkacc[db][r] = 0.f; dvacc[db][r] = 0.f; }
+            for (int pp = 0; pp < nparts; ++pp) {
+                const float* const src = split.pool + (size_t)(sbase + pp) * SLOT;
+#pragma unroll
+                for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 a = *reinterpret_cast<const f32x4*>(src + piece(0, db, g));
+                        const f32x4 b = *reinterpret_cast<const f32x4*>(src + piece(1, db, g));
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            dkacc[db][4 * g + e] += a[e];
+                            dvacc[db][4 * g + e] += b[e];
+                        }
+                    }
+            }
+        }
+    }
 
     // Epilogue through LDS (stage_piece / store_rows); the staging buffers are
     // free: every tile ended with a barrier and no copy is in flight.
@@ -711,11 +932,31 @@ void launch(const BwdArgs& a, int stages, hipStream_t st) {
                            drop, a.blk);
     }
     if (stages & 2) {
-        const int nk = (a.N + 127) / 128;
-        hipLaunchKernelGGL((bwd_dkdv_kernel<D, MODE, DROP>), dim3(nk * bh), dim3(256), 0, st,
+        const int nk = (a.N + kBlkKeys - 1) / kBlkKeys;
+        BlkSplit split;
+        int helpers = 0;
+        if constexpr (MODE >= kMaskBlock) {
+            if (a.split.plan) {   // plan the parts, then helpers first in the grid
+                split = a.split;
+                helpers = split.slots;
+                int dev = 0, cus = 0;
+                if (hipGetDevice(&dev) != hipSuccess ||
+                    hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+                    cus < 1)
+                    cus = 256;
+                split.conc = 2 * cus;   // two dK/dV workgroups per CU
+                const int n_items = nk * bh;
+                constexpr bool CAUSAL = MODE == kMaskBlockCausal;
+                hipLaunchKernelGGL((blk_count_kernel<64, CAUSAL>), dim3((n_items + 3) / 4), dim3(256), 0,
+                                   st, a.blk, bh, a.N, n_items, split.plan);
+                hipLaunchKernelGGL(blk_plan_kernel, dim3(1), dim3(1024), 0, st, split.plan, split.meta,
+                                   n_items, split.slots, split.conc);
+            }
+        }
+        hipLaunchKernelGGL((bwd_dkdv_kernel<D, MODE, DROP>), dim3(helpers + nk * bh), dim3(256), 0, st,
                            (const uint16_t*)a.q, (const uint16_t*)a.k, (const uint16_t*)a.v,
                            (const uint16_t*)a.dout, a.lse, a.D, (uint16_t*)a.dk, (uint16_t*)a.dv,
-                           bh, a.N, a.tau * kLog2e, a.tau, a.window, a.sinks, drop, a.blk);
+                           bh, a.N, a.tau * kLog2e, a.tau, a.window, a.sinks, drop, a.blk, split);
     }
 }
 

@@ -19,6 +19,33 @@ struct BlockSparse {
     int nbq = 0, nbk = 0, lgbq = 0, lgbk = 0, heads = 0, H = 1;
 };
 
+// Block-sparse backward: a key tile whose list of active query tiles is long
+// is walked in parts by several dK/dV workgroups (its owner and helpers).
+// Each part writes fp32 partial dK and dV to a slot, and the last part to
+// finish adds the slots in part order and stores dK and dV.  The workspace
+// holds, after D: the plan, four ints per (key tile, head) item (helpers,
+// first helper, first slot, arrivals; the count pass leaves the list length
+// in the first), 64 ints of totals (helpers in use), then the slots.
+struct BlkSplit {
+    int* plan = nullptr;     // nullptr: no splitting, every owner walks its whole list
+    int* meta = nullptr;
+    float* pool = nullptr;   // [slots][2 (dK, dV)][128 * d] in the workgroup's register layout
+    int slots = 0;
+    int conc = 0;            // dK/dV workgroups resident at once (sizes the parts; set at launch)
+};
+constexpr int kBlkKeys = 128;   // keys per dK/dV workgroup
+inline size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+inline size_t blk_split_items(int B, int H, int N) {
+    return (size_t)B * H * ((N + kBlkKeys - 1) / kBlkKeys);
+}
+inline size_t blk_split_fixed_bytes(int B, int H, int N) {   // D, plan, totals
+    return align256((size_t)B * H * N * sizeof(float)) +
+           align256(blk_split_items(B, H, N) * 4 * sizeof(int)) + 256;
+}
+inline size_t blk_split_slot_bytes(int d) { return (size_t)2 * kBlkKeys * d * sizeof(float); }
+constexpr int kBlkMaxSlots = 4096;
+constexpr int kBlkMinPart = 4;   // smallest planned part (query tiles): shorter lists are never split
+
 struct FwdArgs {
     const void *q, *k, *v;
     void* o;
@@ -95,8 +122,9 @@ struct BwdArgs {
     unsigned long long seed = 0;
     unsigned int offset = 0;
     BlockSparse blk;
+    BlkSplit split;       // block-sparse only
 };
-// stages: bit 0 = D preprocess, bit 1 = dK/dV, bit 2 = dQ (launched in that order)
+// stages: bit 0 = dQ (which also writes D), bit 1 = dK/dV (reads D); launched in that order
 void launch_bwd(const BwdArgs& a, int stages, hipStream_t st);
 void launch_bwd_f32(const BwdArgs& a, int stages, hipStream_t st);   // dtype kF32 (no block mask)
 

@@ -149,6 +149,27 @@ void check_block_sparse() {
     CHECK(fa_bwd_block_sparse(P, P, P, P, L, P, P, P, P, 2, 3, 1000, 64, 0.125f, 0, M, 1, 32, 1024,
                               P, 2 * 3 * 1000 * 4, FA_BF16, nullptr) == FA_OK);
     CHECK(n_bwd == n0 + 1 && last_bwd.blk.nbq == 32 && last_bwd.blk.nbk == 1);
+    CHECK(last_bwd.split.plan == nullptr && last_bwd.split.slots == 0);   // D only: no split
+    // the split workspace: D, the plan (4 ints per 128-key tile and head), 256 bytes of totals,
+    // then slots of 2 * 128 * d floats, here the default 32
+    const size_t Dbytes = (size_t)2 * 3 * 1000 * 4, items = (size_t)2 * 3 * 8;
+    const size_t fixed = (Dbytes + 255) / 256 * 256 + (items * 16 + 255) / 256 * 256 + 256;
+    const size_t need = fa_bwd_block_sparse_workspace_bytes(2, 3, 1000, 64);
+    CHECK(need == fixed + 32 * (size_t)2 * 128 * 64 * 4);
+    CHECK(fa_bwd_block_sparse_workspace_bytes(2, 3, 1000, 96) == 0);
+    CHECK(fa_bwd_block_sparse_workspace_bytes(0, 3, 1000, 64) == 0);
+    char* const W = static_cast<char*>(P);
+    CHECK(fa_bwd_block_sparse(P, P, P, P, L, P, P, P, P, 2, 3, 1000, 64, 0.125f, 0, M, 1, 32, 1024,
+                              P, need, FA_BF16, nullptr) == FA_OK);
+    CHECK(last_bwd.split.plan == reinterpret_cast<int*>(W + (Dbytes + 255) / 256 * 256));
+    CHECK(last_bwd.split.meta == reinterpret_cast<int*>(W + fixed - 256));
+    CHECK(last_bwd.split.pool == reinterpret_cast<float*>(W + fixed) && last_bwd.split.slots == 32);
+    CHECK(fa_bwd_block_sparse(P, P, P, P, L, P, P, P, P, 2, 3, 1000, 64, 0.125f, 0, M, 1, 32, 1024,
+                              P, fixed + 2 * 2 * 128 * 64 * 4 - 1, FA_BF16, nullptr) == FA_OK);
+    CHECK(last_bwd.split.plan == nullptr);   // fewer than two slots: no split
+    CHECK(fa_bwd_block_sparse(P, P, P, P, L, P, P, P, P, 2, 3, 1000, 64, 0.125f, 0, M, 1, 32, 1024,
+                              P, fixed + (size_t)5000 * 2 * 128 * 64 * 4, FA_BF16, nullptr) == FA_OK);
+    CHECK(last_bwd.split.slots == fa::kBlkMaxSlots);
     expect_reject(FA_ERR_UNSUPPORTED, [&] {
         return fa_bwd_block_sparse(P, P, P, P, L, P, P, P, P, 2, 3, 1000, 64, 0.125f, 0, M, 1, 32, 1024,
                                    P, 2 * 3 * 1000 * 4, FA_F32, nullptr);
