@@ -364,8 +364,8 @@ def bench_extra(fa, reps=50):
     lse = torch.empty(1, 1, w.N, device=dev)
     ms = med(lambda: fa.fwd(q, k, v, w.tau, False, o, lse))
     out["tiny_fp32_fwd"] = {"shape": [w.B, w.H, w.N, w.d], "dtype": "f32", "ms": ms,
-                            "note": "latency-bound (32 single-wave workgroups, each reading its "
-                                    "256 key rows one after another); checked for parity, "
+                            "note": "latency-bound (32 workgroups of 8 waves, each wave reading "
+                                    "its 32 key rows one after another); checked for parity, "
                                     "no roofline"}
     del q, k, v, o, lse
 

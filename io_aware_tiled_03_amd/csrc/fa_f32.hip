@@ -44,22 +44,26 @@ __device__ __forceinline__ bool kept(const Dropout& drop, int i, int j, int bh) 
     return drop.keep(w, j & 3);
 }
 
-// Forward: one wave = 64 / LPR query rows; keys in chunks of 8 (the chunk's
-// scores in registers, max, rescale, exp, accumulate).  The row reads have no
-// branch around them, so a chunk's reads are in flight together; 8 keys keep
-// them within the register budget (32 spilled at d = 128) and measured
-// fastest (the 1x1x256x64 forward 114 -> 77 us against chunks of 32 read
-// one key at a time).
-template <int D, int LPR>
-__global__ __launch_bounds__(64) void fwd_f32_kernel(
+// Forward: a workgroup of NS waves takes 64 / LPR query rows; wave w walks
+// the w-th of NS equal slices of the rows' key range, keys in chunks of 8
+// (the chunk's scores in registers, max, rescale, exp, accumulate), and the
+// NS partial (m, l, o) of each row are combined through LDS with the same
+// rescaling rule.  The row reads have no branch around them, so a chunk's
+// reads are in flight together; 8 keys keep them within the register budget
+// (32 spilled at d = 128) and measured fastest (the 1x1x256x64 forward 114 ->
+// 77 us against chunks of 32 read one key at a time).  The key split shortens
+// each wave's chain of dependent reads NS-fold.
+template <int D, int LPR, int NS>
+__global__ __launch_bounds__(64 * NS) void fwd_f32_kernel(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
     float* __restrict__ O, float* __restrict__ LSE, int BH, int N, float scale_log2, float tau,
     int causal, int window, int sinks, Dropout drop) {
     constexpr int RPW = 64 / LPR, DS = D / LPR, KC = 8;
-    const int lane = threadIdx.x;
+    __shared__ float s_o[NS][RPW][D], s_m[NS][RPW], s_l[NS][RPW];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int bh = (int)(blockIdx.x % BH);
     const int rt = (int)(blockIdx.x / BH);
-    const int row = rt * RPW + lane % RPW, c0 = (lane / RPW) * DS;
+    const int rr = lane % RPW, row = rt * RPW + rr, c0 = (lane / RPW) * DS;
     const size_t base = (size_t)bh * N * D;
     const bool live = row < N;
     float q[DS], o[DS];
@@ -73,7 +77,10 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(
     float m = neg_inf(), l = 0.f;
     const int last_row = min(N, rt * RPW + RPW) - 1;
     const int kend = causal ? last_row + 1 : N;
-    for (int k0 = 0; k0 < kend; k0 += KC) {
+    // this wave's slice of the keys, whole chunks
+    const int nch = (kend + KC - 1) / KC;
+    const int kb = KC * (nch * wave / NS), ke = min(kend, KC * (nch * (wave + 1) / NS));
+    for (int k0 = kb; k0 < ke; k0 += KC) {
         float s[KC];
         float mx = neg_inf();
         // Keys past kend read the row kend - 1 instead (their scores are
@@ -120,6 +127,31 @@ __global__ __launch_bounds__(64) void fwd_f32_kernel(
             }
         }
         m = mnew;
+    }
+    if constexpr (NS > 1) {   // combine the slices: rescale each to the largest m
+#pragma unroll
+        for (int c = 0; c < DS; ++c) s_o[wave][rr][c0 + c] = o[c];
+        if (c0 == 0) {
+            s_m[wave][rr] = m;
+            s_l[wave][rr] = l;
+        }
+        __syncthreads();
+        if (wave != 0) return;
+        float mm = neg_inf();
+#pragma unroll
+        for (int w = 0; w < NS; ++w) mm = fmaxf(mm, s_m[w][rr]);
+        l = 0.f;
+#pragma unroll
+        for (int c = 0; c < DS; ++c) o[c] = 0.f;
+#pragma unroll
+        for (int w = 0; w < NS; ++w) {
+            const float mw = s_m[w][rr];
+            const float a = mw == neg_inf() ? 0.f : fast_exp2((mw - mm) * scale_log2);
+            l = __builtin_fmaf(a, s_l[w][rr], l);
+#pragma unroll
+            for (int c = 0; c < DS; ++c) o[c] = __builtin_fmaf(a, s_o[w][rr][c0 + c], o[c]);
+        }
+        m = mm;
     }
     if (live) {
         const float inv = (drop.thr > 0 ? drop.scale : 1.f) / l;
@@ -299,13 +331,17 @@ Dropout make_drop(int thr, unsigned long long seed, unsigned int offset) {
 // causal 1x4x1024x128 forward 0.65 -> 0.46 ms and backward 1.76 -> 0.82 ms;
 // 16 lanes per row was slower at 2x8x2048x64.
 constexpr int kFwdLPR = 8, kDqLPR = 8, kDkvLPR = 8;
+// Waves per forward workgroup, each taking a slice of the key range: 8
+// measured fastest (1x1x256x64 forward 77 -> 23 us with 4, 15 us with 8;
+// causal 1x4x1024x128 0.33 -> 0.10 ms).
+constexpr int kFwdSplit = 8;
 
 template <int D>
 void fwd_d(const FwdArgs& a, hipStream_t st) {
     constexpr int RPW = 64 / kFwdLPR;
     const int bh = a.B * a.H;
     const int nt = (a.N + RPW - 1) / RPW;
-    hipLaunchKernelGGL((fwd_f32_kernel<D, kFwdLPR>), dim3(nt * bh), dim3(64), 0, st,
+    hipLaunchKernelGGL((fwd_f32_kernel<D, kFwdLPR, kFwdSplit>), dim3(nt * bh), dim3(64 * kFwdSplit), 0, st,
                        (const float*)a.q, (const float*)a.k, (const float*)a.v, (float*)a.o, a.lse,
                        bh, a.N, a.tau * kLog2e, a.tau, a.causal, a.window, a.sinks,
                        make_drop(a.drop_thr, a.seed, a.offset));
