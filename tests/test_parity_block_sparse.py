@@ -203,16 +203,18 @@ def _check_bwd_heads(x, tau, causal, mask, blk, g, label):
 
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_block_sparse_bwd_split_long_lists(d, causal):
+@pytest.mark.parametrize("N,blk", [(2048, 64), (2000, 32)])
+def test_block_sparse_bwd_split_long_lists(N, blk, d, causal):
     """A global key block makes key tile 0's list of query tiles (32 of them
-    at N = 2048) several times longer than the others (about 4): with the
-    split workspace its dK/dV is computed in parts by several workgroups and
-    summed by the last part.  Checked against the oracle, bit-identical over
-    two calls, and against the same call with a D-only workspace (every list
-    walked whole), which must agree within the bounds."""
+    at N = 2048; N = 2000 leaves a ragged last tile) several times longer than
+    the others: with the split workspace its dK/dV is computed in parts by
+    several workgroups and summed by the last part.  Checked against the
+    oracle, bit-identical over two calls, and against the same call with a
+    D-only workspace (every list walked whole), which must agree within the
+    bounds."""
     import io_aware_tiled_03_amd as fa
-    B, H, N, blk = 1, 2, 2048, 64
-    x = fa_inputs.dense_inputs(B, H, N, d, "bf16", 23000 + d + causal, with_do=True)
+    B, H = 1, 2
+    x = fa_inputs.dense_inputs(B, H, N, d, "bf16", 23000 + N + d + causal, with_do=True)
     tau = 1.0 / np.sqrt(d)
     mask = _global_band_mask(H, N, blk, causal)
     split = _bwd_with_workspace(x, tau, causal, mask, blk, fa.bwd_block_sparse_workspace_bytes(B, H, N, d))
