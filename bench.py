@@ -400,11 +400,16 @@ def bench_extra(fa, reps=50):
     ms = med(lambda: fa.fwd(q, k, v, 1 / math.sqrt(d), True, o, lse, block_mask=bm,
                             block_size=(bs, bs)))
     fl = 4.0 * B * H * d * pairs
+    # at this density the binding roofline is HBM: Q, K, V read and O, LSE written once
+    # (538 MB, 67 us at 8 TB/s) outweigh the products (86 GFLOP, 34 us at 2.5 PFLOP/s)
+    nbytes = 4.0 * B * H * N * d * 2 + B * H * N * 4
     out["block_sparse_prefill"] = {"shape": [B, H, N, d], "block": [bs, bs],
                                    "pattern": "band +-1 block and global first key block, causal",
                                    "density": round(pairs / (N * (N + 1) / 2), 4), "ms": ms,
                                    "TFLOP/s": round(fl / ms / 1e9, 2),
-                                   "frac_mfma_bf16": round(fl / ms / 1e-3 / PEAK_MFMA_BF16, 4)}
+                                   "frac_mfma_bf16": round(fl / ms / 1e-3 / PEAK_MFMA_BF16, 4),
+                                   "GB/s": round(nbytes / ms / 1e6, 1),
+                                   "frac_hbm": round(nbytes / ms / 1e-3 / PEAK_HBM, 4)}
     # its backward, with the workspace that lets the global key block's long
     # list of query tiles be split over several workgroups
     sws = torch.empty(fa.bwd_block_sparse_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
