@@ -265,6 +265,76 @@ def time_events(fn, reps, warmup=10):
     return [a.elapsed_time(b) for a, b in ev]
 
 
+def rate_under_load(run, flops, seconds=1.2):
+    """TFLOP/s of `run` called back to back for about `seconds` (the second half timed with
+    HIP events, after the first half brought the clock to its level under this load), with
+    the sclk level sampled throughout."""
+    import torch
+    samples, stop = [], threading.Event()
+
+    def sampler():
+        while not stop.is_set():
+            v = read_sclk_mhz()
+            if v is not None:
+                samples.append(v)
+            time.sleep(0.01)
+    t = threading.Thread(target=sampler, daemon=True)
+    t.start()
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds / 2:
+        run()
+        torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 0
+    e0.record(stream)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds / 2:
+        run()
+        n += 1
+        torch.cuda.synchronize()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    stop.set()
+    t.join()
+    ms = e0.elapsed_time(e1) / n
+    s = sorted(samples)
+    return {"TFLOP/s": round(flops / ms / 1e9, 1), "frac_of_nominal": round(flops / ms / 1e-3 / PEAK_MFMA_BF16, 4),
+            "ms_per_call": round(ms, 4), "sclk_mhz_median": s[len(s) // 2] if s else None}
+
+
+def ceilings(fa, headline_tflops, seconds=1.2):
+    """Rates this part reaches on synthetic matrix-core loops with a given mix of work per
+    bf16 product (fa_calib.h), and on the vendor library's bf16 GEMM, each timed under its
+    own load; the headline kernel's rate as a fraction of each."""
+    import torch
+    g = torch.Generator().manual_seed(7)
+    seed = (torch.randn(fa.CALIB_SEED_BYTES // 2, generator=g) * 0.5).to(torch.bfloat16).cuda()
+    grid, iters = 2048, 2000
+    out = torch.empty(grid * 256, device="cuda")
+    res = {"note": "synthetic loops (no HBM traffic, barriers or masking): what the part reaches "
+                   "for each mix of work per 32x32x16 bf16 product; the headline's kernel issues "
+                   "one 1 KB LDS operand read, one exp2 and about four other vector "
+                   "instructions per product",
+           "mixes": []}
+    for mix, name in enumerate(fa.calib_mixes()):
+        r = rate_under_load(lambda: fa.calib_mfma(mix, grid, iters, seed, out),
+                            fa.calib_flops(mix, grid, iters), seconds)
+        r = {"mix": name, **r, "headline_fraction_of_this": round(headline_tflops / r["TFLOP/s"], 4)}
+        res["mixes"].append(r)
+    del seed, out
+    n = 8192
+    a = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(n, n, device="cuda", dtype=torch.bfloat16)
+    c = torch.empty(n, n, device="cuda", dtype=torch.bfloat16)
+    r = rate_under_load(lambda: torch.matmul(a, b, out=c), 2.0 * n ** 3, seconds)
+    res["library_gemm"] = {"op": "torch.matmul bf16 8192 x 8192 x 8192 (vendor BLAS)", **r,
+                           "headline_fraction_of_this": round(headline_tflops / r["TFLOP/s"], 4)}
+    del a, b, c
+    torch.cuda.empty_cache()
+    return res
+
+
 def upload(ht, dev="cuda"):
     """HostTensor -> GPU tensor with exactly the same bits."""
     import torch
@@ -608,6 +678,10 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-extra", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the synthetic matrix-core ceilings and the library GEMM")
+    ap.add_argument("--ceiling-seconds", type=float, default=1.2,
+                    help="run time of each ceiling measurement (half of it timed)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="only run a plain device-to-device copy of MIB MiB five times "
                          "(scales the HBM byte counters of a profiler run) and exit")
@@ -713,6 +787,8 @@ def main(argv=None):
     }
     del q, k, v, o, lse
     torch.cuda.empty_cache()
+    if not args.no_ceilings:
+        line["ceilings"] = ceilings(fa, achieved, args.ceiling_seconds)
     gpu_extra = None
     if not args.no_extra:
         line["also_measured"], gpu_extra = bench_extra(fa)

@@ -57,6 +57,15 @@ SIGNATURES = {
     "fa_status_string": (ctypes.c_char_p, [_I]),
 }
 
+# (name, restype, argtypes) of every symbol that fa_calib.h declares (measurement aid, not
+# part of the attention path).
+CALIB_SIGNATURES = {
+    "fa_calib_mix_count": (_I, []),
+    "fa_calib_mix_name": (ctypes.c_char_p, [_I]),
+    "fa_calib_flops": (ctypes.c_double, [_I, _I, _I]),
+    "fa_calib_mfma": (_I, [_I, _I, _I, _P, _P, _P]),
+}
+
 _lib = None
 
 
@@ -74,7 +83,7 @@ def lib():
             raise RuntimeError("libfa.so is not built at %s; run "
                                "`python -m io_aware_tiled_03_amd.build`" % LIB_PATH)
         handle = ctypes.CDLL(LIB_PATH)
-        for name, (res, args) in SIGNATURES.items():
+        for name, (res, args) in list(SIGNATURES.items()) + list(CALIB_SIGNATURES.items()):
             fn = getattr(handle, name)
             fn.restype, fn.argtypes = res, args
         _lib = handle
@@ -391,3 +400,31 @@ def bwd(q, k, v, o, lse, do, tau=None, causal=False, dq=None, dk=None, dv=None, 
     else:
         check("fa_bwd_stage", lib().fa_bwd_stage(int(stage), *args))
     return dq, dk, dv
+
+
+CALIB_SEED_BYTES = 65536
+
+
+def calib_mixes():
+    """Descriptions of the synthetic matrix-core mixes (fa_calib.h), by id."""
+    L = lib()
+    return [L.fa_calib_mix_name(i).decode() for i in range(L.fa_calib_mix_count())]
+
+
+def calib_flops(mix, grid, iters):
+    return lib().fa_calib_flops(int(mix), int(grid), int(iters))
+
+
+def calib_mfma(mix, grid, iters, seed, out):
+    """One launch of synthetic mix `mix` on the current stream (fa_calib_mfma).
+
+    seed: a device tensor of at least 64 KB (any bf16 values); out: a float32
+    device tensor of grid * 256 elements."""
+    import torch
+    if seed.numel() * seed.element_size() < CALIB_SEED_BYTES or not seed.is_contiguous():
+        raise ValueError("seed must be a contiguous tensor of at least %d bytes" % CALIB_SEED_BYTES)
+    _expect(out, "out", (int(grid) * 256,), torch.float32)
+    _same_gpu([("seed", seed), ("out", out)])
+    check("fa_calib_mfma", lib().fa_calib_mfma(int(mix), int(grid), int(iters), seed.data_ptr(),
+                                               out.data_ptr(), _stream(out)))
+    return out

@@ -27,7 +27,7 @@ OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
 SOURCES = ["fa_api.cpp", "fa_plan.cpp", "fa_fwd.hip", "fa_f32.hip", "fa_decode.hip", "fa_bwd.hip",
-           "fa_noalloc.hip"]
+           "fa_noalloc.hip", "fa_calib.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17", "-Wall",
          "-Wno-unused-command-line-argument",

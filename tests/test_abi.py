@@ -17,8 +17,8 @@ def _lib():
     return fa, fa.lib()
 
 
-def _declared():
-    text = open(os.path.join(ROOT, "include", "fa.h")).read()
+def _declared(header="fa.h"):
+    text = open(os.path.join(ROOT, "include", header)).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
 
@@ -26,12 +26,36 @@ def _declared():
 def test_header_declares_the_binding_symbols():
     import io_aware_tiled_03_amd as fa
     assert _declared() == sorted(fa.SIGNATURES)
+    assert _declared("fa_calib.h") == sorted(fa.CALIB_SIGNATURES)
+
+
+def test_every_header_is_covered():
+    assert sorted(os.listdir(os.path.join(ROOT, "include"))) == ["fa.h", "fa_calib.h"]
 
 
 def test_library_exports_every_declared_symbol():
     fa, lib = _lib()
-    for name in _declared():
+    for name in _declared() + _declared("fa_calib.h"):
         assert hasattr(lib, name), name
+
+
+def test_calib_host_checks():
+    """The synthetic-mix entry point validates its arguments before launching."""
+    fa, lib = _lib()
+    n = lib.fa_calib_mix_count()
+    assert n >= 2
+    assert all(lib.fa_calib_mix_name(i) for i in range(n))
+    assert lib.fa_calib_mix_name(n) is None and lib.fa_calib_mix_name(-1) is None
+    # mix 0: one wave per SIMD, 8 chains; 4 waves x iters x 8 x 32768 per workgroup
+    assert lib.fa_calib_flops(0, 2, 10) == 2 * 4 * 10 * 8 * 32768.0
+    assert lib.fa_calib_flops(n, 2, 10) == 0.0
+    assert lib.fa_calib_mfma(0, 1, 2, None, P, None) == 1
+    assert lib.fa_calib_mfma(0, 1, 2, P + 8, P, None) == 6
+    assert lib.fa_calib_mfma(n, 1, 2, P, P, None) == 7
+    assert lib.fa_calib_mfma(0, 0, 2, P, P, None) == 7
+    assert lib.fa_calib_mfma(0, 65537, 2, P, P, None) == 7
+    assert lib.fa_calib_mfma(0, 1, 3, P, P, None) == 7
+    assert lib.fa_calib_mfma(0, 1, 0, P, P, None) == 7
 
 
 def test_status_strings():

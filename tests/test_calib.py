@@ -1,0 +1,34 @@
+"""The synthetic matrix-core loops of fa_calib.h (a measurement aid): every mix launches, its
+checksum output is finite, and two launches with the same seed data agree bit for bit."""
+import pytest
+
+pytestmark = pytest.mark.gpu
+
+
+def test_every_mix_runs_and_repeats():
+    import torch
+
+    import io_aware_tiled_03_amd as fa
+    g = torch.Generator().manual_seed(11)
+    seed = (torch.randn(fa.CALIB_SEED_BYTES // 2, generator=g) * 0.5).to(torch.bfloat16).cuda()
+    grid, iters = 8, 6
+    for mix, name in enumerate(fa.calib_mixes()):
+        print("calib mix", mix, name, flush=True)
+        a = fa.calib_mfma(mix, grid, iters, seed, torch.empty(grid * 256, device="cuda"))
+        b = fa.calib_mfma(mix, grid, iters, seed, torch.empty(grid * 256, device="cuda"))
+        torch.cuda.synchronize()
+        assert torch.isfinite(a).all(), name
+        assert torch.equal(a, b), name
+        assert fa.calib_flops(mix, grid, iters) > 0
+
+
+def test_binding_rejects_short_buffers():
+    import torch
+
+    import io_aware_tiled_03_amd as fa
+    seed = torch.zeros(fa.CALIB_SEED_BYTES // 2 - 8, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        fa.calib_mfma(0, 2, 2, seed, torch.empty(512, device="cuda"))
+    seed = torch.zeros(fa.CALIB_SEED_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        fa.calib_mfma(0, 2, 2, seed, torch.empty(511, device="cuda"))
