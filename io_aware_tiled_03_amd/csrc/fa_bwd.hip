@@ -45,6 +45,18 @@ __device__ __forceinline__ int kperm(int m) {
 
 template <int N_> using ic = std::integral_constant<int, N_>;
 
+// Row stride (elements) of the staged tiles: Q and dO in the dK/dV kernel, K and V in the dQ
+// kernel.  Each tile is read both ways: by rows (ds_read_b128, lane i -> row kperm(i)), which is
+// free of bank conflicts for any stride of 16 x odd bytes, and transposed (ds_read_b64_tr_b16,
+// four rows by 16 lanes), whose rate depends on the stride as well: measured on gfx950 with
+// eight waves per CU, 63 B per clock per CU at 272 bytes against 117 at 304 (and 234 for the row
+// reads at either).  d = 128 pads rows to 304 bytes (16 x 19): 3-5% on the d = 128 backward,
+// outputs unchanged.  d = 64 keeps 144 bytes (16 x 9), at which the transposing reads already run
+// at the 117 B per clock that no other 16 x odd stride improves.  The block-sparse kernels keep
+// 272 bytes: at 304 the block-sparse dQ kernel's two workgroups per CU would not fit the LDS.
+template <int D, bool BLK>
+constexpr int bwd_row_stride() { return (D == 128 && !BLK) ? D + 24 : D + 8; }
+
 // Direct global -> LDS staging of a tile of ROWS rows of a [N, D] bf16 matrix
 // into padded LDS rows of STR elements (STR*2 = 16 * odd bytes).  One wave
 // instruction fills 1 KB of LDS; every lane loads the 16-byte chunk that
@@ -217,7 +229,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     // the larger tile would cost occupancy or is unmeasured.
     constexpr int BC = 128, BR = (D == 64 && !BLK) ? 128 : 64;
     static_assert(!BLK || (BC == kBlkKeys && BR == 64), "the split plan counts 64-row query tiles of 128 keys");
-    constexpr int STR = D + 8;                 // padded row (16 * odd bytes)
+    constexpr int STR = bwd_row_stride<D, BLK>();
     // Without dropout, dS = P o (dP - D) takes -D as the starting accumulator
     // of the dP = dO V^T product, so the subtraction costs nothing; LDS then
     // holds -D.  (With dropout, dS = P o (Z o dP - D) scales dP alone.)  This
@@ -683,7 +695,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     constexpr bool CAUSAL = MODE == kMaskCausal || MODE == kMaskWindow || MODE == kMaskBlockCausal;
     constexpr bool WIN = MODE == kMaskWindow, BLK = MODE >= kMaskBlock;
     constexpr int BR = 128, BC = 64;
-    constexpr int STR = D + 8;
+    constexpr int STR = bwd_row_stride<D, BLK>();
     __shared__ __attribute__((aligned(16))) uint16_t sK0[BC * STR], sK1[BC * STR];
     __shared__ __attribute__((aligned(16))) uint16_t sV0[BC * STR], sV1[BC * STR];
     // block-sparse: the workgroup's active key tiles, in order
