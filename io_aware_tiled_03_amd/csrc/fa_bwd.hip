@@ -45,20 +45,23 @@ __device__ __forceinline__ int kperm(int m) {
 
 template <int N_> using ic = std::integral_constant<int, N_>;
 
-// Row stride (elements) of the staged tiles: Q and dO in the dK/dV kernel, K and V in the dQ
-// kernel.  Each tile is read both ways: by rows (ds_read_b128, lane i -> row kperm(i)), which is
-// free of bank conflicts for any stride of 16 x odd bytes, and transposed (ds_read_b64_tr_b16,
-// four rows by 16 lanes), whose rate depends on the stride as well: measured on gfx950 with
-// eight waves per CU, 63 B per clock per CU at 272 bytes against 117 at 304 (and 234 for the row
-// reads at either).  d = 128 pads rows to 304 bytes (16 x 19): 3-5% on the d = 128 backward,
-// outputs unchanged.  d = 64 keeps 144 bytes (16 x 9), at which the transposing reads already run
-// at the 117 B per clock that no other 16 x odd stride improves.  The block-sparse kernels keep
-// 272 bytes: at 304 the block-sparse dQ kernel's two workgroups per CU would not fit the LDS.
-template <int D, bool BLK>
-constexpr int bwd_row_stride() { return (D == 128 && !BLK) ? D + 24 : D + 8; }
+// Staged tiles (Q and dO in the dK/dV kernel, K and V in the dQ kernel) are read two ways: by
+// rows (ds_read_b128, lane i at row kperm(i), 16 lanes on 16 rows of one 16-row block) and
+// transposed (ds_read_b64_tr_b16, each 16-lane group on four consecutive rows, 64 bytes of each).
+// With rows padded to 16 x odd bytes the row reads are free of bank conflicts, but four
+// consecutive rows of the transposing reads fall on overlapping banks.  Logical row r is therefore
+// stored at physical row lds_row(r): inside each 16-row block the two 2-bit fields of r trade
+// places (r = 4a + b goes to 4b + a; the map is its own inverse), so the four consecutive logical
+// rows of a transposing read sit four physical rows apart (4 x 16 x odd bytes = 64 mod 256: the
+// four 64-byte pieces tile the banks), and the 16 rows of a row read still go to 16 distinct
+// physical rows of their block.  Measured on gfx950 (the two patterns alone, eight waves per CU):
+// transposing reads at 272-byte rows 64 B per clock per CU before, 168 after; at 144 bytes 117
+// before, conflict-free after; row reads 234 B per clock either way.
+__device__ __forceinline__ int lds_row(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
 
 // Direct global -> LDS staging of a tile of ROWS rows of a [N, D] bf16 matrix
-// into padded LDS rows of STR elements (STR*2 = 16 * odd bytes).  One wave
+// into padded LDS rows of STR elements (STR*2 = 16 * odd bytes), tile row r at LDS row
+// lds_row(r).  One wave
 // instruction fills 1 KB of LDS; every lane loads the 16-byte chunk that
 // belongs at its LDS position (padding positions load a duplicate chunk that
 // is never read).  Rows past N read as zeros through the buffer descriptor.
@@ -77,7 +80,8 @@ struct TileCopy {
         for (int t = 0; t < PW; ++t)
             if (wave + NWAVES * t < NI) {
                 const int pos = (wave + NWAVES * t) * 64 + lane, row = pos / CPR, c = pos % CPR;
-                const uint32_t off = (uint32_t)(row * D + (c < D / 8 ? c : 0) * 8) * 2;
+                // LDS row `row` holds tile row lds_row(row)
+                const uint32_t off = (uint32_t)(lds_row(row) * D + (c < D / 8 ? c : 0) * 8) * 2;
                 buf_ld16_lds(rs, off + t0, lds + (wave + NWAVES * t) * 512);
             }
     }
@@ -229,7 +233,7 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     // the larger tile would cost occupancy or is unmeasured.
     constexpr int BC = 128, BR = (D == 64 && !BLK) ? 128 : 64;
     static_assert(!BLK || (BC == kBlkKeys && BR == 64), "the split plan counts 64-row query tiles of 128 keys");
-    constexpr int STR = bwd_row_stride<D, BLK>();
+    constexpr int STR = D + 8;                 // padded row (16 * odd bytes)
     // Without dropout, dS = P o (dP - D) takes -D as the starting accumulator
     // of the dP = dO V^T product, so the subtraction costs nothing; LDS then
     // holds -D.  (With dropout, dS = P o (Z o dP - D) scales dP alone.)  This
@@ -298,11 +302,13 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
     TileCopy<BR, D, STR, 4> cp;
     cp.init(wave, lane);
     // operand read offsets: A operand rows (queries) in kperm order; transposed
-    // operands via the transposing read (lane s of 16-lane group G: row
-    // 8*(G/2) + s/4 (+4), column 16*(G%2) + 4*(s%4))
-    const int a_off = kperm(ln) * STR + hf * 8;
+    // operands via the transposing read (lane s of 16-lane group G: tile row
+    // 8*(G/2) + s/4, and +4 for the second read, column 16*(G%2) + 4*(s%4)).
+    // Physical rows through lds_row: tile row 8*(G/2) + s/4 (+ a multiple of 16)
+    // is LDS row 4*(s/4) + 2*(G/2), and the second read's row the next LDS row.
+    const int a_off = lds_row(kperm(ln)) * STR + hf * 8;
     const int G = lane >> 4, sl = lane & 15;
-    const int t_off = (8 * (G >> 1) + (sl >> 2)) * STR + 16 * (G & 1) + 4 * (sl & 3);
+    const int t_off = (4 * (sl >> 2) + 2 * (G >> 1)) * STR + 16 * (G & 1) + 4 * (sl & 3);
 
     const int n_qt = (N + BR - 1) / BR;
     const int qt0 = CAUSAL ? k0 / BR : 0;
@@ -402,8 +408,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                 u32x4 ot[D / 32], qt4[D / 32];
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    ot[db] = lds_read_tr16_x2(o_lds + tb + db * 32, o_lds + tb + db * 32 + 4 * STR);
-                    qt4[db] = lds_read_tr16_x2(q_lds + tb + db * 32, q_lds + tb + db * 32 + 4 * STR);
+                    ot[db] = lds_read_tr16_x2(o_lds + tb + db * 32, o_lds + tb + db * 32 + STR);
+                    qt4[db] = lds_read_tr16_x2(q_lds + tb + db * 32, q_lds + tb + db * 32 + STR);
                 }
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
@@ -516,8 +522,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                 u32x4 ot[D / 32], qt4[D / 32];
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    ot[db] = lds_read_tr16_x2(o_lds + tb + db * 32, o_lds + tb + db * 32 + 4 * STR);
-                    qt4[db] = lds_read_tr16_x2(q_lds + tb + db * 32, q_lds + tb + db * 32 + 4 * STR);
+                    ot[db] = lds_read_tr16_x2(o_lds + tb + db * 32, o_lds + tb + db * 32 + STR);
+                    qt4[db] = lds_read_tr16_x2(q_lds + tb + db * 32, q_lds + tb + db * 32 + STR);
                 }
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
@@ -695,7 +701,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     constexpr bool CAUSAL = MODE == kMaskCausal || MODE == kMaskWindow || MODE == kMaskBlockCausal;
     constexpr bool WIN = MODE == kMaskWindow, BLK = MODE >= kMaskBlock;
     constexpr int BR = 128, BC = 64;
-    constexpr int STR = bwd_row_stride<D, BLK>();
+    constexpr int STR = D + 8;
     __shared__ __attribute__((aligned(16))) uint16_t sK0[BC * STR], sK1[BC * STR];
     __shared__ __attribute__((aligned(16))) uint16_t sV0[BC * STR], sV1[BC * STR];
     // block-sparse: the workgroup's active key tiles, in order
@@ -747,9 +753,10 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
     const rsrc_t vrs = make_rsrc(V + base, (uint32_t)N * D * 2);
     TileCopy<BC, D, STR, 4> cp;
     cp.init(wave, lane);
-    const int a_off = kperm(ln) * STR + hf * 8;
+    // operand read offsets as in the dK/dV kernel (rows through lds_row)
+    const int a_off = lds_row(kperm(ln)) * STR + hf * 8;
     const int G = lane >> 4, sl = lane & 15;
-    const int t_off = (8 * (G >> 1) + (sl >> 2)) * STR + 16 * (G & 1) + 4 * (sl & 3);
+    const int t_off = (4 * (sl >> 2) + 2 * (G >> 1)) * STR + 16 * (G & 1) + 4 * (sl & 3);
 
     const int kend = CAUSAL ? min(N, q0 + BR) : N;
     const int ntiles = (kend + BC - 1) / BC;
@@ -825,7 +832,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
                 u32x4 kt4[D / 32];
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    kt4[db] = lds_read_tr16_x2(k_lds + tb + db * 32, k_lds + tb + db * 32 + 4 * STR);
+                    kt4[db] = lds_read_tr16_x2(k_lds + tb + db * 32, k_lds + tb + db * 32 + STR);
                 }
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) dqacc[db] = mfma32x32x16(kt4[db], dsf, dqacc[db]);
