@@ -335,6 +335,22 @@ def ceilings(fa, headline_tflops, seconds=1.2):
     return res
 
 
+def lds_patterns(fa, seconds=0.6):
+    """LDS read patterns of the kernels' operand reads, each alone (fa_calib.h): bytes per clock
+    per CU at the sampled sclk."""
+    import torch
+    grid, iters = 1024, 4000
+    out = torch.empty(grid * 512, dtype=torch.int32, device="cuda")
+    res = []
+    for pat, name in enumerate(fa.calib_lds_patterns()):
+        nbytes = fa.calib_lds_bytes(pat, grid, iters)
+        r = rate_under_load(lambda: fa.calib_lds(pat, grid, iters, out), nbytes, seconds)
+        ms, mhz = r["ms_per_call"], r["sclk_mhz_median"] or 2400.0
+        res.append({"pattern": name, "ms_per_call": ms, "sclk_mhz_median": mhz,
+                    "B_per_clk_per_CU": round(nbytes / (ms * 1e-3) / (mhz * 1e6) / 256, 1)})
+    return res
+
+
 def upload(ht, dev="cuda"):
     """HostTensor -> GPU tensor with exactly the same bits."""
     import torch
@@ -680,6 +696,9 @@ def main(argv=None):
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-ceilings", action="store_true",
                     help="skip the synthetic matrix-core ceilings and the library GEMM")
+    ap.add_argument("--lds-patterns", action="store_true",
+                    help="only time the kernels' LDS read patterns alone (fa_calib.h), print one "
+                         "JSON line and exit")
     ap.add_argument("--ceiling-seconds", type=float, default=1.2,
                     help="run time of each ceiling measurement (half of it timed)")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -724,6 +743,10 @@ def main(argv=None):
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": n, "launches": 5}))
+        return 0
+
+    if args.lds_patterns:
+        print(json.dumps({"lds_patterns": lds_patterns(fa)}))
         return 0
 
     w = fa_inputs.WORKLOADS[3]

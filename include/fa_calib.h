@@ -10,7 +10,9 @@
  * arithmetic) issued between products all take their share.  Each mix below
  * runs one such combination with nothing else in the loop, so its rate is
  * measured on the same part, under the same clock behaviour, as the kernel it
- * is compared with.  None of this is part of the attention path.
+ * is compared with.  A second set runs the kernels' LDS read patterns alone,
+ * which is how their row layouts were chosen.  None of this is part of the
+ * attention path.
  *
  * Conventions follow fa.h (fa_status results, device pointers, stream).
  */
@@ -47,6 +49,26 @@ double fa_calib_flops(int mix, int grid, int iters);
  * (FA_ERR_ARG otherwise, also for an unknown mix); FA_ERR_NULL, FA_ERR_ALIGN
  * for bad pointers; FA_ERR_HIP for a launch error. */
 fa_status fa_calib_mfma(int mix, int grid, int iters, const void* seed, float* out, void* stream);
+
+/* LDS read patterns of the kernels' operand reads, each run alone (eight waves
+ * per workgroup, 64-row tiles): row reads (ds_read_b128 in the kernels' row
+ * order) and transposing reads (ds_read_b64_tr_b16) at several row strides, with
+ * and without the backward kernels' row permutation.  Count and descriptions: */
+int fa_calib_lds_count(void);
+const char* fa_calib_lds_name(int pattern);   /* NULL when out of range */
+
+/* LDS bytes that one fa_calib_lds(pattern, grid, iters, ...) launch reads; 0 for
+ * an invalid pattern, grid < 1 or iters < 1. */
+double fa_calib_lds_bytes(int pattern, int grid, int iters);
+
+/* Enqueues one launch of LDS read pattern `pattern`: `grid` workgroups of eight
+ * waves, `iters` steps of eight reads per wave.
+ * out : device pointer, 16-byte aligned, to grid * 512 unsigned ints (a
+ *       checksum per lane; overwritten).
+ * grid in [1, FA_CALIB_MAX_GRID], iters in [1, FA_CALIB_MAX_ITERS] (FA_ERR_ARG
+ * otherwise, also for an unknown pattern); FA_ERR_NULL, FA_ERR_ALIGN for a bad
+ * pointer; FA_ERR_HIP for a launch error. */
+fa_status fa_calib_lds(int pattern, int grid, int iters, unsigned int* out, void* stream);
 
 #ifdef __cplusplus
 }

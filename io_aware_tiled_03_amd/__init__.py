@@ -64,6 +64,10 @@ CALIB_SIGNATURES = {
     "fa_calib_mix_name": (ctypes.c_char_p, [_I]),
     "fa_calib_flops": (ctypes.c_double, [_I, _I, _I]),
     "fa_calib_mfma": (_I, [_I, _I, _I, _P, _P, _P]),
+    "fa_calib_lds_count": (_I, []),
+    "fa_calib_lds_name": (ctypes.c_char_p, [_I]),
+    "fa_calib_lds_bytes": (ctypes.c_double, [_I, _I, _I]),
+    "fa_calib_lds": (_I, [_I, _I, _I, _P, _P]),
 }
 
 _lib = None
@@ -427,4 +431,25 @@ def calib_mfma(mix, grid, iters, seed, out):
     _same_gpu([("seed", seed), ("out", out)])
     check("fa_calib_mfma", lib().fa_calib_mfma(int(mix), int(grid), int(iters), seed.data_ptr(),
                                                out.data_ptr(), _stream(out)))
+    return out
+
+
+def calib_lds_patterns():
+    """Descriptions of the LDS read patterns (fa_calib.h), by id."""
+    L = lib()
+    return [L.fa_calib_lds_name(i).decode() for i in range(L.fa_calib_lds_count())]
+
+
+def calib_lds_bytes(pattern, grid, iters):
+    return lib().fa_calib_lds_bytes(int(pattern), int(grid), int(iters))
+
+
+def calib_lds(pattern, grid, iters, out):
+    """One launch of LDS read pattern `pattern` on the current stream (fa_calib_lds);
+    out: an int32 device tensor of grid * 512 elements."""
+    import torch
+    _expect(out, "out", (int(grid) * 512,), torch.int32)
+    _same_gpu([("out", out)])
+    check("fa_calib_lds", lib().fa_calib_lds(int(pattern), int(grid), int(iters), out.data_ptr(),
+                                             _stream(out)))
     return out

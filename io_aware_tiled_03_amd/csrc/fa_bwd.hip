@@ -54,9 +54,9 @@ template <int N_> using ic = std::integral_constant<int, N_>;
 // places (r = 4a + b goes to 4b + a; the map is its own inverse), so the four consecutive logical
 // rows of a transposing read sit four physical rows apart (4 x 16 x odd bytes = 64 mod 256: the
 // four 64-byte pieces tile the banks), and the 16 rows of a row read still go to 16 distinct
-// physical rows of their block.  Measured on gfx950 (the two patterns alone, eight waves per CU):
-// transposing reads at 272-byte rows 64 B per clock per CU before, 168 after; at 144 bytes 117
-// before, conflict-free after; row reads 234 B per clock either way.
+// physical rows of their block.  Measured on gfx950 with the two patterns alone (fa_calib_lds,
+// eight waves per workgroup): transposing reads at 272-byte rows 63 B per clock per CU before,
+// about 180 after; at 144-byte rows 120 before, about 185 after; row reads about 235 either way.
 __device__ __forceinline__ int lds_row(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
 
 // Direct global -> LDS staging of a tile of ROWS rows of a [N, D] bf16 matrix

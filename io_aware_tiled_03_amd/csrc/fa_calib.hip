@@ -135,3 +135,115 @@ extern "C" fa_status fa_calib_mfma(int mix, int grid, int iters, const void* see
     kMixes[mix].launch(grid, static_cast<const uint4*>(seed), out, iters, static_cast<hipStream_t>(stream));
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
+
+// ---------------------------------------------------------------------------
+// LDS read patterns of the attention kernels' operand reads, each alone: eight
+// waves per workgroup read one pattern eight times per step from a 64-row tile
+// of `stride`-byte rows.  Row reads: ds_read_b128, lane i at row kperm(i % 32)
+// (the kernels' row order), 16 bytes at column 16 * (i / 32) (+32 per read).
+// Transposing reads: ds_read_b64_tr_b16, lane s of 16-lane group G at row
+// 8 * (G / 2) + s / 4, column 32 * (G % 2) + 8 * (s % 4) bytes (+64 per read),
+// and the second read of each pair four rows on; with SPACED, the rows go
+// through the backward kernels' permutation inside each 16-row block (tile row
+// 4a + b at LDS row 4b + a).
+
+namespace {
+
+__device__ __forceinline__ int cal_kperm(int m) {
+    const int j = 4 * (m >> 3) + (m & 3);
+    return 16 * (j >> 3) + 8 * ((m >> 2) & 1) + (j & 7);
+}
+__device__ __forceinline__ int cal_spaced(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
+
+typedef short cal_v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) cal_v4i16 cal_lds_v4i16;
+
+template <bool TR, bool SPACED, int STRIDE, int D>
+__global__ __launch_bounds__(512) void calib_lds_kernel(uint32_t* __restrict__ out, int iters) {
+    __shared__ __attribute__((aligned(16))) unsigned char tile[64 * STRIDE + 256];
+    const int lane = threadIdx.x & 63;
+    for (int i = threadIdx.x; i < (64 * STRIDE + 256) / 4; i += 512)
+        reinterpret_cast<uint32_t*>(tile)[i] = (uint32_t)i * 2654435761u;
+    __syncthreads();
+    const int G = lane >> 4, sl = lane & 15;
+    int off;
+    if constexpr (TR) {
+        // tile rows r0 + s/4 and r0 + 4 + s/4: LDS rows 4*(s/4) + r0/4 (+1) when spaced
+        off = (SPACED ? 4 * (sl >> 2) + 2 * (G >> 1) : 8 * (G >> 1) + (sl >> 2)) * STRIDE + 32 * (G & 1) + 8 * (sl & 3);
+    } else {
+        const int r = cal_kperm(lane & 31);
+        off = (SPACED ? cal_spaced(r) : r) * STRIDE + 16 * (lane >> 5);
+    }
+    uint32_t acc = 0;
+    for (int it = 0; it < iters; ++it) {
+        int o = off;
+        asm volatile("" : "+v"(o));   // the address is opaque: every step reads again
+        const unsigned char* base = tile + o;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            if constexpr (TR) {
+                constexpr int NC = D / 32;   // 64-byte column groups per row
+                const int hi = (r / NC) * (SPACED ? 1 : 4) * STRIDE;
+                const cal_v4i16 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((cal_lds_v4i16*)(base + (r % NC) * 64 + hi));
+                acc += (uint32_t)(uint16_t)v.x ^ ((uint32_t)(uint16_t)v.y << 16) ^ (uint32_t)(uint16_t)v.z ^
+                       ((uint32_t)(uint16_t)v.w << 16);
+            } else {
+                constexpr int NC = D / 16;   // 32-byte column steps per row
+                const uint4 v = *reinterpret_cast<const uint4*>(base + (r % NC) * 32 + (r / NC) * 32 * STRIDE);
+                acc += v.x ^ v.y ^ v.z ^ v.w;
+            }
+        }
+    }
+    out[blockIdx.x * 512 + threadIdx.x] = acc;
+}
+
+struct LdsPattern {
+    const char* name;
+    int bytes_per_read;   // per wave
+    void (*launch)(int grid, uint32_t* out, int iters, hipStream_t st);
+};
+
+template <bool TR, bool SPACED, int STRIDE, int D>
+void launch_lds(int grid, uint32_t* out, int iters, hipStream_t st) {
+    calib_lds_kernel<TR, SPACED, STRIDE, D><<<grid, 512, 0, st>>>(out, iters);
+}
+
+const LdsPattern kLds[] = {
+    {"row reads, 272-byte rows (d=128)", 1024, launch_lds<false, false, 272, 128>},
+    {"row reads, 288-byte rows (d=128)", 1024, launch_lds<false, false, 288, 128>},
+    {"row reads, 320-byte rows (d=128)", 1024, launch_lds<false, false, 320, 128>},
+    {"row reads, 272-byte rows, rows permuted (d=128)", 1024, launch_lds<false, true, 272, 128>},
+    {"transposing reads, 272-byte rows (d=128)", 512, launch_lds<true, false, 272, 128>},
+    {"transposing reads, 288-byte rows (d=128)", 512, launch_lds<true, false, 288, 128>},
+    {"transposing reads, 304-byte rows (d=128)", 512, launch_lds<true, false, 304, 128>},
+    {"transposing reads, 320-byte rows (d=128)", 512, launch_lds<true, false, 320, 128>},
+    {"transposing reads, 272-byte rows, rows permuted (d=128)", 512, launch_lds<true, true, 272, 128>},
+    {"row reads, 144-byte rows (d=64)", 1024, launch_lds<false, false, 144, 64>},
+    {"transposing reads, 144-byte rows (d=64)", 512, launch_lds<true, false, 144, 64>},
+    {"transposing reads, 144-byte rows, rows permuted (d=64)", 512, launch_lds<true, true, 144, 64>},
+};
+constexpr int kNumLds = sizeof(kLds) / sizeof(kLds[0]);
+
+}  // namespace
+
+extern "C" int fa_calib_lds_count(void) { return kNumLds; }
+
+extern "C" const char* fa_calib_lds_name(int pattern) {
+    return (pattern >= 0 && pattern < kNumLds) ? kLds[pattern].name : nullptr;
+}
+
+extern "C" double fa_calib_lds_bytes(int pattern, int grid, int iters) {
+    if (pattern < 0 || pattern >= kNumLds || grid < 1 || iters < 1) return 0.0;
+    // 8 waves per workgroup, 8 reads per step
+    return (double)grid * 8.0 * (double)iters * 8.0 * kLds[pattern].bytes_per_read;
+}
+
+extern "C" fa_status fa_calib_lds(int pattern, int grid, int iters, unsigned int* out, void* stream) {
+    if (!out) return FA_ERR_NULL;
+    if ((uintptr_t)out & 15) return FA_ERR_ALIGN;
+    if (pattern < 0 || pattern >= kNumLds || grid < 1 || grid > FA_CALIB_MAX_GRID || iters < 1 ||
+        iters > FA_CALIB_MAX_ITERS)
+        return FA_ERR_ARG;
+    kLds[pattern].launch(grid, reinterpret_cast<uint32_t*>(out), iters, static_cast<hipStream_t>(stream));
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}

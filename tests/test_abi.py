@@ -56,6 +56,16 @@ def test_calib_host_checks():
     assert lib.fa_calib_mfma(0, 65537, 2, P, P, None) == 7
     assert lib.fa_calib_mfma(0, 1, 3, P, P, None) == 7
     assert lib.fa_calib_mfma(0, 1, 0, P, P, None) == 7
+    m = lib.fa_calib_lds_count()
+    assert m >= 2 and all(lib.fa_calib_lds_name(i) for i in range(m))
+    assert lib.fa_calib_lds_name(m) is None
+    # pattern 0: row reads, 1 KB per wave read; 8 waves x 8 reads per step
+    assert lib.fa_calib_lds_bytes(0, 3, 5) == 3 * 8 * 5 * 8 * 1024.0
+    assert lib.fa_calib_lds(0, 1, 1, None, None) == 1
+    assert lib.fa_calib_lds(0, 1, 1, P + 4, None) == 6
+    assert lib.fa_calib_lds(m, 1, 1, P, None) == 7
+    assert lib.fa_calib_lds(0, 0, 1, P, None) == 7
+    assert lib.fa_calib_lds(0, 1, 0, P, None) == 7
 
 
 def test_status_strings():

@@ -1,5 +1,6 @@
-"""The synthetic matrix-core loops of fa_calib.h (a measurement aid): every mix launches, its
-checksum output is finite, and two launches with the same seed data agree bit for bit."""
+"""The synthetic loops of fa_calib.h (a measurement aid): every matrix-core mix and every LDS
+read pattern launches, and two launches with the same data agree bit for bit (the matrix-core
+checksums are also finite)."""
 import pytest
 
 pytestmark = pytest.mark.gpu
@@ -20,6 +21,20 @@ def test_every_mix_runs_and_repeats():
         assert torch.isfinite(a).all(), name
         assert torch.equal(a, b), name
         assert fa.calib_flops(mix, grid, iters) > 0
+
+
+def test_every_lds_pattern_runs_and_repeats():
+    import torch
+
+    import io_aware_tiled_03_amd as fa
+    grid, iters = 4, 3
+    for pat, name in enumerate(fa.calib_lds_patterns()):
+        print("calib lds pattern", pat, name, flush=True)
+        a = fa.calib_lds(pat, grid, iters, torch.empty(grid * 512, dtype=torch.int32, device="cuda"))
+        b = fa.calib_lds(pat, grid, iters, torch.empty(grid * 512, dtype=torch.int32, device="cuda"))
+        torch.cuda.synchronize()
+        assert torch.equal(a, b), name
+        assert fa.calib_lds_bytes(pat, grid, iters) > 0
 
 
 def test_binding_rejects_short_buffers():
