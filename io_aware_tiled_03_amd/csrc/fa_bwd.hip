@@ -57,18 +57,37 @@ template <int N_> using ic = std::integral_constant<int, N_>;
 // physical rows of their block.  Measured on gfx950 with the two patterns alone (fa_calib_lds,
 // eight waves per workgroup): transposing reads at 272-byte rows 63 B per clock per CU before,
 // about 180 after; at 144-byte rows 120 before, about 185 after; row reads about 235 either way.
-__device__ __forceinline__ int lds_row(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
+// The block-sparse kernels keep plain row order (PERM = false): their few, scattered query or key
+// tiles measured 2.5% slower with the permutation (the 1x32x16384x128 band-and-global backward,
+// 0.739 -> 0.759 ms), while the dense and window backward gained.
+template <bool PERM>
+__device__ __forceinline__ int lds_row(int r) {
+    return PERM ? (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3) : r;
+}
+// Per-lane offsets (elements) of the operand reads.  Row reads: tile row kperm(lane % 32), column
+// 8 * (lane / 32).  Transposing reads (lane s of 16-lane group G): tile row 8*(G/2) + s/4, and
+// four rows on for the second read of a pair, column 16*(G%2) + 4*(s%4); with the permutation that
+// tile row (plus a multiple of 16) is LDS row 4*(s/4) + 2*(G/2), and the second read's row the next
+// LDS row.
+template <bool PERM, int STR>
+__device__ __forceinline__ int row_read_off(int lane) { return lds_row<PERM>(kperm(lane & 31)) * STR + (lane >> 5) * 8; }
+template <bool PERM, int STR>
+__device__ __forceinline__ int tr_read_off(int lane) {
+    const int G = lane >> 4, sl = lane & 15;
+    return (PERM ? 4 * (sl >> 2) + 2 * (G >> 1) : 8 * (G >> 1) + (sl >> 2)) * STR + 16 * (G & 1) + 4 * (sl & 3);
+}
+template <bool PERM, int STR>
+constexpr int tr_second_row() { return PERM ? STR : 4 * STR; }
 
 // Direct global -> LDS staging of a tile of ROWS rows of a [N, D] bf16 matrix
 // into padded LDS rows of STR elements (STR*2 = 16 * odd bytes), tile row r at LDS row
-// lds_row(r).  One wave
-// instruction fills 1 KB of LDS; every lane loads the 16-byte chunk that
+// lds_row<PERM>(r).  One wave instruction fills 1 KB of LDS; every lane loads the 16-byte chunk that
 // belongs at its LDS position (padding positions load a duplicate chunk that
 // is never read).  Rows past N read as zeros through the buffer descriptor.
 // The byte offsets are recomputed at each issue (a few integer operations):
 // held in an array inside the struct, which the kernels' lambdas capture by
 // reference, they were kept in scratch memory in some variants.
-template <int ROWS, int D, int STR, int NWAVES>
+template <int ROWS, int D, int STR, int NWAVES, bool PERM>
 struct TileCopy {
     static constexpr int CPR = STR / 8, NI = ROWS * CPR / 64, PW = (NI + NWAVES - 1) / NWAVES;
     static_assert(ROWS * CPR % 64 == 0, "whole wave instructions");
@@ -80,8 +99,8 @@ struct TileCopy {
         for (int t = 0; t < PW; ++t)
             if (wave + NWAVES * t < NI) {
                 const int pos = (wave + NWAVES * t) * 64 + lane, row = pos / CPR, c = pos % CPR;
-                // LDS row `row` holds tile row lds_row(row)
-                const uint32_t off = (uint32_t)(lds_row(row) * D + (c < D / 8 ? c : 0) * 8) * 2;
+                // LDS row `row` holds tile row lds_row(row) (the map is its own inverse)
+                const uint32_t off = (uint32_t)(lds_row<PERM>(row) * D + (c < D / 8 ? c : 0) * 8) * 2;
                 buf_ld16_lds(rs, off + t0, lds + (wave + NWAVES * t) * 512);
             }
     }
@@ -299,16 +318,13 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
 
     const rsrc_t qrs = make_rsrc(Q + base, (uint32_t)N * D * 2);
     const rsrc_t ors = make_rsrc(dO + base, (uint32_t)N * D * 2);
-    TileCopy<BR, D, STR, 4> cp;
+    TileCopy<BR, D, STR, 4, !BLK> cp;
     cp.init(wave, lane);
     // operand read offsets: A operand rows (queries) in kperm order; transposed
-    // operands via the transposing read (lane s of 16-lane group G: tile row
-    // 8*(G/2) + s/4, and +4 for the second read, column 16*(G%2) + 4*(s%4)).
-    // Physical rows through lds_row: tile row 8*(G/2) + s/4 (+ a multiple of 16)
-    // is LDS row 4*(s/4) + 2*(G/2), and the second read's row the next LDS row.
-    const int a_off = lds_row(kperm(ln)) * STR + hf * 8;
-    const int G = lane >> 4, sl = lane & 15;
-    const int t_off = (4 * (sl >> 2) + 2 * (G >> 1)) * STR + 16 * (G & 1) + 4 * (sl & 3);
+    // operands via the transposing read
+    const int a_off = row_read_off<!BLK, STR>(lane);
+    const int t_off = tr_read_off<!BLK, STR>(lane);
+    constexpr int T2 = tr_second_row<!BLK, STR>();
 
     const int n_qt = (N + BR - 1) / BR;
     const int qt0 = CAUSAL ? k0 / BR : 0;
@@ -408,8 +424,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                 u32x4 ot[D / 32], qt4[D / 32];
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    ot[db] = lds_read_tr16_x2(o_lds + tb + db * 32, o_lds + tb + db * 32 + STR);
-                    qt4[db] = lds_read_tr16_x2(q_lds + tb + db * 32, q_lds + tb + db * 32 + STR);
+                    ot[db] = lds_read_tr16_x2(o_lds + tb + db * 32, o_lds + tb + db * 32 + T2);
+                    qt4[db] = lds_read_tr16_x2(q_lds + tb + db * 32, q_lds + tb + db * 32 + T2);
                 }
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
@@ -522,8 +538,8 @@ __global__ __launch_bounds__(256, D == 64 ? 2 : 1) void bwd_dkdv_kernel(
                 u32x4 ot[D / 32], qt4[D / 32];
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    ot[db] = lds_read_tr16_x2(o_lds + tb + db * 32, o_lds + tb + db * 32 + STR);
-                    qt4[db] = lds_read_tr16_x2(q_lds + tb + db * 32, q_lds + tb + db * 32 + STR);
+                    ot[db] = lds_read_tr16_x2(o_lds + tb + db * 32, o_lds + tb + db * 32 + T2);
+                    qt4[db] = lds_read_tr16_x2(q_lds + tb + db * 32, q_lds + tb + db * 32 + T2);
                 }
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
@@ -751,12 +767,12 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
 
     const rsrc_t krs = make_rsrc(K + base, (uint32_t)N * D * 2);
     const rsrc_t vrs = make_rsrc(V + base, (uint32_t)N * D * 2);
-    TileCopy<BC, D, STR, 4> cp;
+    TileCopy<BC, D, STR, 4, !BLK> cp;
     cp.init(wave, lane);
-    // operand read offsets as in the dK/dV kernel (rows through lds_row)
-    const int a_off = lds_row(kperm(ln)) * STR + hf * 8;
-    const int G = lane >> 4, sl = lane & 15;
-    const int t_off = (4 * (sl >> 2) + 2 * (G >> 1)) * STR + 16 * (G & 1) + 4 * (sl & 3);
+    // operand read offsets as in the dK/dV kernel
+    const int a_off = row_read_off<!BLK, STR>(lane);
+    const int t_off = tr_read_off<!BLK, STR>(lane);
+    constexpr int T2 = tr_second_row<!BLK, STR>();
 
     const int kend = CAUSAL ? min(N, q0 + BR) : N;
     const int ntiles = (kend + BC - 1) / BC;
@@ -832,7 +848,7 @@ __global__ __launch_bounds__(256, 2) void bwd_dq_kernel(
                 u32x4 kt4[D / 32];
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    kt4[db] = lds_read_tr16_x2(k_lds + tb + db * 32, k_lds + tb + db * 32 + STR);
+                    kt4[db] = lds_read_tr16_x2(k_lds + tb + db * 32, k_lds + tb + db * 32 + T2);
                 }
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) dqacc[db] = mfma32x32x16(kt4[db], dsf, dqacc[db]);
