@@ -331,6 +331,20 @@ def ceilings(fa, headline_tflops, seconds=1.2):
     res["library_gemm"] = {"op": "torch.matmul bf16 8192 x 8192 x 8192 (vendor BLAS)", **r,
                            "headline_fraction_of_this": round(headline_tflops / r["TFLOP/s"], 4)}
     del a, b, c
+    # HBM: a streaming read of 4 GiB (non-temporal 16-byte loads, as the decode kernels issue),
+    # at a few grid sizes; the best rate is the ceiling the decode kernels are read against
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device="cuda")
+    best = None
+    for grid in (256, 512, 1024, 2048, 4096, 8192):
+        chk = torch.empty(grid * 256, dtype=torch.int32, device="cuda")
+        r = rate_under_load(lambda: fa.calib_hbm_read(buf, grid, chk), float(buf.numel()), seconds)
+        gbs = round(buf.numel() / (r["ms_per_call"] * 1e-3) / 1e9, 1)
+        if best is None or gbs > best["GB/s"]:
+            best = {"op": "streaming read of 4 GiB, non-temporal 16-byte loads (fa_calib_hbm_read)",
+                    "grid": grid, "GB/s": gbs, "frac_of_8TB/s": round(gbs / (PEAK_HBM / 1e9), 4),
+                    "ms_per_call": r["ms_per_call"], "sclk_mhz_median": r["sclk_mhz_median"]}
+    res["hbm_stream_read"] = best
+    del buf
     torch.cuda.empty_cache()
     return res
 
@@ -819,6 +833,12 @@ def main(argv=None):
             gm = gpu_extra["gpt2m"]
             gpu_extra = {"gpt2m": {"o_nc": gm["o_nc"].float().cpu().numpy().astype(np.float64),
                                    "o_c": gm["o_c"].float().cpu().numpy().astype(np.float64)}}
+    if "ceilings" in line and "also_measured" in line:
+        hb = line["ceilings"]["hbm_stream_read"]["GB/s"]
+        for key in ("decode_splitkv", "decode_paged_gqa"):
+            if key in line["also_measured"]:
+                am = line["also_measured"][key]
+                am["fraction_of_hbm_stream_read"] = round(am["GB/s"] / hb, 4)
     if not args.no_cpu:
         line["cpu_baseline"] = cpu_baseline(xh, o_host, lse_host, gpu_extra)
     print(json.dumps(line), flush=True)

@@ -11,7 +11,8 @@
  * runs one such combination with nothing else in the loop, so its rate is
  * measured on the same part, under the same clock behaviour, as the kernel it
  * is compared with.  A second set runs the kernels' LDS read patterns alone,
- * which is how their row layouts were chosen.  None of this is part of the
+ * which is how their row layouts were chosen, and a third streams a buffer from
+ * HBM, the ceiling of the decode kernels.  None of this is part of the
  * attention path.
  *
  * Conventions follow fa.h (fa_status results, device pointers, stream).
@@ -69,6 +70,18 @@ double fa_calib_lds_bytes(int pattern, int grid, int iters);
  * otherwise, also for an unknown pattern); FA_ERR_NULL, FA_ERR_ALIGN for a bad
  * pointer; FA_ERR_HIP for a launch error. */
 fa_status fa_calib_lds(int pattern, int grid, int iters, unsigned int* out, void* stream);
+
+/* Enqueues one streaming read of `bytes` bytes at `buf` (non-temporal 16-byte
+ * loads, the load form of the decode kernels; `grid` workgroups of 256 lanes,
+ * each on its own contiguous share of the buffer): the HBM read rate the part
+ * reaches with nothing else in the loop.
+ * buf  : device pointer, 16-byte aligned, `bytes` readable bytes (read only).
+ * out  : device pointer, 16-byte aligned, to grid * 256 unsigned ints (a
+ *        checksum per lane; overwritten).
+ * bytes a positive multiple of 16, grid in [1, FA_CALIB_MAX_GRID] (FA_ERR_ARG
+ * otherwise); FA_ERR_NULL, FA_ERR_ALIGN for a bad pointer; FA_ERR_HIP for a
+ * launch error. */
+fa_status fa_calib_hbm_read(const void* buf, size_t bytes, int grid, unsigned int* out, void* stream);
 
 #ifdef __cplusplus
 }

@@ -68,6 +68,7 @@ CALIB_SIGNATURES = {
     "fa_calib_lds_name": (ctypes.c_char_p, [_I]),
     "fa_calib_lds_bytes": (ctypes.c_double, [_I, _I, _I]),
     "fa_calib_lds": (_I, [_I, _I, _I, _P, _P]),
+    "fa_calib_hbm_read": (_I, [_P, _Z, _I, _P, _P]),
 }
 
 _lib = None
@@ -452,4 +453,19 @@ def calib_lds(pattern, grid, iters, out):
     _same_gpu([("out", out)])
     check("fa_calib_lds", lib().fa_calib_lds(int(pattern), int(grid), int(iters), out.data_ptr(),
                                              _stream(out)))
+    return out
+
+
+def calib_hbm_read(buf, grid, out):
+    """One streaming read of the whole of `buf` (a contiguous device tensor whose size in bytes
+    is a multiple of 16) on the current stream (fa_calib_hbm_read); out: an int32 device tensor of
+    grid * 256 elements."""
+    import torch
+    nbytes = buf.numel() * buf.element_size()
+    if not buf.is_contiguous() or nbytes % 16:
+        raise ValueError("buf must be contiguous and a multiple of 16 bytes")
+    _expect(out, "out", (int(grid) * 256,), torch.int32)
+    _same_gpu([("buf", buf), ("out", out)])
+    check("fa_calib_hbm_read", lib().fa_calib_hbm_read(buf.data_ptr(), nbytes, int(grid),
+                                                       out.data_ptr(), _stream(out)))
     return out

@@ -247,3 +247,46 @@ extern "C" fa_status fa_calib_lds(int pattern, int grid, int iters, unsigned int
     kLds[pattern].launch(grid, reinterpret_cast<uint32_t*>(out), iters, static_cast<hipStream_t>(stream));
     return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
+
+// ---------------------------------------------------------------------------
+// HBM streaming read: each workgroup reads its own contiguous share of a
+// buffer in 16-byte chunks with non-temporal loads (the load form of the
+// decode kernels), its 256 lanes on consecutive chunks and 8 chunks in flight
+// per lane (32 KB per workgroup and step); the chunks are folded into one
+// checksum per lane.
+
+namespace {
+
+typedef uint32_t cal_u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void calib_read_kernel(const cal_u32x4* __restrict__ buf, size_t nchunks,
+                                                         uint32_t* __restrict__ out) {
+    const size_t per = (nchunks + gridDim.x - 1) / gridDim.x;
+    const size_t beg = (size_t)blockIdx.x * per;
+    const size_t end = beg + per < nchunks ? beg + per : nchunks;
+    uint32_t acc = 0;
+    size_t i = beg + threadIdx.x;
+    for (; i + 7 * 256 < end; i += 8 * 256) {
+        cal_u32x4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(buf + i + u * 256);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < end; i += 256) {
+        const cal_u32x4 v = __builtin_nontemporal_load(buf + i);
+        acc += v.x ^ v.y ^ v.z ^ v.w;
+    }
+    out[blockIdx.x * 256 + threadIdx.x] = acc;
+}
+
+}  // namespace
+
+extern "C" fa_status fa_calib_hbm_read(const void* buf, size_t bytes, int grid, unsigned int* out, void* stream) {
+    if (!buf || !out) return FA_ERR_NULL;
+    if (((uintptr_t)buf | (uintptr_t)out) & 15) return FA_ERR_ALIGN;
+    if (bytes == 0 || (bytes & 15) || grid < 1 || grid > FA_CALIB_MAX_GRID) return FA_ERR_ARG;
+    calib_read_kernel<<<grid, 256, 0, static_cast<hipStream_t>(stream)>>>(static_cast<const cal_u32x4*>(buf), bytes / 16,
+                                                                        reinterpret_cast<uint32_t*>(out));
+    return hipGetLastError() == hipSuccess ? FA_OK : FA_ERR_HIP;
+}

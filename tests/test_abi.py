@@ -66,6 +66,11 @@ def test_calib_host_checks():
     assert lib.fa_calib_lds(m, 1, 1, P, None) == 7
     assert lib.fa_calib_lds(0, 0, 1, P, None) == 7
     assert lib.fa_calib_lds(0, 1, 0, P, None) == 7
+    assert lib.fa_calib_hbm_read(None, 16, 1, P, None) == 1
+    assert lib.fa_calib_hbm_read(P + 8, 16, 1, P, None) == 6
+    assert lib.fa_calib_hbm_read(P, 0, 1, P, None) == 7
+    assert lib.fa_calib_hbm_read(P, 24, 1, P, None) == 7
+    assert lib.fa_calib_hbm_read(P, 16, 0, P, None) == 7
 
 
 def test_status_strings():

@@ -37,6 +37,28 @@ def test_every_lds_pattern_runs_and_repeats():
         assert fa.calib_lds_bytes(pat, grid, iters) > 0
 
 
+def test_hbm_read_checksum():
+    """The streaming read folds every chunk once: workgroup b reads chunks [b*per, (b+1)*per)
+    (per = ceil(chunks / grid)), its lane t the chunks t, t + 256, ... of that range, and the lane's
+    checksum is the sum of their four-word XORs, which the test recomputes on the host."""
+    import torch
+
+    import io_aware_tiled_03_amd as fa
+    g = torch.Generator().manual_seed(5)
+    host = torch.randint(0, 2 ** 31 - 1, (1000 * 4 + 36,), generator=g, dtype=torch.int64)
+    words = host.to(torch.int32)
+    grid = 3
+    out = fa.calib_hbm_read(words.cuda(), grid, torch.empty(grid * 256, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    w = words.numpy().astype("uint32").reshape(-1, 4)
+    x = w[:, 0] ^ w[:, 1] ^ w[:, 2] ^ w[:, 3]
+    per = -(-len(x) // grid)
+    want = [int(x[b * per:min((b + 1) * per, len(x))][t::256].astype("uint64").sum() % 2 ** 32)
+            for b in range(grid) for t in range(256)]
+    got = (out.cpu().numpy().astype("int64") % 2 ** 32).tolist()
+    assert got == want
+
+
 def test_binding_rejects_short_buffers():
     import torch
 
