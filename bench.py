@@ -728,9 +728,9 @@ def main(argv=None):
         d = args.summarize_counters
         cmds = ["rocprofv3 --pmc %s --output-format csv -d %s -o %s -- python -u bench.py %s"
                 % (c, r, o, a) for c, r, o, a in (
-                    ("FETCH_SIZE", d[0], "run", "--steps 5 --warmup 1 --no-extra --no-cpu"),
+                    ("FETCH_SIZE", d[0], "run", "--steps 5 --warmup 1 --no-extra --no-cpu --no-ceilings"),
                     ("FETCH_SIZE", d[1], "copy", "--calibrate-copy 1024"),
-                    ("WRITE_SIZE", d[2], "run", "--steps 5 --warmup 1 --no-extra --no-cpu"),
+                    ("WRITE_SIZE", d[2], "run", "--steps 5 --warmup 1 --no-extra --no-cpu --no-ceilings"),
                     ("WRITE_SIZE", d[3], "copy", "--calibrate-copy 1024"))]
         summarize_counters(d[0], d[1], d[2], d[3], 1024, cmds)
         return 0

@@ -57,8 +57,20 @@ __device__ __forceinline__ int kperm(int m) {
 #define FA_FWD_KPAD 8        // K row padding (bf16 elements)
 #endif
 #ifndef FA_FWD_VPAD
-#define FA_FWD_VPAD 16       // V row padding (bf16 elements)
+#define FA_FWD_VPAD 16       // V row padding (bf16 elements), natural row order
 #endif
+
+// V tiles are read only by the transposing read, each 16-lane group on 64 bytes
+// of four consecutive keys, which share banks at rows of 16 x odd bytes and
+// partly at the padded 288-byte rows.  The d = 128 causal kernel (the long
+// prefill) instead stores key r of a tile at LDS row vrow(r) of 272-byte rows:
+// vrow swaps the two 2-bit fields of r inside each 16-row block, so the four keys
+// of a read sit four rows apart (4 x 16 x odd bytes = 64 mod 256: the pieces
+// cover the banks once).  Long causal prefill 1.906 -> 1.892 ms, outputs
+// identical.  The other kernels keep natural order: with the permutation the
+// d = 128 non-causal kernel spilled 20 bytes and the d = 64 dropout kernels
+// went over the registers of three waves per SIMD, for at most 1% elsewhere.
+__device__ __forceinline__ int vrow(int r) { return (r & ~15) | ((r & 3) << 2) | ((r >> 2) & 3); }
 // d=128: the score products' K operand reads are issued this many ahead of
 // the products that use them (the compiler's own order kept two in flight,
 // exposing the LDS latency before every other product; four measured 2%
@@ -74,6 +86,9 @@ template <int N_> using ic = std::integral_constant<int, N_>;
 // Mask modes of the bf16 forward (kMaskBlock*: block-sparse, without or with
 // the causal mask).
 enum : int { kMaskNone = 0, kMaskCausal = 1, kMaskWindow = 2, kMaskBlock = 3, kMaskBlockCausal = 4 };
+// V rows through vrow (above) in the d = 128 causal kernel only
+template <int D, int MODE, bool DROP>
+constexpr bool fwd_vperm() { return D == 128 && MODE == kMaskCausal && !DROP; }
 
 // BC keys per tile, NW waves per workgroup (32 query rows each); MODE is one
 // of the mask modes (kMaskWindow: causal with a sliding window and sinks).
@@ -91,7 +106,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
     constexpr int BR = 32 * NW, NKB = BC / 32;
     constexpr int KCH = D / 8;             // 16-byte chunks per row
     constexpr int KSTR = D + FA_FWD_KPAD;  // K row stride (elements), padded against bank conflicts
-    constexpr int VSTR = D + FA_FWD_VPAD;  // V row stride (elements)
+    constexpr bool VPERM = fwd_vperm<D, MODE, DROP>();
+    constexpr int VSTR = VPERM ? D + 8 : D + FA_FWD_VPAD;  // V row stride (elements)
     // Two staging buffers per operand, as distinct LDS variables chosen at
     // compile time: the compiler then knows a read of one buffer cannot alias
     // the direct-to-LDS copies still landing in the other, and does not wait
@@ -154,7 +170,8 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
 #pragma unroll
     for (int t = 0; t < VPW; ++t) {
         const int pos = (wave + NW * t) * 64 + lane, row = pos / VCPR, c = pos % VCPR;
-        vgo[t] = (uint32_t)(row * D + (c < KCH ? c : 0) * 8) * 2;
+        const int key = VPERM ? vrow(row) : row;   // LDS row `row` holds this key of the tile
+        vgo[t] = (uint32_t)(key * D + (c < KCH ? c : 0) * 8) * 2;
     }
     auto stage = [&](int j, auto bufc) __attribute__((always_inline)) {   // copies of tile j into buffer bufc
         constexpr bool B1 = decltype(bufc)::value != 0;
@@ -179,10 +196,13 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
 
     // Per-lane offsets of the operand reads.  K: physical row kb*32 + ln.
     // V (transposing read): lane s of 16-lane group G reads key 8*(G/2) + s/4
-    // (+4 for slots 4..7), columns 16*(G%2) + 4*(s%4).
+    // (+4 for slots 4..7), columns 16*(G%2) + 4*(s%4); through vrow that key (plus
+    // a multiple of 16) is LDS row 4*(s/4) + 2*(G/2), and key +4 the next LDS row.
     const int k_off = ln * KSTR + hf * 8;
     const int G = lane >> 4, sl = lane & 15;
-    const int v_off = (8 * (G >> 1) + (sl >> 2)) * VSTR + 16 * (G & 1) + 4 * (sl & 3);
+    const int v_off = (VPERM ? 4 * (sl >> 2) + 2 * (G >> 1) : 8 * (G >> 1) + (sl >> 2)) * VSTR + 16 * (G & 1) +
+                      4 * (sl & 3);
+    constexpr int V_HI = VPERM ? VSTR : 4 * VSTR;   // offset of the second read (keys +4)
 
     // One key tile from LDS buffer BUF; MASK selects the masked variant (tail
     // tile, or a tile crossing this wave's diagonal under the causal mask).
@@ -322,7 +342,7 @@ __global__ __launch_bounds__(64 * NW, NW == 4 ? 2 : 1) void fwd_bf16_kernel(
                 u32x4 va[D / 32];
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) {
-                    va[db] = lds_read_tr16_x2(&sv[vb + db * 32], &sv[vb + db * 32 + 4 * VSTR]);
+                    va[db] = lds_read_tr16_x2(&sv[vb + db * 32], &sv[vb + db * 32 + V_HI]);
                 }
 #pragma unroll
                 for (int db = 0; db < D / 32; ++db) oacc[db] = mfma32x32x16(va[db], pf[kb][t], oacc[db]);
